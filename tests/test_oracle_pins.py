@@ -1,0 +1,341 @@
+"""Pins for the CPU oracle: each test checks the oracle against something other
+than itself -- values printed on the pages, closed forms, invariants the
+pages state, brute force on tiny inputs, or a library routine that computes
+the same special case.  All of these run on the CPU."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import F16, F32
+from tests.conftest import golden
+
+from llama_decoder_forward_amd import synth
+
+
+def f16_ulp(x):
+    """Spacing of binary16 numbers at |x| (numpy's own float16 type)."""
+    return float(np.spacing(np.float16(abs(x))))
+
+
+# --------------------------------------------------------------------------
+# binary16 conversions: pinned to numpy's float16 casts (correctly rounded,
+# round-to-nearest-even) over every half value, every midpoint between
+# neighbouring halves, and random float32 / float64 inputs.
+# --------------------------------------------------------------------------
+def test_f16_decode_all_bit_patterns():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f16_to_f32_array(h)
+    ref = h.view(np.float16).astype(np.float32)
+    fin = np.isfinite(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[np.isinf(ref)], ref[np.isinf(ref)])
+
+
+def test_f16_round_midpoints_and_neighbours():
+    h = np.arange(0, 0x7bff, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    mid = (lo + hi) / 2  # exact in float64 (and float32)
+    cases = np.concatenate([mid, np.nextafter(mid, 0), np.nextafter(mid, 1), lo, -mid,
+                            [65504.0, 65519.0, 65520.0, 1e6, 2.0 ** -25, 2.0 ** -26, 3 * 2.0 ** -26]])
+    ours = oracle.f64_to_f16_array(cases)
+    ref = cases.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+    c32 = mid.astype(np.float32)  # midpoints are representable in float32
+    assert np.array_equal(oracle.f32_to_f16_array(c32), c32.astype(np.float16).view(np.uint16))
+
+
+def test_f16_round_random_float32():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2 ** 32, size=300_000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f32_to_f16_array(x), ref)
+    y = rng.standard_normal(200_000).astype(np.float32) * np.float32(0.05)
+    assert np.array_equal(oracle.f32_to_f16_array(y), y.astype(np.float16).view(np.uint16))
+
+
+# --------------------------------------------------------------------------
+# Seeded generator
+# --------------------------------------------------------------------------
+def test_splitmix64_published_vectors():
+    with open(f"{__import__('tests.conftest').conftest.ROOT}/tests/golden/splitmix64_vectors.txt") as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    for st, n, out in rows:
+        assert oracle.splitmix64_at(int(st), int(n)) == int(out, 16)
+        assert int(synth.splitmix64(int(st), int(n))) == int(out, 16)
+
+
+def test_weight_generator_moments_and_rounding():
+    seed, tid, n = 1234, 16 + 8 * 3 + 4, 1 << 20
+    w16 = oracle.gen_tensor(seed, tid, 0, n, F16)
+    vals = w16.view(np.float16).astype(np.float64)
+    # Irwin-Hall(4) scaled to sd 0.02: mean 0, sd 0.02, support |w| <= 0.02*2*sqrt(3)
+    assert abs(vals.mean()) < 5 * 0.02 / math.sqrt(n)
+    assert abs(vals.std() / 0.02 - 1) < 0.01
+    assert np.abs(vals).max() <= 0.02 * 2 * math.sqrt(3) + 1e-4
+    # stored values are the correctly rounded double value (numpy's cast)
+    idx = np.arange(0, n, 4099)
+    exact = np.array([oracle.weight_value(seed, tid, int(e)) for e in idx])
+    assert np.array_equal(w16[idx], exact.astype(np.float16).view(np.uint16))
+    w32 = oracle.gen_tensor(seed, tid, 0, 4096, F32)
+    exact32 = np.array([oracle.weight_value(seed, tid, e) for e in range(4096)])
+    assert np.array_equal(w32, exact32.astype(np.float32))
+    # offsets address the same elements
+    assert np.array_equal(oracle.gen_tensor(seed, tid, 777, 100, F16), w16[777:877])
+    # different tensors and seeds give different streams
+    assert not np.array_equal(oracle.gen_tensor(seed, tid + 1, 0, 64, F16), w16[:64])
+    assert not np.array_equal(oracle.gen_tensor(seed + 1, tid, 0, 64, F16), w16[:64])
+
+
+# --------------------------------------------------------------------------
+# FFN width (P1 section 3.6) and sizing
+# --------------------------------------------------------------------------
+def test_ffn_width_printed_example():
+    g = golden("printed_values.txt")
+    assert oracle.ffn_hidden(4096, 256, None) == int(g["ffn_hidden_dim4096_mo256"])
+    # unaligned width 10922 then rounded up: multiple_of=1 leaves it as is
+    assert oracle.ffn_hidden(4096, 1, None) == int(g["ffn_unaligned_dim4096"])
+
+
+@pytest.mark.parametrize("dim,mo,mult", [(64, 32, 0), (5120, 256, 0), (8192, 4096, 1.3),
+                                         (8192, 256, 1.3), (2048, 256, 0)])
+def test_ffn_width_properties(dim, mo, mult):
+    f = oracle.ffn_hidden(dim, mo, mult)
+    base = oracle.ffn_hidden(dim, 1, mult)
+    assert f % mo == 0 and base <= f < base + mo
+    assert base <= 8 * dim / 3 * (mult or 1) + 1
+
+
+# --------------------------------------------------------------------------
+# RMSNorm (P1 section 3.2)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("c", [0.5, 1e-3, 3.0, -0.02])
+def test_rmsnorm_constant_vector(c):
+    D, eps = 64, 1e-5
+    x = np.full(D, c, np.float32)
+    exact = c / math.sqrt(c * c + eps)  # closed form: every entry
+    y32 = oracle.rmsnorm(x, eps, F32)
+    assert np.allclose(y32, exact, rtol=4e-7, atol=0)
+    y16 = oracle.rmsnorm(x, eps, F16)
+    assert np.all(np.abs(y16 - exact) <= f16_ulp(exact) / 2 * 1.0001)
+
+
+def test_rmsnorm_against_float64_and_eps():
+    rng = np.random.default_rng(2)
+    for scale in [1.0, 1e-3, 30.0]:
+        x = (rng.standard_normal(4096) * scale).astype(np.float32)
+        ms = np.mean(x.astype(np.float64) ** 2)
+        exact = x.astype(np.float64) / np.sqrt(ms + 1e-5)
+        y = oracle.rmsnorm(x, 1e-5, F32).astype(np.float64)
+        assert np.max(np.abs(y - exact) / np.abs(exact).max()) < 2e-6
+        # output RMS is 1/sqrt(1 + eps/ms): eps matters at scale 1e-3
+        rms = math.sqrt(np.mean(y ** 2))
+        assert abs(rms - 1 / math.sqrt(1 + 1e-5 / ms)) < 3e-6
+        y16 = oracle.rmsnorm(x, 1e-5, F16)
+        assert np.all(np.abs(y16 - exact) <= np.array([f16_ulp(v) for v in exact]) * 0.5001 + 1e-7)
+
+
+def test_rmsnorm_weight_and_scale_invariance():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(512).astype(np.float32)
+    w = np.full(512, 2.0, np.float32)
+    assert np.array_equal(oracle.rmsnorm(x, 0.0, F32, w=w), 2 * oracle.rmsnorm(x, 0.0, F32))
+    # with eps = 0 a power-of-two scale is exact
+    assert np.array_equal(oracle.rmsnorm(8 * x, 0.0, F32), oracle.rmsnorm(x, 0.0, F32))
+
+
+# --------------------------------------------------------------------------
+# RoPE (P1 sections 3.3 and 9)
+# --------------------------------------------------------------------------
+def test_rope_table_closed_form():
+    d, S = 128, 64
+    c, s = oracle.rope_table(d, S, 10000.0)
+    # theta_0 = 1: angles are the positions themselves
+    m = np.arange(S)
+    assert np.array_equal(c[:, 0], np.cos(m.astype(np.float32).astype(np.float64)).astype(np.float32))
+    assert np.array_equal(s[:, 0], np.sin(m.astype(np.float32).astype(np.float64)).astype(np.float32))
+    i = np.arange(d // 2)
+    theta = 10000.0 ** (-2 * i / d)
+    ang = np.outer(m, theta)
+    assert np.allclose(c, np.cos(ang), atol=2e-5) and np.allclose(s, np.sin(ang), atol=2e-5)
+    assert np.array_equal(c[0], np.ones(d // 2, np.float32)) and np.array_equal(s[0], np.zeros(d // 2, np.float32))
+
+
+def test_rope_adjacent_pairs_and_direction():
+    d = 16
+    c, s = oracle.rope_table(d, 8, 10000.0)
+    for i in range(d // 2):
+        e = np.zeros(d, np.float32)
+        e[2 * i] = 1.0  # the complex number 1 in pair i
+        r = oracle.rope_apply(e, c[5], s[5])
+        want = np.zeros(d, np.float32)
+        want[2 * i], want[2 * i + 1] = c[5, i], s[5, i]  # (1+0i)(cos+i sin)
+        assert np.array_equal(r, want)
+
+
+def test_rope_norm_and_relative_position():
+    d = 128
+    rng = np.random.default_rng(4)
+    c, s = oracle.rope_table(d, 2048, 10000.0)
+    q = rng.standard_normal(d).astype(np.float32)
+    k = rng.standard_normal(d).astype(np.float32)
+    assert np.array_equal(oracle.rope_apply(q, c[0], s[0]), q)  # m = 0 is the identity
+    for m in [1, 7, 100, 1500]:
+        r = oracle.rope_apply(q, c[m], s[m]).astype(np.float64)
+        pair = lambda v: np.hypot(v[0::2], v[1::2])
+        assert np.allclose(pair(r), pair(q.astype(np.float64)), rtol=3e-7, atol=1e-7)
+    def dot(m, n):
+        return float(np.dot(oracle.rope_apply(q, c[m], s[m]).astype(np.float64),
+                            oracle.rope_apply(k, c[n], s[n]).astype(np.float64)))
+    for (m, n, delta) in [(3, 1, 5), (10, 10, 100), (40, 7, 900)]:
+        tol = 1e-5 * (1 + m + n + 2 * delta)  # fp32 angle error grows with position
+        assert abs(dot(m, n) - dot(m + delta, n + delta)) < tol
+    assert abs(dot(3, 1) - dot(4, 1)) > 1e-3  # but it does depend on m - n
+
+
+# --------------------------------------------------------------------------
+# Attention (P1 section 3.5)
+# --------------------------------------------------------------------------
+def test_attention_special_cases():
+    rng = np.random.default_rng(5)
+    d = 16
+    q = rng.standard_normal(d).astype(np.float32)
+    K = rng.standard_normal((1, d)).astype(np.float32)
+    V = rng.standard_normal((1, d)).astype(np.float32)
+    assert np.array_equal(oracle.attention_row(q, K, V), V[0])  # one key: output = v
+    K = np.repeat(rng.standard_normal((1, d)).astype(np.float32), 7, axis=0)
+    V = rng.standard_normal((7, d)).astype(np.float32)
+    out = oracle.attention_row(q, K, V)
+    assert np.allclose(out, V.astype(np.float64).mean(0), atol=1e-6)  # equal keys: mean of v
+
+
+def test_attention_textbook_float64():
+    rng = np.random.default_rng(6)
+    for L, d in [(5, 16), (33, 128), (200, 64)]:
+        q = rng.standard_normal(d).astype(np.float32)
+        K = rng.standard_normal((L, d)).astype(np.float32)
+        V = rng.standard_normal((L, d)).astype(np.float32)
+        sc = K.astype(np.float64) @ q.astype(np.float64) / math.sqrt(d)
+        p = np.exp(sc - sc.max())
+        p /= p.sum()
+        ref = p @ V.astype(np.float64)
+        assert np.allclose(oracle.attention_row(q, K, V), ref, atol=2e-6)
+        assert np.allclose(oracle.attention_row(q, K, V, acc64=True), ref, atol=1e-7)
+
+
+# --------------------------------------------------------------------------
+# SwiGLU's SiLU (P1 section 3.6)
+# --------------------------------------------------------------------------
+def test_silu_closed_form():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(30.0) == 30.0
+    assert oracle.silu(-30.0) == pytest.approx(-30.0 * math.exp(-30.0), rel=1e-6)
+    for x in np.linspace(-8, 8, 33):
+        x = float(np.float32(x))
+        assert oracle.silu(x) == pytest.approx(x / (1 + math.exp(-x)), rel=2e-7, abs=1e-12)
+        assert oracle.silu(-x) == pytest.approx(oracle.silu(x) - x, abs=4e-6)
+
+
+# --------------------------------------------------------------------------
+# Sampling (P1 sections 4.2-4.3, P2 section 4)
+# --------------------------------------------------------------------------
+def test_argmax_ties_lowest_index():
+    lg = np.array([0.1, 3.0, -1.0, 3.0, 2.0], np.float32)
+    assert oracle.argmax(lg) == 1
+
+
+def test_softmax_temperature():
+    from scipy.special import softmax
+    rng = np.random.default_rng(7)
+    lg = (rng.standard_normal(32000) * 1.3).astype(np.float32)
+    for t in [0.6, 0.8, 1.0, 2.5]:
+        p = oracle.softmax_temp(lg, t)
+        ref = softmax(lg.astype(np.float64) / np.float64(np.float32(t)))
+        assert np.allclose(p, ref, rtol=2e-5, atol=1e-10)
+        assert abs(p.astype(np.float64).sum() - 1) < 1e-4
+    p = oracle.softmax_temp(lg, 1e-3)  # t -> 0 approaches argmax
+    assert p[oracle.argmax(lg)] > 0.999
+
+
+def _brute_nucleus(P, top_p, u):
+    """Top-p without sorting, from the definition: E_i is the integer mass of
+    every token ranked above i (higher probability, or equal probability and
+    lower id); i is kept iff E_i <= p; the draw is the kept token whose
+    interval [E_i, E_i + Q_i) holds the scaled uniform."""
+    V = len(P)
+    Q = [int(float(p) * 2 ** 48) for p in P]
+    E = [sum(Q[j] for j in range(V) if P[j] > P[i] or (P[j] == P[i] and j < i)) for i in range(V)]
+    thr = int(math.floor(float(np.float32(top_p)) * 2 ** 48))
+    kept = [i for i in range(V) if E[i] <= thr]
+    S = sum(Q[i] for i in kept)
+    t = (int(math.floor(float(u) * 2 ** 24)) * S) >> 24
+    pick = [i for i in kept if E[i] <= t < E[i] + Q[i]]
+    return kept, (pick[0] if pick else min(kept, key=lambda i: E[i]))
+
+
+def _min_cardinality_nucleus(P, top_p):
+    """Enumerate every subset of a 16-token vocabulary: the nucleus is the
+    smallest set whose mass exceeds p, choosing the largest mass among sets of
+    that size (everything when no set exceeds p)."""
+    V = len(P)
+    Q = [int(float(p) * 2 ** 48) for p in P]
+    thr = int(math.floor(float(np.float32(top_p)) * 2 ** 48))
+    best = None
+    for r in range(1, V + 1):
+        cands = [c for c in itertools.combinations(range(V), r) if sum(Q[i] for i in c) > thr]
+        if cands:
+            m = max(sum(Q[i] for i in c) for c in cands)
+            best = [c for c in cands if sum(Q[i] for i in c) == m]
+            break
+    return best
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_top_p_brute_force_16(case):
+    rng = np.random.default_rng(100 + case)
+    V = 16
+    if case < 6:
+        P = rng.dirichlet(np.ones(V) * (0.3 + case)).astype(np.float32)
+    elif case < 9:  # ties and zeros
+        P = np.array(rng.integers(0, 4, V), np.float64)
+        P = (P / P.sum()).astype(np.float32)
+    else:
+        lg = (rng.standard_normal(V) * 2).astype(np.float32)
+        P = oracle.softmax_temp(lg, 0.7)
+    for top_p in [0.05, 0.5, 0.9, 0.95, 1.0]:
+        k = oracle.top_p(P, top_p, 0.0)[1]
+        kept, _ = _brute_nucleus(P, top_p, 0.0)
+        assert k == len(kept)
+        sets = _min_cardinality_nucleus(P, top_p)
+        if sets is None:
+            assert k == V
+        else:
+            assert len(sets[0]) == k
+            assert tuple(sorted(kept)) in [tuple(sorted(s)) for s in sets]
+        for u in np.linspace(0, 1 - 2 ** -24, 97, dtype=np.float64):
+            u = np.float32(np.floor(u * 2 ** 24) / 2 ** 24)
+            tok, _ = oracle.top_p(P, top_p, float(u))
+            assert tok == _brute_nucleus(P, top_p, u)[1]
+            assert P[tok] > 0
+
+
+def test_top_p_boundaries():
+    # probabilities that are exact binary fractions so cumsum boundaries are exact
+    P = np.array([0.5, 0.25, 0.125, 0.125], np.float32)
+    assert oracle.top_p(P, 0.5, 0.0)[1] == 2      # E = 0, .5, .75: 0.5 <= p kept, 0.75 not
+    assert oracle.top_p(P, 0.4999, 0.0)[1] == 1   # always at least one token
+    assert oracle.top_p(P, 1e-9, 0.9)[0] == 0
+    assert oracle.top_p(P, 1.0, 0.0)[1] == 4
+    # inverse CDF over kept {0,1}: mass .75, token 0 for u < 2/3
+    assert oracle.top_p(P, 0.5, 0.66)[0] == 0 and oracle.top_p(P, 0.5, 0.67)[0] == 1
+    assert oracle.top_p(P, 1.0, 1 - 2 ** -24)[0] == 3
+    # ties are ordered by token id
+    Pt = np.array([0.25, 0.25, 0.25, 0.25], np.float32)
+    assert [oracle.top_p(Pt, 1.0, u)[0] for u in (0.0, 0.3, 0.6, 0.9)] == [0, 1, 2, 3]
