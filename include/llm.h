@@ -1,0 +1,207 @@
+/*
+ * llm.h -- C ABI of the MI355X (gfx950) Llama-2 decoder forward library.
+ *
+ * The library runs the decoder-only forward pass described in the
+ * walkthrough "Meta Llama 源码深度剖析与生产应用教程" (section 2 data flow,
+ * sections 3.2-3.8 for the layer) with the reference's static per-layer KV
+ * cache (section 3.1), as a full-prompt causal prefill followed by one-token
+ * decode steps (section 4.2, and the course notes on generate, section 1),
+ * and ends in last-position logits with greedy, temperature and top-p
+ * sampling (section 4.3).  Every step runs in hand-written HIP kernels on one
+ * GPU.
+ *
+ * Conventions for every call:
+ *  - Return value: LLM_OK (0) or a negative llm_status.  Nothing aborts and no
+ *    C++ exception crosses this boundary; llm_last_error() returns a message.
+ *  - Arguments are validated on the host before any GPU work is queued; an
+ *    invalid call changes no state.
+ *  - A failing HIP call returns LLM_EDEVICE and poisons the handle: every later
+ *    call on it returns LLM_EDEVICE too (destroy is still allowed).
+ *  - Pointers without a _d suffix are host pointers; `_d` entry points take
+ *    device pointers.  The caller owns everything it passes; the handle owns
+ *    all memory it allocates (weights, KV cache, token buffer, logits,
+ *    workspace) and frees it in llm_destroy.
+ *  - All work is ordered on one HIP stream (the caller's, or the handle's
+ *    own).  llm_prefill, llm_decode and the _d calls are asynchronous; calls
+ *    that return values into host memory synchronise the stream.
+ *  - A handle is not thread-safe.
+ */
+#ifndef LLM_H
+#define LLM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LLM_OK = 0,
+    LLM_EINVAL = -1,   /* argument out of range or inconsistent */
+    LLM_ESTATE = -2,   /* call not allowed in the handle's current state */
+    LLM_ENOMEM = -3,   /* device allocation failed */
+    LLM_EDEVICE = -4   /* a HIP call failed; the handle is poisoned */
+} llm_status;
+
+typedef enum { LLM_F32 = 0, LLM_F16 = 1 } llm_dtype;
+
+/* Model hyper-parameters: the fields of ModelArgs (walkthrough section 3.1)
+ * plus the RoPE base (section 3.3) and the storage type.
+ *  n_kv_heads <= 0 means n_kv_heads = n_heads (MHA).
+ *  ffn_dim_multiplier <= 0 means None.  The FFN width is int(2*4*dim/3),
+ *    times the multiplier (int), rounded up to multiple_of (section 3.6).
+ *  max_batch_size x max_seq_len fixes the static KV cache extents.
+ *  dtype LLM_F16 stores weights, activations and cache in binary16 with fp32
+ *    accumulation; LLM_F32 stores them in binary32.
+ * Supported shapes: dim divisible by n_heads, n_heads by n_kv_heads,
+ * max_batch_size <= 4096.  LLM_F16 models need head_dim 128, dim and the
+ * FFN width multiples of 64, vocab_size a multiple of 16, max_seq_len a
+ * multiple of 64 and n_heads / n_kv_heads <= 16.  LLM_F32 models are limited
+ * to dim <= 4096 and max_seq_len <= 8192.  Other shapes give LLM_EINVAL. */
+typedef struct {
+    int32_t n_layers, dim, n_heads, n_kv_heads;
+    int32_t vocab_size, multiple_of;
+    float ffn_dim_multiplier;
+    float norm_eps, rope_theta;
+    int32_t max_batch_size, max_seq_len;
+    int32_t dtype;
+} llm_params;
+
+typedef struct llm llm_t;
+
+/* ---- sizing (host only, no GPU needed) -------------------------------- */
+
+/* FFN hidden width of the parameters (walkthrough section 3.6), or < 0. */
+int64_t llm_ffn_hidden(const llm_params *p);
+/* Bytes of the static KV cache: n_layers * 2 * max_batch * n_kv_heads *
+ * max_seq_len * head_dim * element size (walkthrough section 3.1). */
+int64_t llm_kv_cache_bytes(const llm_params *p);
+/* Bytes of all layer matrices plus the output head (what one decode step
+ * streams); the embedding table is gathered, not streamed, and excluded. */
+int64_t llm_weight_bytes(const llm_params *p);
+/* Check parameters without creating anything: LLM_OK or LLM_EINVAL. */
+int llm_check_params(const llm_params *p);
+
+/* ---- lifetime ---------------------------------------------------------- */
+
+/* Create a model on the current HIP device.  Every weight is drawn from the
+ * seeded generator (SplitMix64 streams per tensor, Irwin-Hall(4) normal with
+ * standard deviation 0.02, rounded once to the storage type); RMSNorm weights
+ * are 1.  The KV cache is zeroed.  `hip_stream` is a hipStream_t to order all
+ * work on, or NULL for a stream owned by the handle.
+ * Errors: LLM_EINVAL (parameters), LLM_ENOMEM, LLM_EDEVICE.  On error *out is
+ * NULL. */
+int llm_create(const llm_params *p, uint64_t seed, void *hip_stream, llm_t **out);
+
+/* A handle that validates arguments and tracks state exactly like a real
+ * one but allocates nothing and queues no GPU work; value-returning calls
+ * return LLM_ESTATE.  For checking the call protocol without a GPU. */
+int llm_create_dry(const llm_params *p, llm_t **out);
+
+void llm_destroy(llm_t *h);
+const char *llm_last_error(const llm_t *h);
+/* The hipStream_t all of the handle's work is ordered on (owned by the
+ * handle unless one was passed to llm_create); NULL for a dry handle. */
+void *llm_get_stream(llm_t *h);
+
+/* ---- the forward pass --------------------------------------------------- */
+
+/* Prefill (Transformer.forward(tokens, 0), walkthrough sections 2 and 3.8):
+ * tokens[B][T] row-major at positions 0..T-1 with the causal mask.  Writes
+ * the KV cache for positions [0, T), stores the tokens in the handle's token
+ * buffer tok[B][max_seq_len], and leaves fp32 logits[B][vocab] of position
+ * T-1.  Requires 1 <= B <= max_batch_size, 1 <= T <= max_seq_len, every
+ * token in [0, vocab).  Host tokens are copied before the call returns. */
+int llm_prefill(llm_t *h, const int32_t *tokens, int32_t B, int32_t T);
+int llm_prefill_d(llm_t *h, const int32_t *tokens_d, int32_t B, int32_t T);
+
+/* One decode step (seqlen 1, no mask: the course notes on generate,
+ * section 3): runs tok[:, prev_pos] at position prev_pos against cached keys
+ * 0..prev_pos, writes the KV cache at prev_pos, leaves logits of position
+ * prev_pos.  Requires a prior prefill, 1 <= prev_pos <= last_pos + 1,
+ * prev_pos < max_seq_len, and the token column prev_pos written (by the
+ * prefill, llm_sample or llm_set_tokens); else LLM_ESTATE / LLM_EINVAL. */
+int llm_decode(llm_t *h, int32_t prev_pos);
+
+/* Sample the next token of every row from the current logits (position
+ * last_pos): temperature <= 0 is greedy argmax (lowest id on ties);
+ * otherwise P = softmax(logits / temperature) in fp32 and top-p sampling
+ * (walkthrough section 4.3) made exact: tokens ordered by (P desc, id asc),
+ * Q_i = floor(P_i * 2^48), E_i = sum of Q before i, token i kept iff
+ * E_i <= floor(top_p * 2^48); with S the kept mass and U = floor(u * 2^24)
+ * the drawn token is the first kept i with E_{i+1} > floor(U * S / 2^24).
+ * uniforms[B] are in [0, 1).  The token is written to tok[:, last_pos + 1]
+ * when last_pos + 1 < max_seq_len and copied to out_tokens[B] when it is not
+ * NULL (then the call synchronises).  top_p must lie in (0, 1], temperature
+ * must be finite. */
+int llm_sample(llm_t *h, float temperature, float top_p, const float *uniforms,
+               int32_t *out_tokens);
+/* Same with uniforms and output in device memory; never synchronises.
+ * out_tokens_d may be NULL. */
+int llm_sample_d(llm_t *h, float temperature, float top_p, const float *uniforms_d,
+                 int32_t *out_tokens_d);
+
+/* The reference's prompt forcing, where(mask, prompt_token, sampled)
+ * (walkthrough section 4.2): tok[b][pos] = tokens[b] for every row b < B of
+ * the last prefill whose mask[b] is non-zero (mask NULL: all rows).
+ * Requires 0 <= pos < max_seq_len, tokens in [0, vocab). */
+int llm_set_tokens(llm_t *h, int32_t pos, const int32_t *tokens, const uint8_t *mask);
+
+/* Copy fp32 logits[B][vocab] of the last forward into host memory (syncs). */
+int llm_get_logits(llm_t *h, float *out);
+/* Same into device memory (async). */
+int llm_get_logits_d(llm_t *h, float *out_d);
+/* Copy the token buffer rows [0, B) columns [0, n_cols) into host memory as
+ * int32[B][n_cols] (syncs). */
+int llm_get_tokens(llm_t *h, int32_t n_cols, int32_t *out);
+
+/* Top-p draw on caller-supplied probabilities probs[B][vocab] (host, fp32)
+ * with the exact rule of llm_sample; out[B] receives the token ids (syncs).
+ * For checking the sampler on identical inputs. */
+int llm_sample_probs(llm_t *h, const float *probs, int32_t B, float top_p,
+                     const float *uniforms, int32_t *out);
+
+/* Wait for all queued work. */
+int llm_sync(llm_t *h);
+
+/* ---- inspection and single-operation entry points (device pointers) ----
+ * These run one kernel of the forward pass in isolation on the handle's
+ * stream, for parity checks of each step. */
+
+/* Read `count` logical elements [first, first+count) of a weight tensor in
+ * its logical row-major [out][in] order, as stored (uint16 binary16 bit
+ * patterns for LLM_F16, float for LLM_F32), into host memory.  Tensor ids:
+ * 0 tok_embeddings, 1 output head, 16 + 8*layer + {0 wq, 1 wk, 2 wv, 3 wo,
+ * 4 w1, 5 w2, 6 w3}. */
+int llm_read_weights(llm_t *h, int32_t tensor_id, int64_t first, int64_t count, void *out);
+
+/* y[M][dim] = RMSNorm(x[M][dim]) (walkthrough section 3.2) in the storage
+ * type. */
+int llm_op_rmsnorm(llm_t *h, const void *x_d, int32_t M, void *y_d);
+
+/* y[M][N] = round(W x) for one of the model's packed matrices, plain store:
+ *  mat 0: layer's [wq; wk; wv] (N = (n_heads + 2 n_kv_heads) * head_dim),
+ *  mat 1: layer's wo (N = dim), mat 2: layer's w1/w3 interleaved in blocks of
+ *  8 rows (packed row 16j + r is w1 row 8j + r for r < 8, w3 row 8j + r - 8
+ *  otherwise; N = 2 * ffn), mat 3: layer's w2 (N = dim), mat 4: output head
+ *  (N = vocab; layer ignored).  x is [M][K] in the storage type. */
+int llm_op_linear(llm_t *h, int32_t layer, int32_t mat, const void *x_d, int32_t M, void *y_d);
+
+/* Write caller K/V rows into the layer's cache: k_d, v_d are
+ * [B][T][n_kv_heads][head_dim] in the storage type, for positions
+ * pos0..pos0+T-1 of rows 0..B-1. */
+int llm_op_kv_write(llm_t *h, int32_t layer, const void *k_d, const void *v_d, int32_t B,
+                    int32_t T, int32_t pos0);
+
+/* Attention of q[B][T][n_heads][head_dim] at positions pos0..pos0+T-1 over
+ * the layer's cached keys 0..pos (causal), out in the same shape.  T == 1
+ * runs the split-K decode kernel, T > 1 with pos0 == 0 the causal prefill
+ * kernel. */
+int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_t T,
+                     int32_t pos0, void *out_d);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLM_H */

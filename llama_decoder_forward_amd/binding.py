@@ -1,0 +1,236 @@
+"""ctypes binding of libllm.so: the C ABI of include/llm.h under the same
+names.  Argument marshalling only -- every step of the forward pass runs in
+the library's HIP kernels.  Importing this module fails loudly when the
+library has not been built."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libllm.so")
+
+LLM_OK, LLM_EINVAL, LLM_ESTATE, LLM_ENOMEM, LLM_EDEVICE = 0, -1, -2, -3, -4
+LLM_F32, LLM_F16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m llama_decoder_forward_amd.build` "
+                      "(or __graft_entry__.build()); there is no fallback path")
+
+_lib = C.CDLL(LIB_PATH)
+
+
+class llm_params(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("dim", C.c_int32), ("n_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("vocab_size", C.c_int32), ("multiple_of", C.c_int32),
+                ("ffn_dim_multiplier", C.c_float), ("norm_eps", C.c_float),
+                ("rope_theta", C.c_float), ("max_batch_size", C.c_int32),
+                ("max_seq_len", C.c_int32), ("dtype", C.c_int32)]
+
+
+_vp = C.c_void_p
+_P = C.POINTER(llm_params)
+EXPORTS = {
+    "llm_ffn_hidden": (C.c_int64, [_P]),
+    "llm_kv_cache_bytes": (C.c_int64, [_P]),
+    "llm_weight_bytes": (C.c_int64, [_P]),
+    "llm_check_params": (C.c_int, [_P]),
+    "llm_create": (C.c_int, [_P, C.c_uint64, _vp, C.POINTER(_vp)]),
+    "llm_create_dry": (C.c_int, [_P, C.POINTER(_vp)]),
+    "llm_destroy": (None, [_vp]),
+    "llm_last_error": (C.c_char_p, [_vp]),
+    "llm_get_stream": (_vp, [_vp]),
+    "llm_prefill": (C.c_int, [_vp, _vp, C.c_int32, C.c_int32]),
+    "llm_prefill_d": (C.c_int, [_vp, _vp, C.c_int32, C.c_int32]),
+    "llm_decode": (C.c_int, [_vp, C.c_int32]),
+    "llm_sample": (C.c_int, [_vp, C.c_float, C.c_float, _vp, _vp]),
+    "llm_sample_d": (C.c_int, [_vp, C.c_float, C.c_float, _vp, _vp]),
+    "llm_set_tokens": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
+    "llm_get_logits": (C.c_int, [_vp, _vp]),
+    "llm_get_logits_d": (C.c_int, [_vp, _vp]),
+    "llm_get_tokens": (C.c_int, [_vp, C.c_int32, _vp]),
+    "llm_sample_probs": (C.c_int, [_vp, _vp, C.c_int32, C.c_float, _vp, _vp]),
+    "llm_sync": (C.c_int, [_vp]),
+    "llm_read_weights": (C.c_int, [_vp, C.c_int32, C.c_int64, C.c_int64, _vp]),
+    "llm_op_rmsnorm": (C.c_int, [_vp, _vp, C.c_int32, _vp]),
+    "llm_op_linear": (C.c_int, [_vp, C.c_int32, C.c_int32, _vp, C.c_int32, _vp]),
+    "llm_op_kv_write": (C.c_int, [_vp, C.c_int32, _vp, _vp, C.c_int32, C.c_int32, C.c_int32]),
+    "llm_op_attention": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32, C.c_int32, C.c_int32, _vp]),
+}
+for _name, (_res, _args) in EXPORTS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class LlmError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (status {code})")
+        self.code = code
+
+
+def _arr(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(C.c_void_p)
+
+
+def make_params(n_layers, dim, n_heads, n_kv_heads, vocab_size, multiple_of, ffn_dim_multiplier=0.0,
+                norm_eps=1e-5, rope_theta=10000.0, max_batch_size=1, max_seq_len=2048,
+                dtype=LLM_F16) -> llm_params:
+    return llm_params(n_layers, dim, n_heads, n_kv_heads, vocab_size, multiple_of,
+                      float(ffn_dim_multiplier or 0.0), norm_eps, rope_theta, max_batch_size,
+                      max_seq_len, dtype)
+
+
+def llm_ffn_hidden(p: llm_params) -> int:
+    return _lib.llm_ffn_hidden(C.byref(p))
+
+
+def llm_kv_cache_bytes(p: llm_params) -> int:
+    return _lib.llm_kv_cache_bytes(C.byref(p))
+
+
+def llm_weight_bytes(p: llm_params) -> int:
+    return _lib.llm_weight_bytes(C.byref(p))
+
+
+def llm_check_params(p: llm_params) -> int:
+    return _lib.llm_check_params(C.byref(p))
+
+
+class Handle:
+    """An llm_t* with the library's calls as methods (same names, minus the
+    prefix) and errors raised as LlmError."""
+
+    def __init__(self, ptr, params: llm_params):
+        self.ptr = ptr
+        self.params = params
+        self.B = 0
+
+    def _ck(self, rc):
+        if rc != LLM_OK:
+            msg = _lib.llm_last_error(self.ptr)
+            raise LlmError(rc, msg.decode() if msg else "error")
+        return rc
+
+    @property
+    def V(self):
+        return self.params.vocab_size
+
+    def stream(self) -> int:
+        return _lib.llm_get_stream(self.ptr) or 0
+
+    def prefill(self, tokens):
+        t, p = _arr(tokens, np.int32)
+        B, T = t.shape
+        self._ck(_lib.llm_prefill(self.ptr, p, B, T))
+        self.B = B
+
+    def prefill_d(self, tokens_ptr: int, B: int, T: int):
+        self._ck(_lib.llm_prefill_d(self.ptr, C.c_void_p(tokens_ptr), B, T))
+        self.B = B
+
+    def decode(self, prev_pos: int):
+        self._ck(_lib.llm_decode(self.ptr, prev_pos))
+
+    def sample(self, temperature: float, top_p: float = 1.0, uniforms=None, want_tokens=True):
+        up = None
+        if uniforms is not None:
+            u, up = _arr(uniforms, np.float32)
+        out = np.empty(self.B, np.int32) if want_tokens else None
+        self._ck(_lib.llm_sample(self.ptr, temperature, top_p, up,
+                                 out.ctypes.data_as(C.c_void_p) if want_tokens else None))
+        return out
+
+    def sample_d(self, temperature: float, top_p: float, uniforms_ptr: int, out_ptr: int = 0):
+        self._ck(_lib.llm_sample_d(self.ptr, temperature, top_p, C.c_void_p(uniforms_ptr or None),
+                                   C.c_void_p(out_ptr or None)))
+
+    def set_tokens(self, pos: int, tokens, mask=None):
+        t, tp = _arr(tokens, np.int32)
+        mp = None
+        if mask is not None:
+            m, mp = _arr(np.asarray(mask).astype(np.uint8), np.uint8)
+        self._ck(_lib.llm_set_tokens(self.ptr, pos, tp, mp))
+
+    def get_logits(self) -> np.ndarray:
+        out = np.empty((self.B, self.V), np.float32)
+        self._ck(_lib.llm_get_logits(self.ptr, out.ctypes.data_as(C.c_void_p)))
+        return out
+
+    def get_logits_d(self, out_ptr: int):
+        self._ck(_lib.llm_get_logits_d(self.ptr, C.c_void_p(out_ptr)))
+
+    def get_tokens(self, n_cols: int) -> np.ndarray:
+        out = np.empty((self.B, n_cols), np.int32)
+        self._ck(_lib.llm_get_tokens(self.ptr, n_cols, out.ctypes.data_as(C.c_void_p)))
+        return out
+
+    def sample_probs(self, probs, top_p: float, uniforms) -> np.ndarray:
+        p, pp = _arr(probs, np.float32)
+        u, up = _arr(uniforms, np.float32)
+        B = p.shape[0]
+        out = np.empty(B, np.int32)
+        self._ck(_lib.llm_sample_probs(self.ptr, pp, B, top_p, up, out.ctypes.data_as(C.c_void_p)))
+        return out
+
+    def sync(self):
+        self._ck(_lib.llm_sync(self.ptr))
+
+    def read_weights(self, tensor_id: int, first: int, count: int) -> np.ndarray:
+        dt = np.uint16 if self.params.dtype == LLM_F16 else np.float32
+        out = np.empty(count, dt)
+        self._ck(_lib.llm_read_weights(self.ptr, tensor_id, first, count, out.ctypes.data_as(C.c_void_p)))
+        return out
+
+    def op_rmsnorm(self, x_ptr: int, M: int, y_ptr: int):
+        self._ck(_lib.llm_op_rmsnorm(self.ptr, C.c_void_p(x_ptr), M, C.c_void_p(y_ptr)))
+
+    def op_linear(self, layer: int, mat: int, x_ptr: int, M: int, y_ptr: int):
+        self._ck(_lib.llm_op_linear(self.ptr, layer, mat, C.c_void_p(x_ptr), M, C.c_void_p(y_ptr)))
+
+    def op_kv_write(self, layer: int, k_ptr: int, v_ptr: int, B: int, T: int, pos0: int):
+        self._ck(_lib.llm_op_kv_write(self.ptr, layer, C.c_void_p(k_ptr), C.c_void_p(v_ptr), B, T, pos0))
+
+    def op_attention(self, layer: int, q_ptr: int, B: int, T: int, pos0: int, out_ptr: int):
+        self._ck(_lib.llm_op_attention(self.ptr, layer, C.c_void_p(q_ptr), B, T, pos0, C.c_void_p(out_ptr)))
+
+    def destroy(self):
+        if self.ptr:
+            _lib.llm_destroy(self.ptr)
+            self.ptr = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.destroy()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def llm_create(params: llm_params, seed: int, hip_stream: int | None = None) -> Handle:
+    out = C.c_void_p()
+    rc = _lib.llm_create(C.byref(params), seed, C.c_void_p(hip_stream or None), C.byref(out))
+    if rc != LLM_OK:
+        raise LlmError(rc, "llm_create failed")
+    return Handle(out, params)
+
+
+def llm_create_dry(params: llm_params) -> Handle:
+    out = C.c_void_p()
+    rc = _lib.llm_create_dry(C.byref(params), C.byref(out))
+    if rc != LLM_OK:
+        raise LlmError(rc, "llm_create_dry failed")
+    return Handle(out, params)
+
+
+def params_for(workload, max_batch_size=None, max_seq_len=None) -> llm_params:
+    """llm_params of a configs.Workload."""
+    return make_params(**workload.model_kwargs(max_batch_size, max_seq_len))

@@ -1,0 +1,422 @@
+// Scaled dot-product attention over the static KV cache (walkthrough
+// section 3.5 step 5): scores q.k / sqrt(d), the causal mask of section 3.8
+// (query at position p sees keys 0..p), softmax in fp32 with the maximum
+// subtracted, weighted sum of values; query head h reads KV head h / n_rep
+// (repeat_kv, section 3.4).
+//
+// Cache layout (per layer): K[b][kvh][s][d] (key-major), V[b][kvh][d][s]
+// (d-major).  Both kernels compute S^T = K Q^T and O^T = V^T P^T with
+// v_mfma_f32_16x16x32_f16, so the query is the MFMA column (lane % 16) and
+// each lane owns its query's running max / sum with no cross-lane moves.
+//
+// Key permutation: inside a 32-key step, row r of S^T sub-tile t (t = 0, 1)
+// is key 8*(r/4) + 4*t + r%4.  The accumulator lane group g then holds keys
+// 8g..8g+7 of the step, which is exactly the B-operand k-group of P^T, and
+// the matching A operand V^T[d][8g..8g+7] is one contiguous 16-byte load.
+#include "common.h"
+
+namespace {
+
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Key (0..31 within a step) held in row r of sub-tile t.
+__device__ __forceinline__ int perm_key(int t, int r) { return 8 * (r >> 2) + 4 * t + (r & 3); }
+
+constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp(m_old - m_new) is never NaN
+
+// ---------------------------------------------------------------------------
+// Decode: split-K over the attended length.  Grid (B*Hkv, ceil(S/256)); each
+// of the 4 waves handles 64 keys for all n_rep query heads of the KV head,
+// so every K/V byte is read once per query group.  Partials (unnormalised
+// o, running max, running sum) go to part[(b*H + h)][sub] and are merged in
+// sub order by attn_combine_kernel.
+// ---------------------------------------------------------------------------
+constexpr int DEC_KEYS_PER_WAVE = 64;
+
+__global__ __launch_bounds__(256) void attn_decode_kernel(const half_t *__restrict__ q,
+                                                          const half_t *__restrict__ kc,
+                                                          const half_t *__restrict__ vc, int H,
+                                                          int Hkv, int S, const int *pos_dev,
+                                                          int pos_imm, float *part, int nsub)
+{
+    const int hd = 128;
+    const int bk = blockIdx.x, b = bk / Hkv, kvh = bk % Hkv;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int L = (pos_dev ? *pos_dev : pos_imm) + 1;
+    const int sub = blockIdx.y * 4 + wave;
+    const int key0 = sub * DEC_KEYS_PER_WAVE;
+    if (key0 >= L) return;
+    const int n_rep = H / Hkv;
+    const int r = lane & 15, g = lane >> 4;
+    const bool qv = r < n_rep;
+    const int h = kvh * n_rep + r;
+    const float scale = 1.0f / sqrtf((float)hd);
+
+    // Q^T as B operand: column r (query head), k-group g over the 4 d-steps.
+    half8 qb[4];
+    const half8 z = {};
+    const half_t *qrow = q + ((int64_t)b * H + (qv ? h : 0)) * hd;
+#pragma unroll
+    for (int s = 0; s < 4; s++) qb[s] = qv ? *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g) : z;
+
+    const half_t *K = kc + ((int64_t)b * Hkv + kvh) * S * hd;
+    const half_t *V = vc + ((int64_t)b * Hkv + kvh) * hd * S;
+
+    floatx4 acc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float mrun = kNegBig, lrun = 0.f;
+
+    for (int st = 0; st < DEC_KEYS_PER_WAVE / 32; st++) {
+        const int k0 = key0 + 32 * st;
+        if (k0 >= L) break;
+        // S^T for the two permuted sub-tiles
+        floatx4 sc[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int key = k0 + perm_key(t, r);
+            const bool kv_ok = key < L;
+            const half_t *krow = K + (int64_t)(kv_ok ? key : 0) * hd + 8 * g;
+            floatx4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                half8 kf = kv_ok ? *reinterpret_cast<const half8 *>(krow + 32 * s) : z;
+                a = mfma16(kf, qb[s], a);
+            }
+            sc[t] = a;
+        }
+        // lane group g holds keys k0 + 8g + 4t + i for its query column
+        float p[8];
+        float mx = kNegBig;
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int key = k0 + 8 * g + 4 * t + i;
+                float v = key < L ? sc[t][i] * scale : -INFINITY;
+                p[4 * t + i] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(mrun, mx);
+        const float fac = expf(mrun - mnew);
+        float ls = 0.f;
+        half8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            float ev = expf(p[e] - mnew);
+            ls += ev;
+            pb[e] = (half_t)ev;
+        }
+        ls += __shfl_xor(ls, 16);
+        ls += __shfl_xor(ls, 32);
+        lrun = lrun * fac + ls;
+        mrun = mnew;
+        // O^T += V^T P^T over 8 d-tiles of 16
+        const int kk = k0 + 8 * g;
+        const bool vok = kk + 8 <= L;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) {
+            const half_t *vrow = V + (int64_t)(16 * dt + r) * S + kk;
+            half8 vf;
+            if (vok) {
+                vf = *reinterpret_cast<const half8 *>(vrow);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) vf[e] = (kk + e < L) ? vrow[e] : (half_t)0.f;
+            }
+            acc[dt] = mfma16(vf, pb, acc[dt] * fac);
+        }
+    }
+    if (!qv) return;
+    float *pp = part + (((int64_t)b * H + h) * nsub + sub) * (hd + 2);
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++)
+        *reinterpret_cast<float4 *>(pp + 16 * dt + 4 * g) =
+            make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (g == 0) {
+        pp[hd] = mrun;
+        pp[hd + 1] = lrun;
+    }
+}
+
+// Merge the per-wave partials of one (b, h) in sub order; out = round(o / l).
+__global__ void attn_combine_kernel(const float *part, int H, int nsub, const int *pos_dev,
+                                    int pos_imm, half_t *out)
+{
+    const int hd = 128;
+    const int bh = blockIdx.x, d = threadIdx.x;
+    const int L = (pos_dev ? *pos_dev : pos_imm) + 1;
+    const int used = (L + DEC_KEYS_PER_WAVE - 1) / DEC_KEYS_PER_WAVE;
+    const float *pp = part + (int64_t)bh * nsub * (hd + 2);
+    float M = kNegBig;
+    for (int s = 0; s < used; s++) M = fmaxf(M, pp[(int64_t)s * (hd + 2) + hd]);
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < used; s++) {
+        const float *p = pp + (int64_t)s * (hd + 2);
+        float w = expf(p[hd] - M);
+        num += w * p[d];
+        den += w * p[hd + 1];
+    }
+    out[(int64_t)bh * hd + d] = (half_t)(num / den);
+}
+
+// ---------------------------------------------------------------------------
+// Causal prefill (positions 0..T-1 of every row): flash-style online
+// softmax.  Grid (B*H, ceil(T/128)); 4 waves x 32 queries (two MFMA column
+// groups).  64-key tiles of K (in permuted operand order) and V^T are staged
+// in LDS with register prefetch of the next tile.  Tiles entirely above a
+// wave's last query are skipped; the diagonal tile is masked.
+// ---------------------------------------------------------------------------
+constexpr int PF_Q = 128, PF_K = 64;
+
+__global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restrict__ q,
+                                                           const half_t *__restrict__ kc,
+                                                           const half_t *__restrict__ vc, int T,
+                                                           int H, int Hkv, int S,
+                                                           half_t *__restrict__ out)
+{
+    const int hd = 128;
+    __shared__ half8 kl[PF_K * hd / 8];  // 4 sub-tiles x 4 d-steps x 64 lanes
+    __shared__ half8 vl[PF_K * hd / 8];  // 8 d-tiles x 2 key-steps x 64 lanes
+    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int kvh = h / (H / Hkv);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int q0 = blockIdx.y * PF_Q;
+    const int wq0 = q0 + 32 * wave;  // this wave's first query
+    const float scale = 1.0f / sqrtf((float)hd);
+    const half8 z = {};
+
+    half8 qb[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+        const int t = wq0 + 16 * c + r;
+        const half_t *qrow = q + (((int64_t)b * T + (t < T ? t : 0)) * H + h) * hd;
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+            qb[c][s] = t < T ? *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g) : z;
+    }
+
+    const half_t *K = kc + ((int64_t)b * Hkv + kvh) * S * hd;
+    const half_t *V = vc + ((int64_t)b * Hkv + kvh) * hd * S;
+
+    floatx4 acc[2][8];
+#pragma unroll
+    for (int c = 0; c < 2; c++)
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) acc[c][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float mrun[2] = {kNegBig, kNegBig}, lrun[2] = {0.f, 0.f};
+
+    const int qlast = min(q0 + PF_Q, T) - 1;
+    const int ntiles = qlast / PF_K + 1;
+
+    half8 rk[4], rv[4];
+    auto load_tile = [&](int kt) {
+        const int base = kt * PF_K;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int c = tid + 256 * j;
+            const int key = c >> 4, dch = c & 15;  // K: 64 keys x 16 chunks of 8 d
+            rk[j] = base + key < T ? *reinterpret_cast<const half8 *>(K + (int64_t)(base + key) * hd + dch * 8) : z;
+            const int d = c >> 3, kch = c & 7;     // V^T: 128 d x 8 chunks of 8 keys
+            rv[j] = base + kch * 8 + 8 <= T
+                        ? *reinterpret_cast<const half8 *>(V + (int64_t)d * S + base + kch * 8)
+                        : z;
+            if (base + kch * 8 < T && base + kch * 8 + 8 > T) {
+                half8 t8;
+                for (int e = 0; e < 8; e++)
+                    t8[e] = base + kch * 8 + e < T ? V[(int64_t)d * S + base + kch * 8 + e] : (half_t)0.f;
+                rv[j] = t8;
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int c = tid + 256 * j;
+            {
+                const int key = c >> 4, dch = c & 15;
+                const int ks = key >> 5, kap = key & 31;
+                const int t = (kap >> 2) & 1, rr = 4 * (kap >> 3) + (kap & 3);
+                const int s = dch >> 2, gg = dch & 3;
+                kl[((ks * 2 + t) * 4 + s) * 64 + rr + 16 * gg] = rk[j];
+            }
+            {
+                const int d = c >> 3, kch = c & 7;
+                const int ks = kch >> 2, gg = kch & 3;
+                vl[((d >> 4) * 2 + ks) * 64 + (d & 15) + 16 * gg] = rv[j];
+            }
+        }
+    };
+
+    load_tile(0);
+    for (int kt = 0; kt < ntiles; kt++) {
+        __syncthreads();  // previous tile's readers are done
+        store_tile();
+        __syncthreads();
+        if (kt + 1 < ntiles) load_tile(kt + 1);
+        const int kbase = kt * PF_K;
+        if (kbase > wq0 + 31) continue;  // all keys after this wave's queries
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            const int qi = wq0 + 16 * c + r;  // this lane's query position
+            float p[2][8];
+            float mx = kNegBig;
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    floatx4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; s++)
+                        a = mfma16(kl[((ks * 2 + t) * 4 + s) * 64 + lane], qb[c][s], a);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int key = kbase + 32 * ks + 8 * g + 4 * t + i;
+                        float v = key <= qi ? a[i] * scale : -INFINITY;
+                        p[ks][4 * t + i] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(mrun[c], mx);
+            const float fac = expf(mrun[c] - mnew);
+            float ls = 0.f;
+            half8 pb[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    float ev = expf(p[ks][e] - mnew);
+                    ls += ev;
+                    pb[ks][e] = (half_t)ev;
+                }
+            ls += __shfl_xor(ls, 16);
+            ls += __shfl_xor(ls, 32);
+            lrun[c] = lrun[c] * fac + ls;
+            mrun[c] = mnew;
+#pragma unroll
+            for (int dt = 0; dt < 8; dt++) {
+                floatx4 o = acc[c][dt] * fac;
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++) o = mfma16(vl[(dt * 2 + ks) * 64 + lane], pb[ks], o);
+                acc[c][dt] = o;
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+        const int t = wq0 + 16 * c + r;
+        if (t >= T) continue;
+        const float inv = 1.0f / lrun[c];
+        half_t *orow = out + (((int64_t)b * T + t) * H + h) * hd;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) {
+            half4 o;
+#pragma unroll
+            for (int i = 0; i < 4; i++) o[i] = (half_t)(acc[c][dt][i] * inv);
+            *reinterpret_cast<half4 *>(orow + 16 * dt + 4 * g) = o;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 models (small): one work-group per (b, h, query), scores in LDS.
+// ---------------------------------------------------------------------------
+__global__ void attn_f32_kernel(const float *q, const float *kc, const float *vc, int T, int H,
+                                int Hkv, int hd, int S, const int *pos_dev, int pos_imm, float *out)
+{
+    extern __shared__ float sh[];  // L scores
+    const int bh = blockIdx.x, b = bh / H, h = bh % H, t = blockIdx.y;
+    const int kvh = h / (H / Hkv);
+    const int pos = (pos_dev ? *pos_dev : pos_imm) + t;
+    const int L = pos + 1;
+    const float *qr = q + (((int64_t)b * T + t) * H + h) * hd;
+    const float *K = kc + ((int64_t)b * Hkv + kvh) * S * hd;
+    const float *V = vc + ((int64_t)b * Hkv + kvh) * hd * S;
+    const float scale = 1.0f / sqrtf((float)hd);
+    for (int j = threadIdx.x; j < L; j += blockDim.x) {
+        float s = 0.f;
+        for (int d = 0; d < hd; d++) s = fmaf(qr[d], K[(int64_t)j * hd + d], s);
+        sh[j] = s * scale;
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int j = 0; j < L; j++) mx = fmaxf(mx, sh[j]);
+    float sum = 0.f;
+    for (int j = 0; j < L; j++) sum += expf(sh[j] - mx);
+    for (int d = threadIdx.x; d < hd; d += blockDim.x) {
+        float o = 0.f;
+        for (int j = 0; j < L; j++) o = fmaf(expf(sh[j] - mx) / sum, V[(int64_t)d * S + j], o);
+        out[(((int64_t)b * T + t) * H + h) * hd + d] = o;
+    }
+}
+
+template <typename Tv>
+__global__ void kv_write_kernel(const Tv *k, const Tv *v, int T, int pos0, int Hkv, int hd, int S,
+                                Tv *kc, Tv *vc)
+{
+    // one thread per element of k[B][T][Hkv][hd]
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_row = (int64_t)T * Hkv * hd;
+    const int b = (int)(blockIdx.y);
+    if (i >= per_row) return;
+    const int d = (int)(i % hd), kvh = (int)((i / hd) % Hkv), t = (int)(i / ((int64_t)hd * Hkv));
+    const int pos = pos0 + t;
+    kc[(((int64_t)b * Hkv + kvh) * S + pos) * hd + d] = k[(int64_t)b * per_row + i];
+    vc[(((int64_t)b * Hkv + kvh) * hd + d) * S + pos] = v[(int64_t)b * per_row + i];
+}
+
+}  // namespace
+
+hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s)
+{
+    const int nsub = (a.S + DEC_KEYS_PER_WAVE - 1) / DEC_KEYS_PER_WAVE;
+    const int chunks = (a.S + 4 * DEC_KEYS_PER_WAVE - 1) / (4 * DEC_KEYS_PER_WAVE);
+    hipLaunchKernelGGL(attn_decode_kernel, dim3(a.B * a.Hkv, chunks), dim3(256), 0, s,
+                       (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache,
+                       a.H, a.Hkv, a.S, a.pos_dev, a.pos_imm, a.part, nsub);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.H), dim3(128), 0, s, (const float *)a.part,
+                       a.H, nsub, a.pos_dev, a.pos_imm, (half_t *)a.out);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.B * a.H, (a.T + PF_Q - 1) / PF_Q), dim3(256), 0,
+                       s, (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache,
+                       a.T, a.H, a.Hkv, a.S, (half_t *)a.out);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s)
+{
+    size_t sh = sizeof(float) * (size_t)a.S;
+    hipLaunchKernelGGL(attn_f32_kernel, dim3(a.B * a.H, a.T), dim3(64), sh, s, (const float *)a.q,
+                       (const float *)a.kcache, (const float *)a.vcache, a.T, a.H, a.Hkv, a.hd,
+                       a.S, a.pos_dev, a.pos_imm, (float *)a.out);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_write(const void *k, const void *v, int B, int T, int pos0, int Hkv, int hd,
+                           int S, int dtype, void *kcache, void *vcache, hipStream_t s)
+{
+    int64_t per_row = (int64_t)T * Hkv * hd;
+    dim3 grid((unsigned)((per_row + 255) / 256), B);
+    if (dtype == 1)
+        hipLaunchKernelGGL(kv_write_kernel<half_t>, grid, dim3(256), 0, s, (const half_t *)k,
+                           (const half_t *)v, T, pos0, Hkv, hd, S, (half_t *)kcache, (half_t *)vcache);
+    else
+        hipLaunchKernelGGL(kv_write_kernel<float>, grid, dim3(256), 0, s, (const float *)k,
+                           (const float *)v, T, pos0, Hkv, hd, S, (float *)kcache, (float *)vcache);
+    return hipGetLastError();
+}

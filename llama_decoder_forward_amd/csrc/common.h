@@ -1,0 +1,120 @@
+// Internal definitions shared by the HIP kernels and the host library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 half_t;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Weight layout
+//
+// fp16 matrices W[N][K] (logical out x in) are stored as 16 x 32 tiles of
+// 512 halves (1 KiB).  Tile (nt, kt) starts at (nt * K/32 + kt) * 512; inside
+// it, the 8 halves of lane l (l = 0..63) are W[16 nt + l%16][32 kt + 8 (l/16)
+// + e], e = 0..7, at offset 8 l.  This is the A-operand layout of
+// v_mfma_f32_16x16x32_f16, so one 16-byte load per lane fetches an MFMA
+// operand and a wave's 1 KiB load is contiguous.
+// fp32 matrices are plain row-major.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int64_t tiled_offset(int64_t n, int64_t k, int64_t K)
+{
+    int64_t nt = n >> 4, kt = k >> 5;
+    int64_t lane = (n & 15) + 16 * ((k & 31) >> 3);
+    return (nt * (K >> 5) + kt) * 512 + lane * 8 + (k & 7);
+}
+
+// Packed matrices of one layer, in stored row order.
+enum Mat { MAT_QKV = 0, MAT_O = 1, MAT_W13 = 2, MAT_W2 = 3, MAT_HEAD = 4, MAT_EMB = 5 };
+
+// Epilogue kinds applied to the fp32 accumulator of a linear layer.
+enum EpKind {
+    EP_STORE = 0,   // out[m][n] = round(acc)
+    EP_RESID = 1,   // res[m][n] = round(res[m][n] + round(acc))
+    EP_LOGITS = 2,  // out_f32[m][n] = round(acc) widened to fp32
+    EP_QKV = 3,     // RoPE on q and k, q to out, k/v to the KV cache
+    EP_SWIGLU = 4   // g[m][f] = round(round(silu(a)) * b) from interleaved rows
+};
+
+// Everything an epilogue needs; unused fields are ignored.
+struct Epilogue {
+    int kind;
+    void *out;            // STORE / RESID / LOGITS / QKV (q) / SWIGLU (g)
+    int64_t ldo;          // row stride of out in elements
+    // EP_QKV
+    void *kcache;         // this layer's K cache: [maxB][Hkv][S][hd]
+    void *vcache;         // this layer's V cache: [maxB][Hkv][hd][S]
+    const float *rope;    // [S][hd/2][2] cos, sin
+    const int *pos_dev;   // device position of token 0 (decode) or NULL
+    int pos_imm;          // position of token 0 when pos_dev is NULL
+    int T;                // tokens per batch row (m = b*T + t)
+    int H, Hkv, hd, S;
+};
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (each file defines its own); all return hipError_t.
+// ---------------------------------------------------------------------------
+struct GemmArgs {
+    const void *W;     // packed weights (tiled fp16 / row-major fp32)
+    const void *X;     // activations [M][K] (row stride ldx)
+    int64_t ldx;
+    int M, N, K;
+    Epilogue ep;
+    float *partials;   // split-K scratch for the skinny path
+    int *counters;     // per-n-tile arrival counters (zeroed, self-resetting)
+};
+
+hipError_t launch_gen_weights_f16(half_t *dst, int mat, int64_t N, int64_t K, uint64_t seed,
+                                  int layer, int H, int Hkv, int hd, int F, bool tiled,
+                                  hipStream_t s);
+hipError_t launch_gen_weights_f32(float *dst, int mat, int64_t N, int64_t K, uint64_t seed,
+                                  int layer, int H, int Hkv, int hd, int F, hipStream_t s);
+hipError_t launch_fill_f16(half_t *dst, int64_t n, float v, hipStream_t s);
+hipError_t launch_fill_f32(float *dst, int64_t n, float v, hipStream_t s);
+hipError_t launch_zero_bytes(void *dst, int64_t bytes, hipStream_t s);
+hipError_t launch_read_weights(const void *src, int dtype, int mat, int64_t N, int64_t K,
+                               int which, int H, int Hkv, int hd, int F, int64_t first,
+                               int64_t count, void *out, hipStream_t s);
+
+hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int B, int T,
+                        const int *pos_dev, int D, int dtype, void *x, hipStream_t s);
+hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int D, float eps,
+                          int dtype, void *y, hipStream_t s);
+
+hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s);
+hipError_t launch_linear_f32(const GemmArgs &a, hipStream_t s);
+
+struct AttnArgs {
+    const void *q;         // [B*T][H][hd]
+    const void *kcache;    // [maxB][Hkv][S][hd]
+    const void *vcache;    // [maxB][Hkv][hd][S]
+    void *out;             // [B*T][H][hd]
+    int B, T, H, Hkv, hd, S;
+    const int *pos_dev;    // decode: device position, else NULL
+    int pos_imm;
+    float *part;           // decode split-K partials
+    int max_chunks;
+};
+hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
+hipError_t launch_kv_write(const void *k, const void *v, int B, int T, int pos0, int Hkv, int hd,
+                           int S, int dtype, void *kcache, void *vcache, hipStream_t s);
+
+hipError_t launch_argmax(const float *logits, int B, int V, int32_t *tok, int64_t tok_ld,
+                         int write_col, int32_t *out, hipStream_t s);
+hipError_t launch_softmax_temp(const float *logits, int B, int V, float temperature,
+                               float *probs, hipStream_t s);
+hipError_t launch_top_p(const float *probs, int B, int V, float top_p, const float *uniforms,
+                        int32_t *tok, int64_t tok_ld, int write_col, int32_t *out,
+                        hipStream_t s);
+hipError_t launch_set_int(int *dst, int v, hipStream_t s);
+hipError_t launch_set_tokens(int32_t *tok, int64_t tok_ld, int B, int col, const int32_t *vals,
+                             const uint8_t *mask, hipStream_t s);
+
+// Attention split size for the decode kernel (keys per work-group).
+constexpr int ATTN_DEC_CHUNK = 256;

@@ -1,0 +1,360 @@
+// Linear layers of the decoder: Y = W X with fused epilogues.
+//
+// All projections of the layer (wq/wk/wv, wo, w1/w3, w2; walkthrough
+// sections 3.5-3.6) and the output head are bias-free matrix products with
+// fp32 accumulation, rounded once to fp16.  Their epilogues fuse the next
+// elementwise step of the layer: RoPE plus the KV-cache write after the QKV
+// projection (sections 3.3 and 3.5), the residual add after wo and w2
+// (section 3.7), silu(w1 x) * w3 x after the gate/up projection (section
+// 3.6), and the fp32 promotion of the logits (section 2).
+//
+// fp16 path: weights are tiled (see common.h) so that each lane's 16-byte
+// load is an A operand of v_mfma_f32_16x16x32_f16; the activation rows are
+// the B operand (column m = lane % 16).  The accumulator fragment of a lane
+// holds rows n0 + 4*(lane/16) + i, i = 0..3, of column m.
+#include "common.h"
+
+namespace {
+
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float r16(float x) { return (float)(half_t)x; }
+
+// Apply the epilogue to one accumulator fragment.  Every lane of the wave
+// must call this together (EP_SWIGLU exchanges values between lanes);
+// `valid` masks the stores of lanes whose column is past M or whose rows are
+// past N.
+__device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m, bool valid,
+                                              floatx4 acc, int lane)
+{
+#pragma clang fp contract(off)
+    const int g = lane >> 4;
+    const int n = n0 + 4 * g;
+    switch (ep.kind) {
+    case EP_STORE: {
+        if (!valid) break;
+        half4 o;
+        for (int i = 0; i < 4; i++) o[i] = (half_t)acc[i];
+        *reinterpret_cast<half4 *>((half_t *)ep.out + (int64_t)m * ep.ldo + n) = o;
+        break;
+    }
+    case EP_LOGITS: {
+        if (!valid) break;
+        float4 o = make_float4(r16(acc[0]), r16(acc[1]), r16(acc[2]), r16(acc[3]));
+        *reinterpret_cast<float4 *>((float *)ep.out + (int64_t)m * ep.ldo + n) = o;
+        break;
+    }
+    case EP_RESID: {
+        if (!valid) break;
+        half4 *p = reinterpret_cast<half4 *>((half_t *)ep.out + (int64_t)m * ep.ldo + n);
+        half4 r = *p, o;
+        for (int i = 0; i < 4; i++) o[i] = (half_t)((float)r[i] + r16(acc[i]));
+        *p = o;
+        break;
+    }
+    case EP_QKV: {
+        if (!valid) break;
+        const int hd = ep.hd, qrows = ep.H * hd, krows = ep.Hkv * hd;
+        const int pos = (ep.pos_dev ? *ep.pos_dev : ep.pos_imm) + m % ep.T;
+        const int b = m / ep.T;
+        if (n < qrows + krows) {
+            const int d0 = n % hd;  // multiple of 4: pairs (d0, d0+1), (d0+2, d0+3)
+            const float *cs = ep.rope + ((int64_t)pos * (hd / 2) + d0 / 2) * 2;
+            half4 o;
+            for (int p = 0; p < 2; p++) {
+                float a = r16(acc[2 * p]), bb = r16(acc[2 * p + 1]);
+                float c = cs[2 * p], s = cs[2 * p + 1];
+                float re = a * c - bb * s;
+                float im = a * s + bb * c;
+                o[2 * p] = (half_t)re;
+                o[2 * p + 1] = (half_t)im;
+            }
+            if (n < qrows) {
+                *reinterpret_cast<half4 *>((half_t *)ep.out + (int64_t)m * ep.ldo + n) = o;
+            } else {
+                const int kvh = (n - qrows) / hd;
+                half_t *kc = (half_t *)ep.kcache + (((int64_t)b * ep.Hkv + kvh) * ep.S + pos) * hd + d0;
+                *reinterpret_cast<half4 *>(kc) = o;
+            }
+        } else {
+            const int r = n - qrows - krows, kvh = r / hd, d0 = r % hd;
+            half_t *vc = (half_t *)ep.vcache + (((int64_t)b * ep.Hkv + kvh) * hd + d0) * ep.S + pos;
+            for (int i = 0; i < 4; i++) vc[(int64_t)i * ep.S] = (half_t)acc[i];
+        }
+        break;
+    }
+    case EP_SWIGLU: {
+        // packed rows 16j..16j+7 are w1 rows 8j.., rows 16j+8.. are w3 rows:
+        // lanes of groups 0/1 hold a, groups 2/3 hold the matching b.
+        float bv[4];
+        for (int i = 0; i < 4; i++) bv[i] = __shfl_xor(acc[i], 32);
+        if (!valid || g >= 2) break;
+        const int f0 = (n0 >> 4) * 8 + 4 * g;
+        half4 o;
+        for (int i = 0; i < 4; i++) {
+            float a = r16(acc[i]);
+            float s = r16(a / (1.0f + expf(-a)));
+            o[i] = (half_t)(s * r16(bv[i]));
+        }
+        *reinterpret_cast<half4 *>((half_t *)ep.out + (int64_t)m * ep.ldo + f0) = o;
+        break;
+    }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny product for M <= 32 rows (decode steps, short prompts): weight
+// streaming.  One work-group per 16-row tile of W; its NW waves split K into
+// contiguous ranges, each streaming 1 KiB tiles straight into VGPRs with U
+// loads in flight, and the fragments are summed in wave order through LDS.
+// ---------------------------------------------------------------------------
+template <int NW, int U>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__restrict__ W,
+                                                              const half_t *__restrict__ X,
+                                                              int64_t ldx, int M, int N, int K,
+                                                              Epilogue ep)
+{
+    __shared__ floatx4 red[NW][2][64];
+    const int nt = blockIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int KT = K >> 5;
+    const int kt0 = (KT * wave) / NW, kt1 = (KT * (wave + 1)) / NW;
+    const half8 *Wt = reinterpret_cast<const half8 *>(W) + (int64_t)nt * KT * 64 + lane;
+    const int mc = lane & 15, g = lane >> 4;
+    const bool two = M > 16;
+    const bool h0 = mc < M, h1 = mc + 16 < M;
+    const half_t *x0 = X + (int64_t)(h0 ? mc : 0) * ldx + 8 * g;
+    const half_t *x1 = X + (int64_t)(h1 ? mc + 16 : 0) * ldx + 8 * g;
+    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const half8 z = {};
+    for (int kt = kt0; kt < kt1; kt += U) {
+        half8 w[U], b0[U], b1[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) w[u] = (kt + u < kt1) ? Wt[(int64_t)(kt + u) * 64] : z;
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            b0[u] = (h0 && kt + u < kt1) ? *reinterpret_cast<const half8 *>(x0 + (kt + u) * 32) : z;
+        if (two) {
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                b1[u] = (h1 && kt + u < kt1) ? *reinterpret_cast<const half8 *>(x1 + (kt + u) * 32) : z;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) acc0 = mfma16(w[u], b0[u], acc0);
+        if (two) {
+#pragma unroll
+            for (int u = 0; u < U; u++) acc1 = mfma16(w[u], b1[u], acc1);
+        }
+    }
+    red[wave][0][lane] = acc0;
+    red[wave][1][lane] = acc1;
+    __syncthreads();
+    if (wave != 0) return;
+    floatx4 s0 = red[0][0][lane], s1 = red[0][1][lane];
+    for (int w = 1; w < NW; w++) {
+        s0 += red[w][0][lane];
+        s1 += red[w][1][lane];
+    }
+    epilogue_frag(ep, nt * 16, mc, h0, s0, lane);
+    if (two) epilogue_frag(ep, nt * 16, mc + 16, h1, s1, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Tiled product for M > 32 (prefill).  Block tile 128 (W rows) x 128 (tokens)
+// x 64 (K), four waves in a 2x2 arrangement, each owning 4x4 fragments.
+// W tiles are copied to LDS unchanged (their lane order is the operand
+// order); X rows are scattered into the same lane order.  Double-buffered
+// LDS with register prefetch of the next K slab.  Work-groups are remapped
+// so that the ones on one XCD (dispatch is round-robin over 8) take adjacent
+// tiles, and grouped GM token blocks at a time so W slabs are reused from
+// cache.
+// ---------------------------------------------------------------------------
+constexpr int BIG_BN = 128, BIG_BM = 128, BIG_GM = 8;
+
+__global__ __launch_bounds__(256) void gemm_big_kernel(const half_t *__restrict__ W,
+                                                       const half_t *__restrict__ X, int64_t ldx,
+                                                       int M, int N, int K, Epilogue ep)
+{
+    __shared__ half8 lw[2][16 * 64];
+    __shared__ half8 lx[2][16 * 64];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wn = wave >> 1, wm = wave & 1;
+    const int NB = (N + BIG_BN - 1) / BIG_BN, MB = (M + BIG_BM - 1) / BIG_BM;
+    const int total = NB * MB;
+
+    // XCD-aware remap of the dispatch index.
+    int pid = blockIdx.x;
+    {
+        int per = total / 8, rem = total % 8, xcd = pid % 8, local = pid / 8;
+        pid = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+    }
+    const int group = BIG_GM * NB;
+    const int first_mb = (pid / group) * BIG_GM;
+    const int gm = min(MB - first_mb, BIG_GM);
+    const int mb = first_mb + (pid % group) % gm;
+    const int nb = (pid % group) / gm;
+
+    const int KT = K >> 5, NT = N >> 4;
+    const half8 *Wv = reinterpret_cast<const half8 *>(W);
+    const half8 z = {};
+
+    half8 rw[4], rx[4];
+    auto load_slab = [&](int kb) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            int c = tid + 256 * j;
+            int ntl = c >> 7, within = c & 127;
+            int ntg = nb * 8 + ntl;
+            rw[j] = ntg < NT ? Wv[((int64_t)ntg * KT + kb * 2) * 64 + within] : z;
+            int m = c >> 3, ch = c & 7;
+            int mg = mb * BIG_BM + m;
+            rx[j] = mg < M ? *reinterpret_cast<const half8 *>(X + (int64_t)mg * ldx + kb * 64 + ch * 8) : z;
+        }
+    };
+    auto store_slab = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            int c = tid + 256 * j;
+            lw[buf][c] = rw[j];
+            int m = c >> 3, ch = c & 7;
+            int mt = m >> 4, kt = ch >> 2, ln = (m & 15) + 16 * (ch & 3);
+            lx[buf][(mt * 2 + kt) * 64 + ln] = rx[j];
+        }
+    };
+
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int nkb = K / 64;
+    load_slab(0);
+    store_slab(0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; kb++) {
+        const int cur = kb & 1;
+        if (kb + 1 < nkb) load_slab(kb + 1);
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+            half8 a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) a[i] = lw[cur][((wn * 4 + i) * 2 + kt) * 64 + lane];
+#pragma unroll
+            for (int j = 0; j < 4; j++) b[j] = lx[cur][((wm * 4 + j) * 2 + kt) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+        }
+        if (kb + 1 < nkb) store_slab(cur ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int n0 = (nb * 8 + wn * 4 + i) * 16;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int m = (mb * 8 + wm * 4 + j) * 16 + (lane & 15);
+            epilogue_frag(ep, n0, m, m < M && n0 < N, acc[i][j], lane);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 models: plain row-major weights, one thread per output unit (a row, a
+// RoPE pair, or a w1/w3 pair), fp32 accumulation in k order.
+// ---------------------------------------------------------------------------
+__device__ float dot_row_f32(const float *w, const float *x, int K)
+{
+    float s = 0.f;
+    for (int k = 0; k < K; k++) s = fmaf(w[k], x[k], s);
+    return s;
+}
+
+__global__ void linear_f32_kernel(const float *W, const float *X, int64_t ldx, int M, int N, int K,
+                                  Epilogue ep)
+{
+#pragma clang fp contract(off)
+    const int unit = blockIdx.x * blockDim.x + threadIdx.x;
+    const int m = blockIdx.y;
+    const float *x = X + (int64_t)m * ldx;
+    float *out = (float *)ep.out;
+    switch (ep.kind) {
+    case EP_STORE:
+    case EP_LOGITS:
+    case EP_RESID: {
+        if (unit >= N) return;
+        float a = dot_row_f32(W + (int64_t)unit * K, x, K);
+        float *o = out + (int64_t)m * ep.ldo + unit;
+        *o = ep.kind == EP_RESID ? *o + a : a;
+        break;
+    }
+    case EP_QKV: {
+        const int n = 2 * unit;
+        if (n >= N) return;
+        const int hd = ep.hd, qrows = ep.H * hd, krows = ep.Hkv * hd;
+        const int pos = (ep.pos_dev ? *ep.pos_dev : ep.pos_imm) + m % ep.T, b = m / ep.T;
+        float a = dot_row_f32(W + (int64_t)n * K, x, K);
+        float bb = dot_row_f32(W + (int64_t)(n + 1) * K, x, K);
+        if (n < qrows + krows) {
+            const int d0 = n % hd;
+            const float *cs = ep.rope + ((int64_t)pos * (hd / 2) + d0 / 2) * 2;
+            float re = a * cs[0] - bb * cs[1];
+            float im = a * cs[1] + bb * cs[0];
+            if (n < qrows) {
+                out[(int64_t)m * ep.ldo + n] = re;
+                out[(int64_t)m * ep.ldo + n + 1] = im;
+            } else {
+                float *kc = (float *)ep.kcache + (((int64_t)b * ep.Hkv + (n - qrows) / hd) * ep.S + pos) * hd + d0;
+                kc[0] = re;
+                kc[1] = im;
+            }
+        } else {
+            const int r = n - qrows - krows, kvh = r / hd, d0 = r % hd;
+            float *vc = (float *)ep.vcache + (((int64_t)b * ep.Hkv + kvh) * hd + d0) * ep.S + pos;
+            vc[0] = a;
+            vc[ep.S] = bb;
+        }
+        break;
+    }
+    case EP_SWIGLU: {
+        const int f = unit;
+        if (f >= N / 2) return;
+        const int ra = (f >> 3) * 16 + (f & 7);
+        float a = dot_row_f32(W + (int64_t)ra * K, x, K);
+        float b = dot_row_f32(W + (int64_t)(ra + 8) * K, x, K);
+        out[(int64_t)m * ep.ldo + f] = (a / (1.0f + expf(-a))) * b;
+        break;
+    }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
+{
+    if (a.M <= 0) return hipSuccess;
+    if (a.M <= 32) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<8, 8>), dim3(a.N / 16), dim3(512), 0, s,
+                           (const half_t *)a.W, (const half_t *)a.X, a.ldx, a.M, a.N, a.K, a.ep);
+    } else {
+        int NB = (a.N + BIG_BN - 1) / BIG_BN, MB = (a.M + BIG_BM - 1) / BIG_BM;
+        hipLaunchKernelGGL(gemm_big_kernel, dim3(NB * MB), dim3(256), 0, s, (const half_t *)a.W,
+                           (const half_t *)a.X, a.ldx, a.M, a.N, a.K, a.ep);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_f32(const GemmArgs &a, hipStream_t s)
+{
+    if (a.M <= 0) return hipSuccess;
+    int units = (a.ep.kind == EP_QKV || a.ep.kind == EP_SWIGLU) ? a.N / 2 : a.N;
+    hipLaunchKernelGGL(linear_f32_kernel, dim3((units + 63) / 64, a.M), dim3(64), 0, s,
+                       (const float *)a.W, (const float *)a.X, a.ldx, a.M, a.N, a.K, a.ep);
+    return hipGetLastError();
+}

@@ -1,0 +1,858 @@
+// Host side of the library: parameter checks, call-protocol state, device
+// memory plan, and the order of kernels for a prefill and a decode step.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/llm.h"
+#include "common.h"
+
+namespace {
+
+struct Dims {
+    int NL, D, H, Hkv, hd, F, V, maxB, S, dtype, es;
+    int64_t Nqkv;
+};
+
+int64_t ffn_width(const llm_params *p)
+{
+    // walkthrough section 3.6: int(2 * 4d / 3), optional int(mult * h), round
+    // up to multiple_of
+    int64_t h = 4 * (int64_t)p->dim;
+    h = (int64_t)(2.0 * (double)h / 3.0);
+    if (p->ffn_dim_multiplier > 0.0f) h = (int64_t)((double)p->ffn_dim_multiplier * (double)h);
+    int64_t mo = p->multiple_of;
+    return mo * ((h + mo - 1) / mo);
+}
+
+std::string check(const llm_params *p, Dims *d)
+{
+    if (!p) return "params is NULL";
+    if (p->n_layers < 1) return "n_layers must be >= 1";
+    if (p->dim < 2 || p->n_heads < 1 || p->dim % p->n_heads) return "dim must be a positive multiple of n_heads";
+    int Hkv = p->n_kv_heads > 0 ? p->n_kv_heads : p->n_heads;
+    if (Hkv > p->n_heads || p->n_heads % Hkv) return "n_heads must be a multiple of n_kv_heads";
+    if (p->vocab_size < 2) return "vocab_size must be >= 2";
+    if (p->multiple_of < 1) return "multiple_of must be >= 1";
+    if (!(p->norm_eps > 0.f) || !std::isfinite(p->norm_eps)) return "norm_eps must be positive";
+    if (!(p->rope_theta > 0.f) || !std::isfinite(p->rope_theta)) return "rope_theta must be positive";
+    if (!std::isfinite(p->ffn_dim_multiplier)) return "ffn_dim_multiplier must be finite";
+    if (p->max_batch_size < 1 || p->max_batch_size > 4096) return "max_batch_size must be in [1, 4096]";
+    if (p->max_seq_len < 1) return "max_seq_len must be >= 1";
+    if (p->dtype != LLM_F16 && p->dtype != LLM_F32) return "dtype must be LLM_F16 or LLM_F32";
+    int hd = p->dim / p->n_heads;
+    if (hd % 2) return "head_dim must be even (RoPE pairs)";
+    int64_t F = ffn_width(p);
+    if (F < 1 || F > (1 << 24)) return "ffn width out of range";
+    if (p->dtype == LLM_F16) {
+        if (hd != 128) return "fp16 models need head_dim 128";
+        if (p->dim % 64) return "fp16 models need dim % 64 == 0";
+        if (F % 64) return "fp16 models need the ffn width to be a multiple of 64";
+        if (p->vocab_size % 16) return "fp16 models need vocab_size % 16 == 0";
+        if (p->max_seq_len % 64) return "fp16 models need max_seq_len % 64 == 0";
+        if (p->n_heads / Hkv > 16) return "fp16 models need n_heads / n_kv_heads <= 16";
+    } else {
+        if (p->dim > 4096) return "fp32 models are limited to dim <= 4096";
+        if (p->max_seq_len > 8192) return "fp32 models are limited to max_seq_len <= 8192";
+    }
+    if (p->vocab_size > (1 << 22)) return "vocab_size too large";
+    if (d) {
+        d->NL = p->n_layers; d->D = p->dim; d->H = p->n_heads; d->Hkv = Hkv; d->hd = hd;
+        d->F = (int)F; d->V = p->vocab_size; d->maxB = p->max_batch_size; d->S = p->max_seq_len;
+        d->dtype = p->dtype; d->es = p->dtype == LLM_F16 ? 2 : 4;
+        d->Nqkv = (int64_t)(p->n_heads + 2 * Hkv) * hd;
+    }
+    return "";
+}
+
+inline int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
+
+}  // namespace
+
+struct llm {
+    llm_params p{};
+    Dims d{};
+    bool dry = false;
+    hipStream_t stream = nullptr;
+    bool own_stream = false;
+    // weights
+    char *emb = nullptr, *wts = nullptr, *norm_w = nullptr;
+    std::vector<char *> wqkv, wo, w13, w2;
+    char *whead = nullptr;
+    // cache and buffers
+    char *kv = nullptr;
+    int64_t kv_layer_bytes = 0;  // K part then V part
+    float *rope = nullptr;
+    int32_t *tok = nullptr;
+    float *logits = nullptr, *probs = nullptr, *uni = nullptr, *attn_part = nullptr;
+    int32_t *outtok = nullptr, *stage_i32 = nullptr;
+    uint8_t *stage_mask = nullptr;
+    int *pos_dev = nullptr;
+    // activations, sized for ws_rows rows
+    char *ws = nullptr;
+    int64_t ws_rows = 0;
+    char *x = nullptr, *xn = nullptr, *q = nullptr, *o = nullptr, *g = nullptr;
+    // state
+    bool prefilled = false, logits_valid = false, poisoned = false;
+    int cur_B = 0, last_pos = -1;
+    std::vector<uint8_t> col_written;
+    std::string err;
+    // decode graph
+    hipGraphExec_t gexec = nullptr;
+    int graph_B = -1;
+    bool use_graph = true;
+};
+
+namespace {
+
+int fail(llm_t *h, int code, const std::string &msg)
+{
+    if (h) {
+        h->err = msg;
+        if (code == LLM_EDEVICE) h->poisoned = true;
+    }
+    return code;
+}
+
+#define HIPC(h, call)                                                                        \
+    do {                                                                                     \
+        hipError_t e_ = (call);                                                              \
+        if (e_ != hipSuccess)                                                                \
+            return fail((h), LLM_EDEVICE, std::string(#call) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+#define HIPM(h, call)                                                                       \
+    do {                                                                                    \
+        hipError_t e_ = (call);                                                             \
+        if (e_ == hipErrorOutOfMemory) {                                                    \
+            (void)hipGetLastError();                                                        \
+            return fail((h), LLM_ENOMEM, std::string(#call) + ": out of device memory");    \
+        }                                                                                   \
+        if (e_ != hipSuccess)                                                               \
+            return fail((h), LLM_EDEVICE, std::string(#call) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+int guard(llm_t *h)
+{
+    if (!h) return LLM_EINVAL;
+    if (h->poisoned) return LLM_EDEVICE;
+    return LLM_OK;
+}
+
+char *layer_kc(llm_t *h, int l) { return h->kv + (int64_t)l * h->kv_layer_bytes; }
+char *layer_vc(llm_t *h, int l) { return h->kv + (int64_t)l * h->kv_layer_bytes + h->kv_layer_bytes / 2; }
+
+// Activation workspace for `rows` token rows (grows, never shrinks).
+int ensure_ws(llm_t *h, int64_t rows)
+{
+    if (rows <= h->ws_rows) return LLM_OK;
+    const Dims &d = h->d;
+    int64_t bx = align256(rows * d.D * d.es), bq = align256(rows * (int64_t)d.H * d.hd * d.es),
+            bg = align256(rows * (int64_t)d.F * d.es);
+    if (h->ws) {
+        HIPC(h, hipStreamSynchronize(h->stream));
+        HIPC(h, hipFree(h->ws));
+        h->ws = nullptr;
+        h->ws_rows = 0;
+    }
+    void *p = nullptr;
+    HIPM(h, hipMalloc(&p, 2 * bx + 2 * bq + bg));
+    h->ws = (char *)p;
+    h->x = h->ws;
+    h->xn = h->x + bx;
+    h->q = h->xn + bx;
+    h->o = h->q + bq;
+    h->g = h->o + bq;
+    h->ws_rows = rows;
+    // the captured decode graph holds the old addresses
+    if (h->gexec) {
+        (void)hipGraphExecDestroy(h->gexec);
+        h->gexec = nullptr;
+        h->graph_B = -1;
+    }
+    return LLM_OK;
+}
+
+int64_t mat_rows(const Dims &d, int mat)
+{
+    switch (mat) {
+    case MAT_QKV: return d.Nqkv;
+    case MAT_O: return d.D;
+    case MAT_W13: return 2 * (int64_t)d.F;
+    case MAT_W2: return d.D;
+    default: return d.V;
+    }
+}
+
+int64_t mat_cols(const Dims &d, int mat)
+{
+    switch (mat) {
+    case MAT_O: return (int64_t)d.H * d.hd;
+    case MAT_W2: return d.F;
+    default: return d.D;
+    }
+}
+
+const char *mat_ptr(llm_t *h, int layer, int mat)
+{
+    switch (mat) {
+    case MAT_QKV: return h->wqkv[layer];
+    case MAT_O: return h->wo[layer];
+    case MAT_W13: return h->w13[layer];
+    case MAT_W2: return h->w2[layer];
+    case MAT_HEAD: return h->whead;
+    default: return h->emb;
+    }
+}
+
+hipError_t run_linear(llm_t *h, int layer, int mat, const void *X, int64_t ldx, int M,
+                      const Epilogue &ep)
+{
+    GemmArgs a{};
+    a.W = mat_ptr(h, layer, mat);
+    a.X = X;
+    a.ldx = ldx;
+    a.M = M;
+    a.N = (int)mat_rows(h->d, mat);
+    a.K = (int)mat_cols(h->d, mat);
+    a.ep = ep;
+    return h->d.dtype == LLM_F16 ? launch_gemm_f16(a, h->stream) : launch_linear_f32(a, h->stream);
+}
+
+Epilogue make_ep(int kind, void *out, int64_t ldo)
+{
+    Epilogue e{};
+    e.kind = kind;
+    e.out = out;
+    e.ldo = ldo;
+    e.T = 1;
+    return e;
+}
+
+// The forward pass over B rows of T tokens (walkthrough sections 2, 3.5-3.8).
+// Decode (pos_dev != NULL, T == 1) reads its position from device memory so
+// that the launch sequence can be captured once and replayed.
+hipError_t forward(llm_t *h, int B, int T, const int *pos_dev)
+{
+    const Dims &d = h->d;
+    const int M = B * T;
+    const int64_t qd = (int64_t)d.H * d.hd;
+    hipStream_t s = h->stream;
+    hipError_t e;
+#define TRY(x)                        \
+    do {                              \
+        if ((e = (x)) != hipSuccess) \
+            return e;                 \
+    } while (0)
+    TRY(launch_embed(h->emb, h->tok, d.S, B, T, pos_dev, d.D, d.dtype, h->x, s));
+    for (int l = 0; l < d.NL; l++) {
+        const char *nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
+        const char *nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
+        // attention_norm -> wq|wk|wv with RoPE and the KV-cache write
+        TRY(launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s));
+        Epilogue eq = make_ep(EP_QKV, h->q, qd);
+        eq.kcache = layer_kc(h, l);
+        eq.vcache = layer_vc(h, l);
+        eq.rope = h->rope;
+        eq.pos_dev = pos_dev;
+        eq.pos_imm = 0;
+        eq.T = T;
+        eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = d.S;
+        TRY(run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq));
+        // attention over the cache
+        AttnArgs aa{};
+        aa.q = h->q; aa.kcache = eq.kcache; aa.vcache = eq.vcache; aa.out = h->o;
+        aa.B = B; aa.T = T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
+        aa.pos_dev = pos_dev; aa.pos_imm = 0; aa.part = h->attn_part;
+        if (d.dtype == LLM_F32) TRY(launch_attn_f32(aa, s));
+        else if (pos_dev) TRY(launch_attn_decode_f16(aa, s));
+        else TRY(launch_attn_prefill_f16(aa, s));
+        // wo + residual
+        TRY(run_linear(h, l, MAT_O, h->o, qd, M, make_ep(EP_RESID, h->x, d.D)));
+        // ffn_norm -> w1|w3 with SwiGLU -> w2 + residual
+        TRY(launch_rmsnorm(h->x, d.D, nw_ffn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s));
+        TRY(run_linear(h, l, MAT_W13, h->xn, d.D, M, make_ep(EP_SWIGLU, h->g, d.F)));
+        TRY(run_linear(h, l, MAT_W2, h->g, d.F, M, make_ep(EP_RESID, h->x, d.D)));
+    }
+    // final norm on the last position of each row, output head, fp32 logits
+    const char *nw_final = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
+    TRY(launch_rmsnorm(h->x + (int64_t)(T - 1) * d.D * d.es, (int64_t)T * d.D, nw_final, B, d.D,
+                       h->p.norm_eps, d.dtype, h->xn, s));
+    TRY(run_linear(h, 0, MAT_HEAD, h->xn, d.D, B, make_ep(EP_LOGITS, h->logits, d.V)));
+#undef TRY
+    return hipSuccess;
+}
+
+void rope_table_host(int hd, int S, float base, std::vector<float> &t)
+{
+    // walkthrough section 3.3: theta_i = base^(-2i/d); angle = m * theta_i in
+    // fp32; cos and sin of the fp32 angle rounded to fp32.
+    const int half = hd / 2;
+    t.assign((size_t)S * half * 2, 0.f);
+    for (int i = 0; i < half; i++) {
+        float th = (float)(1.0 / std::pow((double)base, (double)(2 * i) / (double)hd));
+        for (int m = 0; m < S; m++) {
+            float ang = (float)m * th;
+            t[((size_t)m * half + i) * 2 + 0] = (float)std::cos((double)ang);
+            t[((size_t)m * half + i) * 2 + 1] = (float)std::sin((double)ang);
+        }
+    }
+}
+
+int build_weights(llm_t *h, uint64_t seed)
+{
+    const Dims &d = h->d;
+    hipStream_t s = h->stream;
+    const int mats[4] = {MAT_QKV, MAT_O, MAT_W13, MAT_W2};
+    for (int l = 0; l < d.NL; l++) {
+        char *ptrs[4] = {h->wqkv[l], h->wo[l], h->w13[l], h->w2[l]};
+        for (int i = 0; i < 4; i++) {
+            int64_t N = mat_rows(d, mats[i]), K = mat_cols(d, mats[i]);
+            if (d.dtype == LLM_F16)
+                HIPC(h, launch_gen_weights_f16((half_t *)ptrs[i], mats[i], N, K, seed, l, d.H, d.Hkv,
+                                               d.hd, d.F, true, s));
+            else
+                HIPC(h, launch_gen_weights_f32((float *)ptrs[i], mats[i], N, K, seed, l, d.H, d.Hkv,
+                                               d.hd, d.F, s));
+        }
+    }
+    if (d.dtype == LLM_F16) {
+        HIPC(h, launch_gen_weights_f16((half_t *)h->whead, MAT_HEAD, d.V, d.D, seed, 0, d.H, d.Hkv,
+                                       d.hd, d.F, true, s));
+        HIPC(h, launch_gen_weights_f16((half_t *)h->emb, MAT_EMB, d.V, d.D, seed, 0, d.H, d.Hkv, d.hd,
+                                       d.F, false, s));
+        HIPC(h, launch_fill_f16((half_t *)h->norm_w, (int64_t)(2 * d.NL + 1) * d.D, 1.0f, s));
+    } else {
+        HIPC(h, launch_gen_weights_f32((float *)h->whead, MAT_HEAD, d.V, d.D, seed, 0, d.H, d.Hkv,
+                                       d.hd, d.F, s));
+        HIPC(h, launch_gen_weights_f32((float *)h->emb, MAT_EMB, d.V, d.D, seed, 0, d.H, d.Hkv, d.hd,
+                                       d.F, s));
+        HIPC(h, launch_fill_f32((float *)h->norm_w, (int64_t)(2 * d.NL + 1) * d.D, 1.0f, s));
+    }
+    return LLM_OK;
+}
+
+int create_impl(llm_t *h, uint64_t seed)
+{
+    const Dims &d = h->d;
+    // weights: every layer matrix and the head in one allocation
+    const int mats[4] = {MAT_QKV, MAT_O, MAT_W13, MAT_W2};
+    int64_t per_layer = 0, offs[4];
+    for (int i = 0; i < 4; i++) {
+        offs[i] = per_layer;
+        per_layer += align256(mat_rows(d, mats[i]) * mat_cols(d, mats[i]) * d.es);
+    }
+    int64_t head_bytes = align256((int64_t)d.V * d.D * d.es);
+    void *p = nullptr;
+    HIPM(h, hipMalloc(&p, per_layer * d.NL + head_bytes));
+    h->wts = (char *)p;
+    h->wqkv.resize(d.NL); h->wo.resize(d.NL); h->w13.resize(d.NL); h->w2.resize(d.NL);
+    for (int l = 0; l < d.NL; l++) {
+        char *b = h->wts + (int64_t)l * per_layer;
+        h->wqkv[l] = b + offs[0]; h->wo[l] = b + offs[1]; h->w13[l] = b + offs[2]; h->w2[l] = b + offs[3];
+    }
+    h->whead = h->wts + per_layer * d.NL;
+    HIPM(h, hipMalloc(&p, align256((int64_t)d.V * d.D * d.es)));
+    h->emb = (char *)p;
+    HIPM(h, hipMalloc(&p, align256((int64_t)(2 * d.NL + 1) * d.D * d.es)));
+    h->norm_w = (char *)p;
+    // static KV cache (walkthrough section 3.1), zeroed
+    h->kv_layer_bytes = 2 * (int64_t)d.maxB * d.Hkv * d.S * d.hd * d.es;
+    HIPM(h, hipMalloc(&p, h->kv_layer_bytes * d.NL));
+    h->kv = (char *)p;
+    HIPC(h, launch_zero_bytes(h->kv, h->kv_layer_bytes * d.NL, h->stream));
+    // RoPE table
+    std::vector<float> rt;
+    rope_table_host(d.hd, d.S, h->p.rope_theta, rt);
+    HIPM(h, hipMalloc(&p, rt.size() * sizeof(float)));
+    h->rope = (float *)p;
+    HIPC(h, hipMemcpyAsync(h->rope, rt.data(), rt.size() * sizeof(float), hipMemcpyHostToDevice, h->stream));
+    // token buffer, logits, sampler and attention scratch
+    HIPM(h, hipMalloc(&p, (int64_t)d.maxB * d.S * sizeof(int32_t)));
+    h->tok = (int32_t *)p;
+    HIPC(h, launch_zero_bytes(h->tok, (int64_t)d.maxB * d.S * sizeof(int32_t), h->stream));
+    HIPM(h, hipMalloc(&p, (int64_t)d.maxB * d.V * sizeof(float)));
+    h->logits = (float *)p;
+    HIPM(h, hipMalloc(&p, (int64_t)d.maxB * d.V * sizeof(float)));
+    h->probs = (float *)p;
+    HIPM(h, hipMalloc(&p, 256 + (int64_t)d.maxB * (sizeof(float) + 2 * sizeof(int32_t) + 1)));
+    h->pos_dev = (int *)p;
+    h->uni = (float *)((char *)p + 64);
+    h->outtok = (int32_t *)(h->uni + d.maxB);
+    h->stage_i32 = h->outtok + d.maxB;
+    h->stage_mask = (uint8_t *)(h->stage_i32 + d.maxB);
+    const int nsub = (d.S + 63) / 64;
+    if (d.dtype == LLM_F16) {
+        HIPM(h, hipMalloc(&p, (int64_t)d.maxB * d.H * nsub * (d.hd + 2) * sizeof(float)));
+        h->attn_part = (float *)p;
+    }
+    int rc = ensure_ws(h, d.maxB);
+    if (rc) return rc;
+    rc = build_weights(h, seed);
+    if (rc) return rc;
+    HIPC(h, hipStreamSynchronize(h->stream));
+    return LLM_OK;
+}
+
+void release(llm_t *h)
+{
+    if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
+    void *bufs[] = {h->wts, h->emb, h->norm_w, h->kv, h->rope, h->tok, h->logits, h->probs,
+                    h->pos_dev, h->attn_part, h->ws};
+    for (void *b : bufs)
+        if (b) (void)hipFree(b);
+    if (h->own_stream && h->stream) (void)hipStreamDestroy(h->stream);
+}
+
+bool tokens_ok(const int32_t *t, int64_t n, int V)
+{
+    for (int64_t i = 0; i < n; i++)
+        if (t[i] < 0 || t[i] >= V) return false;
+    return true;
+}
+
+int after_forward(llm_t *h, hipError_t e)
+{
+    if (e != hipSuccess) return fail(h, LLM_EDEVICE, std::string("kernel launch: ") + hipGetErrorString(e));
+    return LLM_OK;
+}
+
+int prefill_common(llm_t *h, int B, int T)
+{
+    if (!h->dry) {
+        int rc = ensure_ws(h, (int64_t)B * T);
+        if (rc) return rc;
+        hipError_t e = forward(h, B, T, nullptr);
+        rc = after_forward(h, e);
+        if (rc) return rc;
+    }
+    h->prefilled = true;
+    h->logits_valid = true;
+    h->cur_B = B;
+    h->last_pos = T - 1;
+    std::fill(h->col_written.begin(), h->col_written.end(), 0);
+    std::fill(h->col_written.begin(), h->col_written.begin() + T, 1);
+    return LLM_OK;
+}
+
+int check_prefill_args(llm_t *h, int B, int T)
+{
+    if (B < 1 || B > h->d.maxB) return fail(h, LLM_EINVAL, "B must be in [1, max_batch_size]");
+    if (T < 1 || T > h->d.S) return fail(h, LLM_EINVAL, "T must be in [1, max_seq_len]");
+    return LLM_OK;
+}
+
+int sample_common(llm_t *h, float temperature, float top_p, const float *uniforms_d, bool have_u,
+                  int32_t *out_d)
+{
+    const Dims &d = h->d;
+    if (!h->logits_valid) return fail(h, LLM_ESTATE, "no logits: run llm_prefill or llm_decode first");
+    if (!std::isfinite(temperature)) return fail(h, LLM_EINVAL, "temperature must be finite");
+    if (temperature > 0.f) {
+        if (!(top_p > 0.f && top_p <= 1.f)) return fail(h, LLM_EINVAL, "top_p must be in (0, 1]");
+        if (!have_u) return fail(h, LLM_EINVAL, "uniforms are required when temperature > 0");
+    }
+    const int col = h->last_pos + 1 < d.S ? h->last_pos + 1 : -1;
+    if (!h->dry) {
+        hipError_t e;
+        if (temperature <= 0.f) {
+            e = launch_argmax(h->logits, h->cur_B, d.V, h->tok, d.S, col, out_d, h->stream);
+        } else {
+            e = launch_softmax_temp(h->logits, h->cur_B, d.V, temperature, h->probs, h->stream);
+            if (e == hipSuccess)
+                e = launch_top_p(h->probs, h->cur_B, d.V, top_p, uniforms_d, h->tok, d.S, col, out_d,
+                                 h->stream);
+        }
+        int rc = after_forward(h, e);
+        if (rc) return rc;
+    }
+    if (col >= 0) h->col_written[col] = 1;
+    return LLM_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+int64_t llm_ffn_hidden(const llm_params *p)
+{
+    if (!check(p, nullptr).empty()) return -1;
+    return ffn_width(p);
+}
+
+int64_t llm_kv_cache_bytes(const llm_params *p)
+{
+    Dims d;
+    if (!check(p, &d).empty()) return -1;
+    return (int64_t)d.NL * 2 * d.maxB * d.Hkv * d.S * d.hd * d.es;
+}
+
+int64_t llm_weight_bytes(const llm_params *p)
+{
+    Dims d;
+    if (!check(p, &d).empty()) return -1;
+    int64_t per_layer = d.Nqkv * d.D + (int64_t)d.D * d.H * d.hd + 3 * (int64_t)d.F * d.D;
+    return d.es * (d.NL * per_layer + (int64_t)d.V * d.D);
+}
+
+int llm_check_params(const llm_params *p) { return check(p, nullptr).empty() ? LLM_OK : LLM_EINVAL; }
+
+static llm_t *new_handle(const llm_params *p, const Dims &d)
+{
+    llm_t *h = new (std::nothrow) llm_t();
+    if (!h) return nullptr;
+    h->p = *p;
+    h->d = d;
+    h->col_written.assign(d.S, 0);
+    const char *ng = std::getenv("LLM_NO_GRAPH");
+    h->use_graph = !(ng && ng[0] == '1');
+    return h;
+}
+
+int llm_create_dry(const llm_params *p, llm_t **out)
+{
+    if (!out) return LLM_EINVAL;
+    *out = nullptr;
+    Dims d;
+    if (!check(p, &d).empty()) return LLM_EINVAL;
+    llm_t *h = new_handle(p, d);
+    if (!h) return LLM_ENOMEM;
+    h->dry = true;
+    *out = h;
+    return LLM_OK;
+}
+
+int llm_create(const llm_params *p, uint64_t seed, void *hip_stream, llm_t **out)
+{
+    if (!out) return LLM_EINVAL;
+    *out = nullptr;
+    Dims d;
+    std::string why = check(p, &d);
+    if (!why.empty()) {
+        fprintf(stderr, "llm_create: %s\n", why.c_str());
+        return LLM_EINVAL;
+    }
+    llm_t *h = new_handle(p, d);
+    if (!h) return LLM_ENOMEM;
+    if (hip_stream) {
+        h->stream = (hipStream_t)hip_stream;
+    } else {
+        if (hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking) != hipSuccess) {
+            delete h;
+            return LLM_EDEVICE;
+        }
+        h->own_stream = true;
+    }
+    int rc = create_impl(h, seed);
+    if (rc != LLM_OK) {
+        fprintf(stderr, "llm_create: %s\n", h->err.c_str());
+        (void)hipDeviceSynchronize();
+        release(h);
+        delete h;
+        return rc;
+    }
+    *out = h;
+    return LLM_OK;
+}
+
+void llm_destroy(llm_t *h)
+{
+    if (!h) return;
+    if (!h->dry) {
+        if (h->stream) (void)hipStreamSynchronize(h->stream);
+        release(h);
+    }
+    delete h;
+}
+
+const char *llm_last_error(const llm_t *h) { return h ? h->err.c_str() : "null handle"; }
+
+void *llm_get_stream(llm_t *h) { return h ? (void *)h->stream : nullptr; }
+
+int llm_prefill(llm_t *h, const int32_t *tokens, int32_t B, int32_t T)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if ((rc = check_prefill_args(h, B, T))) return rc;
+    if (!tokens) return fail(h, LLM_EINVAL, "tokens is NULL");
+    if (!tokens_ok(tokens, (int64_t)B * T, h->d.V)) return fail(h, LLM_EINVAL, "token id out of [0, vocab)");
+    if (!h->dry) {
+        HIPC(h, hipMemcpy2DAsync(h->tok, (size_t)h->d.S * 4, tokens, (size_t)T * 4, (size_t)T * 4, B,
+                                 hipMemcpyHostToDevice, h->stream));
+        HIPC(h, hipStreamSynchronize(h->stream));
+    }
+    return prefill_common(h, B, T);
+}
+
+int llm_prefill_d(llm_t *h, const int32_t *tokens_d, int32_t B, int32_t T)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if ((rc = check_prefill_args(h, B, T))) return rc;
+    if (!tokens_d) return fail(h, LLM_EINVAL, "tokens is NULL");
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    HIPC(h, hipMemcpy2DAsync(h->tok, (size_t)h->d.S * 4, tokens_d, (size_t)T * 4, (size_t)T * 4, B,
+                             hipMemcpyDeviceToDevice, h->stream));
+    return prefill_common(h, B, T);
+}
+
+int llm_decode(llm_t *h, int32_t prev_pos)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!h->prefilled) return fail(h, LLM_ESTATE, "decode before prefill");
+    if (prev_pos < 1 || prev_pos >= h->d.S) return fail(h, LLM_EINVAL, "prev_pos must be in [1, max_seq_len)");
+    if (prev_pos > h->last_pos + 1) return fail(h, LLM_ESTATE, "prev_pos skips positions whose KV is not written");
+    if (!h->col_written[prev_pos]) return fail(h, LLM_ESTATE, "token column prev_pos has not been written");
+    if (!h->dry) {
+        HIPC(h, launch_set_int(h->pos_dev, prev_pos, h->stream));
+        const int B = h->cur_B;
+        if (h->use_graph) {
+            if (!h->gexec || h->graph_B != B) {
+                if (h->gexec) {
+                    (void)hipGraphExecDestroy(h->gexec);
+                    h->gexec = nullptr;
+                }
+                hipGraph_t graph = nullptr;
+                HIPC(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeRelaxed));
+                hipError_t fe = forward(h, B, 1, h->pos_dev);
+                hipError_t ce = hipStreamEndCapture(h->stream, &graph);
+                if (fe != hipSuccess) return fail(h, LLM_EDEVICE, std::string("capture: ") + hipGetErrorString(fe));
+                if (ce != hipSuccess) return fail(h, LLM_EDEVICE, std::string("end capture: ") + hipGetErrorString(ce));
+                hipError_t ie = hipGraphInstantiate(&h->gexec, graph, nullptr, nullptr, 0);
+                (void)hipGraphDestroy(graph);
+                if (ie != hipSuccess) return fail(h, LLM_EDEVICE, std::string("instantiate: ") + hipGetErrorString(ie));
+                h->graph_B = B;
+            }
+            HIPC(h, hipGraphLaunch(h->gexec, h->stream));
+        } else {
+            rc = after_forward(h, forward(h, B, 1, h->pos_dev));
+            if (rc) return rc;
+        }
+    }
+    h->last_pos = prev_pos;
+    h->logits_valid = true;
+    return LLM_OK;
+}
+
+int llm_sample(llm_t *h, float temperature, float top_p, const float *uniforms, int32_t *out_tokens)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (h->dry && out_tokens) return fail(h, LLM_ESTATE, "dry handle returns no tokens");
+    bool have_u = uniforms != nullptr;
+    if (!h->dry && have_u && temperature > 0.f && h->logits_valid) {
+        HIPC(h, hipMemcpyAsync(h->uni, uniforms, (size_t)h->cur_B * sizeof(float), hipMemcpyHostToDevice,
+                               h->stream));
+        HIPC(h, hipStreamSynchronize(h->stream));
+    }
+    rc = sample_common(h, temperature, top_p, h->uni, have_u, out_tokens ? h->outtok : nullptr);
+    if (rc) return rc;
+    if (out_tokens) {
+        HIPC(h, hipMemcpyAsync(out_tokens, h->outtok, (size_t)h->cur_B * sizeof(int32_t),
+                               hipMemcpyDeviceToHost, h->stream));
+        HIPC(h, hipStreamSynchronize(h->stream));
+    }
+    return LLM_OK;
+}
+
+int llm_sample_d(llm_t *h, float temperature, float top_p, const float *uniforms_d, int32_t *out_tokens_d)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (h->dry && (uniforms_d || out_tokens_d)) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    return sample_common(h, temperature, top_p, uniforms_d, uniforms_d != nullptr, out_tokens_d);
+}
+
+int llm_set_tokens(llm_t *h, int32_t pos, const int32_t *tokens, const uint8_t *mask)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!h->prefilled) return fail(h, LLM_ESTATE, "set_tokens before prefill");
+    if (pos < 0 || pos >= h->d.S) return fail(h, LLM_EINVAL, "pos must be in [0, max_seq_len)");
+    if (!tokens) return fail(h, LLM_EINVAL, "tokens is NULL");
+    const int B = h->cur_B;
+    bool all = true;
+    for (int b = 0; b < B; b++) {
+        bool use = !mask || mask[b];
+        all = all && use;
+        if (use && (tokens[b] < 0 || tokens[b] >= h->d.V)) return fail(h, LLM_EINVAL, "token id out of [0, vocab)");
+    }
+    if (!h->dry) {
+        HIPC(h, hipMemcpyAsync(h->stage_i32, tokens, (size_t)B * 4, hipMemcpyHostToDevice, h->stream));
+        if (mask) HIPC(h, hipMemcpyAsync(h->stage_mask, mask, (size_t)B, hipMemcpyHostToDevice, h->stream));
+        HIPC(h, launch_set_tokens(h->tok, h->d.S, B, pos, h->stage_i32, mask ? h->stage_mask : nullptr, h->stream));
+        HIPC(h, hipStreamSynchronize(h->stream));
+    }
+    if (all) h->col_written[pos] = 1;
+    return LLM_OK;
+}
+
+int llm_get_logits(llm_t *h, float *out)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!out) return fail(h, LLM_EINVAL, "out is NULL");
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no logits");
+    if (!h->logits_valid) return fail(h, LLM_ESTATE, "no logits yet");
+    HIPC(h, hipMemcpyAsync(out, h->logits, (size_t)h->cur_B * h->d.V * sizeof(float), hipMemcpyDeviceToHost,
+                           h->stream));
+    HIPC(h, hipStreamSynchronize(h->stream));
+    return LLM_OK;
+}
+
+int llm_get_logits_d(llm_t *h, float *out_d)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!out_d) return fail(h, LLM_EINVAL, "out is NULL");
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no logits");
+    if (!h->logits_valid) return fail(h, LLM_ESTATE, "no logits yet");
+    HIPC(h, hipMemcpyAsync(out_d, h->logits, (size_t)h->cur_B * h->d.V * sizeof(float),
+                           hipMemcpyDeviceToDevice, h->stream));
+    return LLM_OK;
+}
+
+int llm_get_tokens(llm_t *h, int32_t n_cols, int32_t *out)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!out || n_cols < 1 || n_cols > h->d.S) return fail(h, LLM_EINVAL, "n_cols must be in [1, max_seq_len]");
+    if (h->dry || !h->prefilled) return fail(h, LLM_ESTATE, "no token buffer yet");
+    HIPC(h, hipMemcpy2DAsync(out, (size_t)n_cols * 4, h->tok, (size_t)h->d.S * 4, (size_t)n_cols * 4, h->cur_B,
+                             hipMemcpyDeviceToHost, h->stream));
+    HIPC(h, hipStreamSynchronize(h->stream));
+    return LLM_OK;
+}
+
+int llm_sample_probs(llm_t *h, const float *probs, int32_t B, float top_p, const float *uniforms, int32_t *out)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (B < 1 || B > h->d.maxB) return fail(h, LLM_EINVAL, "B must be in [1, max_batch_size]");
+    if (!probs || !uniforms || !out) return fail(h, LLM_EINVAL, "NULL argument");
+    if (!(top_p > 0.f && top_p <= 1.f)) return fail(h, LLM_EINVAL, "top_p must be in (0, 1]");
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    HIPC(h, hipMemcpyAsync(h->probs, probs, (size_t)B * h->d.V * sizeof(float), hipMemcpyHostToDevice, h->stream));
+    HIPC(h, hipMemcpyAsync(h->uni, uniforms, (size_t)B * sizeof(float), hipMemcpyHostToDevice, h->stream));
+    HIPC(h, launch_top_p(h->probs, B, h->d.V, top_p, h->uni, h->tok, h->d.S, -1, h->outtok, h->stream));
+    HIPC(h, hipMemcpyAsync(out, h->outtok, (size_t)B * sizeof(int32_t), hipMemcpyDeviceToHost, h->stream));
+    HIPC(h, hipStreamSynchronize(h->stream));
+    h->logits_valid = false;  // the probability buffer no longer matches the logits
+    return LLM_OK;
+}
+
+int llm_sync(llm_t *h)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!h->dry) HIPC(h, hipStreamSynchronize(h->stream));
+    return LLM_OK;
+}
+
+int llm_read_weights(llm_t *h, int32_t tensor_id, int64_t first, int64_t count, void *out)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no weights");
+    const Dims &d = h->d;
+    int mat, layer = 0, which = 0;
+    int64_t rows, cols;
+    if (tensor_id == 0) { mat = MAT_EMB; rows = d.V; cols = d.D; }
+    else if (tensor_id == 1) { mat = MAT_HEAD; rows = d.V; cols = d.D; }
+    else if (tensor_id >= 16 && (tensor_id - 16) / 8 < d.NL && (tensor_id - 16) % 8 < 7) {
+        layer = (tensor_id - 16) / 8;
+        which = (tensor_id - 16) % 8;
+        const int wm[7] = {MAT_QKV, MAT_QKV, MAT_QKV, MAT_O, MAT_W13, MAT_W2, MAT_W13};
+        mat = wm[which];
+        int64_t r7[7] = {(int64_t)d.H * d.hd, (int64_t)d.Hkv * d.hd, (int64_t)d.Hkv * d.hd, d.D, d.F, d.D, d.F};
+        rows = r7[which];
+        cols = mat_cols(d, mat);
+    } else {
+        return fail(h, LLM_EINVAL, "unknown tensor id");
+    }
+    if (!out || first < 0 || count < 1 || first + count > rows * cols) return fail(h, LLM_EINVAL, "bad range");
+    void *tmp = nullptr;
+    HIPM(h, hipMalloc(&tmp, count * d.es));
+    hipError_t e = launch_read_weights(mat_ptr(h, layer, mat), d.dtype, mat, mat_rows(d, mat), cols, which,
+                                       d.H, d.Hkv, d.hd, d.F, first, count, tmp, h->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(out, tmp, count * d.es, hipMemcpyDeviceToHost, h->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+    (void)hipFree(tmp);
+    if (e != hipSuccess) return fail(h, LLM_EDEVICE, std::string("read_weights: ") + hipGetErrorString(e));
+    return LLM_OK;
+}
+
+static int op_begin(llm_t *h)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    HIPC(h, hipDeviceSynchronize());
+    return LLM_OK;
+}
+
+static int op_end(llm_t *h, hipError_t e)
+{
+    if (e != hipSuccess) return fail(h, LLM_EDEVICE, std::string("op launch: ") + hipGetErrorString(e));
+    HIPC(h, hipStreamSynchronize(h->stream));
+    return LLM_OK;
+}
+
+int llm_op_rmsnorm(llm_t *h, const void *x_d, int32_t M, void *y_d)
+{
+    int rc = op_begin(h);
+    if (rc) return rc;
+    if (!x_d || !y_d || M < 1) return fail(h, LLM_EINVAL, "bad arguments");
+    return op_end(h, launch_rmsnorm(x_d, h->d.D, h->norm_w, M, h->d.D, h->p.norm_eps, h->d.dtype, y_d, h->stream));
+}
+
+int llm_op_linear(llm_t *h, int32_t layer, int32_t mat, const void *x_d, int32_t M, void *y_d)
+{
+    int rc = op_begin(h);
+    if (rc) return rc;
+    if (!x_d || !y_d || M < 1) return fail(h, LLM_EINVAL, "bad arguments");
+    if (mat < 0 || mat > MAT_HEAD || (mat != MAT_HEAD && (layer < 0 || layer >= h->d.NL)))
+        return fail(h, LLM_EINVAL, "bad matrix or layer");
+    if (mat == MAT_HEAD) layer = 0;
+    Epilogue ep = make_ep(EP_STORE, y_d, mat_rows(h->d, mat));
+    return op_end(h, run_linear(h, layer, mat, x_d, mat_cols(h->d, mat), M, ep));
+}
+
+int llm_op_kv_write(llm_t *h, int32_t layer, const void *k_d, const void *v_d, int32_t B, int32_t T, int32_t pos0)
+{
+    int rc = op_begin(h);
+    if (rc) return rc;
+    const Dims &d = h->d;
+    if (!k_d || !v_d || layer < 0 || layer >= d.NL || B < 1 || B > d.maxB || T < 1 || pos0 < 0 || pos0 + T > d.S)
+        return fail(h, LLM_EINVAL, "bad arguments");
+    return op_end(h, launch_kv_write(k_d, v_d, B, T, pos0, d.Hkv, d.hd, d.S, d.dtype, layer_kc(h, layer),
+                                     layer_vc(h, layer), h->stream));
+}
+
+int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_t T, int32_t pos0, void *out_d)
+{
+    int rc = op_begin(h);
+    if (rc) return rc;
+    const Dims &d = h->d;
+    if (!q_d || !out_d || layer < 0 || layer >= d.NL || B < 1 || B > d.maxB || T < 1 || pos0 < 0 || pos0 + T > d.S)
+        return fail(h, LLM_EINVAL, "bad arguments");
+    AttnArgs aa{};
+    aa.q = q_d; aa.kcache = layer_kc(h, layer); aa.vcache = layer_vc(h, layer); aa.out = out_d;
+    aa.B = B; aa.T = T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
+    aa.pos_dev = nullptr; aa.pos_imm = pos0; aa.part = h->attn_part;
+    hipError_t e;
+    if (d.dtype == LLM_F32) e = launch_attn_f32(aa, h->stream);
+    else if (T == 1) e = launch_attn_decode_f16(aa, h->stream);
+    else if (pos0 == 0) e = launch_attn_prefill_f16(aa, h->stream);
+    else return fail(h, LLM_EINVAL, "fp16 multi-token attention starts at position 0");
+    return op_end(h, e);
+}
+
+}  // extern "C"

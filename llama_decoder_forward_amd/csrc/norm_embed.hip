@@ -1,0 +1,99 @@
+// Embedding gather and RMSNorm.
+#include "common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Row m of x = row tok of E (the reference's tok_embeddings lookup,
+// walkthrough section 2).  Prefill: m = b*T + t reads tok[b][t]; decode
+// (pos_dev != NULL, T == 1): row b reads tok[b][*pos_dev].
+__global__ void embed_kernel(const char *E, const int32_t *tok, int64_t tok_ld, int T,
+                             const int *pos_dev, int64_t row_bytes, char *x)
+{
+    int m = blockIdx.x;
+    int b = m / T, t = m % T;
+    int col = pos_dev ? *pos_dev : t;
+    int32_t id = tok[(int64_t)b * tok_ld + col];
+    const uint4 *src = reinterpret_cast<const uint4 *>(E + (int64_t)id * row_bytes);
+    uint4 *dst = reinterpret_cast<uint4 *>(x + (int64_t)m * row_bytes);
+    for (int64_t i = threadIdx.x; i < row_bytes / 16; i += blockDim.x) dst[i] = src[i];
+}
+
+__device__ __forceinline__ float block_sum(float v, float *red)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); i++) t += red[i];
+    return t;
+}
+
+// RMSNorm (walkthrough section 3.2): r = 1/sqrt(mean(x^2) + eps) in fp32,
+// y = round(round(x * r) * w).  One work-group per row, 16-byte loads.
+__global__ void rmsnorm_f16_kernel(const half_t *x, int64_t ldx, const half_t *w, int D, float eps,
+                                   half_t *y)
+{
+    __shared__ float red[kThreads / 64];
+    const half8 *xr = reinterpret_cast<const half8 *>(x + (int64_t)blockIdx.x * ldx);
+    half8 *yr = reinterpret_cast<half8 *>(y + (int64_t)blockIdx.x * D);
+    const half8 *wr = reinterpret_cast<const half8 *>(w);
+    int nv = D / 8;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < nv; i += blockDim.x) {
+        half8 v = xr[i];
+#pragma unroll
+        for (int e = 0; e < 8; e++) { float f = (float)v[e]; ss += f * f; }
+    }
+    float tot = block_sum(ss, red);
+    float r = __frcp_rn(__fsqrt_rn(tot / (float)D + eps));
+    for (int i = threadIdx.x; i < nv; i += blockDim.x) {
+        half8 v = xr[i], wv = wr[i], o;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            half_t n = (half_t)((float)v[e] * r);
+            o[e] = (half_t)((float)n * (float)wv[e]);
+        }
+        yr[i] = o;
+    }
+}
+
+__global__ void rmsnorm_f32_kernel(const float *x, int64_t ldx, const float *w, int D, float eps,
+                                   float *y)
+{
+    __shared__ float red[kThreads / 64];
+    const float *xr = x + (int64_t)blockIdx.x * ldx;
+    float *yr = y + (int64_t)blockIdx.x * D;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < D; i += blockDim.x) ss += xr[i] * xr[i];
+    float tot = block_sum(ss, red);
+    float r = __frcp_rn(__fsqrt_rn(tot / (float)D + eps));
+    for (int i = threadIdx.x; i < D; i += blockDim.x) yr[i] = (xr[i] * r) * w[i];
+}
+
+}  // namespace
+
+hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int B, int T,
+                        const int *pos_dev, int D, int dtype, void *x, hipStream_t s)
+{
+    int64_t row_bytes = (int64_t)D * (dtype == 1 ? 2 : 4);
+    hipLaunchKernelGGL(embed_kernel, dim3(B * T), dim3(kThreads), 0, s, (const char *)E, tok,
+                       tok_ld, T, pos_dev, row_bytes, (char *)x);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int D, float eps,
+                          int dtype, void *y, hipStream_t s)
+{
+    if (M <= 0) return hipSuccess;
+    if (dtype == 1)
+        hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(M), dim3(kThreads), 0, s, (const half_t *)x, ldx,
+                           (const half_t *)w, D, eps, (half_t *)y);
+    else
+        hipLaunchKernelGGL(rmsnorm_f32_kernel, dim3(M), dim3(kThreads), 0, s, (const float *)x, ldx,
+                           (const float *)w, D, eps, (float *)y);
+    return hipGetLastError();
+}

@@ -79,6 +79,8 @@ def lib():
             "orc_top_p": (C.c_int32, [vp, C.c_int32, C.c_float, C.c_float, P(C.c_int32)]),
             "orc_num_threads": (C.c_int32, []),
             "orc_model_set_weights": (C.c_int, [vp, C.c_int32, vp]),
+            "orc_linear": (None, [vp, C.c_int32, C.c_int32, C.c_int32, vp, C.c_int32, C.c_int32,
+                                  C.c_int32, vp]),
             "orc_f64_to_f16_vec": (None, [vp, C.c_int64, vp]),
             "orc_f32_to_f16_vec": (None, [vp, C.c_int64, vp]),
             "orc_f16_to_f32_vec": (None, [vp, C.c_int64, vp]),
@@ -185,6 +187,21 @@ def attention_row(q, K, V, dtype: int = F32, acc64: bool = False) -> np.ndarray:
     out = np.empty(d, np.float32)
     lib().orc_attention_row(_ptr(q), _ptr(K), _ptr(V), L, d, d, dtype, int(acc64), _ptr(out))
     return out
+
+
+def linear(W, X, out_dtype: int = F16, acc64: bool = False) -> np.ndarray:
+    """Y[M][N] = round(W X) for weights W[N][K] given as uint16 binary16 bit
+    patterns or float32, and float32 rows X[M][K]."""
+    W = np.ascontiguousarray(W)
+    wd = F16 if W.dtype == np.uint16 else F32
+    if wd == F32:
+        W = W.astype(np.float32)
+    X = _f32(X)
+    N, K = W.shape
+    M = X.shape[0]
+    Y = np.empty((M, N), np.float32)
+    lib().orc_linear(_ptr(W), wd, N, K, _ptr(X), M, out_dtype, int(acc64), _ptr(Y))
+    return Y
 
 
 def silu(x: float) -> float:

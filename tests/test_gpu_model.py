@@ -1,0 +1,162 @@
+"""End-to-end parity on the GPU: prefill + decode steps through the C ABI
+against the oracle on the same seeded weights and tokens.
+
+Protocol: the GPU consumes the oracle's token stream (teacher forcing via
+llm_set_tokens), logits are compared at every step (max |delta| <= 5e-2,
+cosine >= 0.9999 per row), and greedy ids must agree wherever the oracle's
+top-1 margin exceeds 0.1."""
+import numpy as np
+import pytest
+
+import oracle
+from llama_decoder_forward_amd import configs, synth
+from tests.gpu_util import cosine, say
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_TOL = 5e-2
+COS_TOL = 0.9999
+MARGIN = 0.1
+
+
+@pytest.fixture(scope="module")
+def B():
+    from llama_decoder_forward_amd import binding
+    return binding
+
+
+def ocfg(kw):
+    return oracle.Cfg(**kw)
+
+
+def gpu_forced_logits(h, tokens, T0, steps):
+    """Prefill tokens[:, :T0], then decode steps at T0.. with the columns
+    forced to `tokens`; returns logits [B][steps+1][V] and the GPU's argmax
+    ids before forcing [B][steps+1]."""
+    h.prefill(tokens[:, :T0])
+    logits = [h.get_logits()]
+    ids = [h.sample(0.0)]
+    for p in range(T0, T0 + steps):
+        h.set_tokens(p, tokens[:, p])
+        h.decode(p)
+        logits.append(h.get_logits())
+        ids.append(h.sample(0.0))
+    return np.stack(logits, 1), np.stack(ids, 1)
+
+
+def oracle_greedy_stream(cfg, seed, prompt, steps):
+    m = oracle.Model(cfg, seed)
+    Bn, T0 = prompt.shape
+    toks = np.zeros((Bn, T0 + steps + 1), np.int32)
+    toks[:, :T0] = prompt
+    lg = m.forward(prompt, 0)
+    margins = []
+    for p in range(T0, T0 + steps + 1):
+        srt = np.sort(lg, -1)
+        margins.append(srt[:, -1] - srt[:, -2])
+        toks[:, p] = lg.argmax(-1)  # numpy argmax: lowest index on ties, like the oracle
+        if p < T0 + steps:
+            lg = m.forward(toks[:, p:p + 1], p)
+    m.close()
+    return toks, np.stack(margins, 1)
+
+
+def check_logits(got, want):
+    d = np.abs(got - want)
+    cos = cosine(got.reshape(-1, got.shape[-1]), want.reshape(-1, want.shape[-1]))
+    say(f"  max|d|={d.max():.3e} min cos={cos.min():.7f}")
+    assert d.max() <= LOGIT_TOL, d.max()
+    assert cos.min() >= COS_TOL, cos.min()
+
+
+def test_tiny_fp32_greedy(B):
+    w = configs.TINY
+    kw = w.model_kwargs()
+    prompt = synth.tokens(w.token_seed, 1, w.prompt_len, w.vocab_size)
+    say("tiny: oracle greedy stream")
+    toks, margins = oracle_greedy_stream(ocfg(kw), w.weight_seed, prompt, w.decode_steps - 1)
+    # 8 + 24 = 32 positions: the last sampled token has no column (S = 32)
+    h = B.llm_create(B.make_params(**kw), w.weight_seed)
+    say("tiny: gpu teacher forced")
+    got, ids = gpu_forced_logits(h, toks, w.prompt_len, w.decode_steps)
+    want = oracle.forward_stream(ocfg(kw), w.weight_seed, toks[:, :w.max_seq_len], w.prompt_len - 1)
+    check_logits(got, want)
+    ok = margins > MARGIN                       # [1][24]: logits at positions 7..30
+    assert np.array_equal(ids[:, :-1][ok], toks[:, w.prompt_len:][ok])
+    # free-running greedy on the GPU gives the oracle's stream up to the first
+    # sub-margin step
+    h.prefill(prompt)
+    free = [h.sample(0.0)[0]]
+    for p in range(w.prompt_len, w.prompt_len + w.decode_steps):
+        h.decode(p)
+        free.append(h.sample(0.0)[0])
+    free = np.array(free)
+    n_ok = int(np.argmin(ok[0])) if not ok[0].all() else ok.shape[1]
+    assert np.array_equal(free[:n_ok], toks[0, w.prompt_len:][:n_ok])
+    # the token buffer holds prompt + sampled tokens; the final sample (at
+    # position S-1) is returned but has no column
+    buf = h.get_tokens(w.max_seq_len)
+    assert np.array_equal(buf[0, :w.prompt_len], prompt[0])
+    assert np.array_equal(buf[0, w.prompt_len:], free[:-1])
+    h.destroy()
+
+
+def small_kw(**kw):
+    base = dict(n_layers=2, dim=512, n_heads=4, n_kv_heads=2, vocab_size=1024, multiple_of=64,
+                ffn_dim_multiplier=0.0, max_batch_size=3, max_seq_len=128, dtype=1)
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("T0", [5, 40])
+def test_small_fp16_forced(B, T0):
+    """GQA fp16 model, 3 rows: prompt 5 (M = 15, skinny products) and 40
+    (M = 120, tiled products), then 12 decode steps."""
+    kw = small_kw()
+    steps = 12
+    toks = synth.tokens(41, 3, T0 + steps, kw["vocab_size"])
+    say("small fp16 forced", T0)
+    h = B.llm_create(B.make_params(**kw), 91)
+    got, _ = gpu_forced_logits(h, toks, T0, steps)
+    want = oracle.forward_stream(ocfg(kw), 91, toks, T0 - 1)
+    check_logits(got, want)
+    h.destroy()
+
+
+def test_small_fp16_sampled_and_deterministic(B):
+    kw = small_kw()
+    T0, steps = 9, 10
+    prompt = synth.tokens(42, 3, T0, kw["vocab_size"])
+    u = synth.uniforms(43, steps + 1, 3)
+    h = B.llm_create(B.make_params(**kw), 92)
+
+    def run():
+        h.prefill(prompt)
+        out = [h.sample(0.8, 0.9, u[0])]
+        for i, p in enumerate(range(T0, T0 + steps)):
+            h.decode(p)
+            out.append(h.sample(0.8, 0.9, u[i + 1]))
+        return np.stack(out, 1), h.get_tokens(T0 + steps + 1)
+
+    a, ta = run()
+    b, tb = run()
+    assert np.array_equal(a, b) and np.array_equal(ta, tb)  # bit-identical reruns
+    assert np.array_equal(ta[:, T0:], a)                      # sampled ids land in the buffer
+    assert np.array_equal(ta[:, :T0], prompt)
+    # the sampled stream, fed back teacher-forced, matches the oracle's logits
+    want = oracle.forward_stream(ocfg(kw), 92, ta[:, :T0 + steps], T0 - 1)
+    got, _ = gpu_forced_logits(h, ta, T0, steps)
+    check_logits(got, want)
+    h.destroy()
+
+
+def test_mha_and_gqa_paths(B):
+    """n_kv_heads = n_heads (MHA) and n_rep = 4 on the same dims."""
+    for hkv in (4, 1):
+        kw = small_kw(n_kv_heads=hkv)
+        toks = synth.tokens(44, 2, 20, kw["vocab_size"])
+        say("heads", hkv)
+        h = B.llm_create(B.make_params(**kw), 93)
+        got, _ = gpu_forced_logits(h, toks, 12, 8)
+        check_logits(got, oracle.forward_stream(ocfg(kw), 93, toks, 11))
+        h.destroy()
