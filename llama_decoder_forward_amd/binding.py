@@ -19,6 +19,15 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m llama_decoder_forward_amd.build` "
                       "(or __graft_entry__.build()); there is no fallback path")
 
+# One HIP runtime per process: torch ships its own libamdhip64 /
+# libhsa-runtime64 under the same sonames as ROCm's.  Importing torch first
+# makes libllm.so bind to that copy; loading ROCm's copy first and torch's
+# afterwards leaves two runtimes in the process and torch then sees no GPU.
+try:
+    import torch  # noqa: F401
+except ImportError:  # torch is optional for the C ABI itself
+    torch = None
+
 _lib = C.CDLL(LIB_PATH)
 
 

@@ -44,6 +44,14 @@ def f16_ulp(x: np.ndarray) -> np.ndarray:
     return np.spacing(np.abs(x).astype(np.float16)).astype(np.float32)
 
 
+def within_one_f16_step(got, want) -> np.ndarray:
+    """True where two fp16 values are at most one rounding step apart (the
+    larger spacing of the two, so a step across a power of two counts)."""
+    got = np.asarray(got, np.float32)
+    want = np.asarray(want, np.float32)
+    return np.abs(got - want) <= np.maximum(f16_ulp(got), f16_ulp(want)) * 1.0001 + 1e-7
+
+
 def cosine(a, b) -> np.ndarray:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from llama_decoder_forward_amd import configs
-from tests.gpu_util import cosine, dev, empty, f16_ulp, host, randn_f16, say
+from tests.gpu_util import cosine, dev, empty, f16_ulp, host, randn_f16, say, within_one_f16_step
 
 pytestmark = pytest.mark.gpu
 
@@ -83,7 +83,7 @@ def test_rmsnorm(B, small):
         y = host(yd).astype(np.float32)
         want = np.stack([oracle.rmsnorm(x[m].astype(np.float32), 1e-5, F16) for m in range(M)])
         d = np.abs(y - want)
-        assert np.all(d <= f16_ulp(want) * 1.0001), d.max()
+        assert np.all(within_one_f16_step(y, want)), d.max()
         assert np.mean(d == 0) > 0.97
 
 
@@ -119,9 +119,19 @@ def test_linear(B, small, mat, M):
     y = host(yd).astype(np.float32)
     want = oracle.linear(W, x.astype(np.float32), F16)
     d = np.abs(y - want)
-    # accumulation order differs: at most one fp16 rounding step apart
-    assert np.all(d <= f16_ulp(want) * 1.0001 + 1e-7), (d.max(), np.unravel_index(d.argmax(), d.shape))
+    ok = accumulation_close(y, want, W, x)
+    assert np.all(ok), [(m, n, y[m, n], want[m, n]) for m, n in np.argwhere(~ok)[:5]]
     assert np.mean(d == 0) > 0.9
+
+
+def accumulation_close(got, want, W, x):
+    """Two results of the same fp32 dot products summed in different orders:
+    within one fp16 rounding step, or within the fp32 accumulation error
+    bound 2^-20 * sum_k |w_k x_k| (values near zero, where fp16 steps are
+    finer than the fp32 sum's own rounding)."""
+    absW = (np.ascontiguousarray(W) & np.uint16(0x7FFF)).astype(np.uint16)
+    mag = oracle.linear(absW, np.abs(x.astype(np.float32)), F32)
+    return within_one_f16_step(got, want) | (np.abs(got - want) <= mag * 2.0 ** -20)
 
 
 def test_linear_7b_shapes_sampled(B):
@@ -158,7 +168,7 @@ def test_linear_7b_shapes_sampled(B):
                 rows.append(oracle.gen_tensor(w.weight_seed, tid, row * K, K, F16))
             want = oracle.linear(np.stack(rows), x[ms].astype(np.float32), F16)
             got = y[np.ix_(ms, ns)].astype(np.float32)
-            assert np.all(np.abs(got - want) <= f16_ulp(want) * 1.0001 + 1e-7)
+            assert np.all(accumulation_close(got, want, np.stack(rows), x[ms]))
     h.destroy()
 
 
