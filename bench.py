@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Decode / prefill benchmark of the gfx950 Llama-2 decoder forward.
+
+One step = one whole generate pass over the workload's batch: prompt tokens
+already in HBM -> prefill -> sample -> decode steps, each followed by a sample
+(and, for ragged prompts, the prompt forcing of the reference's generate
+loop).  The host never synchronises inside a step.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from llama_decoder_forward_amd import configs, synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+
+
+def decode_bytes_per_step(w, B, L_avg):
+    """Algorithmic HBM bytes of one decode step: every layer matrix and the
+    output head once, the attended KV prefix once per KV head, the KV write."""
+    hd = w.head_dim
+    kv_read = B * L_avg * 2 * w.n_kv_heads * hd * 2 * w.n_layers
+    kv_write = B * 2 * w.n_kv_heads * hd * 2 * w.n_layers
+    return w.weight_bytes() + kv_read + kv_write
+
+
+def prefill_flops(w, B, T):
+    """2 * params * tokens for the layer matrices, causal attention
+    2 * B * H * d * T (T + 1) per layer, head at the last position."""
+    lin = 2 * w.layer_params() * B * T * w.n_layers
+    att = 2 * B * w.n_heads * w.head_dim * T * (T + 1) * w.n_layers
+    head = 2 * w.vocab_size * w.dim * B
+    return lin + att + head
+
+
+def cpu_baseline(w, prompt, n_steps=4):
+    """The oracle (untuned) on this host: decode cost of one layer and of the
+    head measured on 1- and 2-layer models of the workload's shape for one
+    row, scaled to the full depth and the batch."""
+    import oracle
+    kw = w.model_kwargs(max_batch_size=1, max_seq_len=w.max_seq_len)
+    T0 = min(len(prompt), 16)
+    times = {}
+    for nl in (1, 2):
+        kw["n_layers"] = nl
+        m = oracle.Model(oracle.Cfg(**kw), w.weight_seed)
+        m.forward(np.asarray(prompt[:T0], np.int32)[None], 0)
+        t0 = time.perf_counter()
+        for i in range(n_steps):
+            m.forward(np.asarray([[prompt[i % T0]]], np.int32), T0 + i)
+        times[nl] = (time.perf_counter() - t0) / n_steps
+        m.close()
+    per_layer = max(times[2] - times[1], 1e-9)
+    head = max(times[1] - per_layer, 0.0)
+    t_token = w.n_layers * per_layer + head
+    return {"value": 1.0 / t_token, "unit": "tok/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_steps} decode steps of one row on 1- and 2-layer models of the "
+                      f"workload's shape after a {T0}-token prefill; per-layer and head time "
+                      f"scaled to {w.n_layers} layers; batch rows run one after another",
+            "seconds_per_token_row": t_token}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=configs.L7B_BS1.name, choices=sorted(configs.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-reps", type=int, default=5)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the decoder's rows are independent, so more GPUs would run data-parallel replicas "
+              "with no exchange, and that path is not built here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from llama_decoder_forward_amd import binding as Bd
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = configs.WORKLOADS[args.workload]
+    B = w.batch
+    ragged = bool(w.prompt_range)
+    if ragged:
+        lens = synth.prompt_lengths(w.token_seed, B, *w.prompt_range)
+        T0 = int(lens.min())
+        Tmax = int(lens.max())
+    else:
+        lens = np.full(B, w.prompt_len, np.int32)
+        T0 = Tmax = w.prompt_len
+    steps = w.decode_steps
+    prompts = synth.tokens(w.token_seed, B, Tmax, w.vocab_size)
+    uni = synth.uniforms(w.uniform_seed, steps + 1, B)
+    temp, top_p = w.temperature, w.top_p
+
+    t_create = time.perf_counter()
+    h = Bd.llm_create(Bd.params_for(w), w.weight_seed)
+    t_create = time.perf_counter() - t_create
+    stream = torch.cuda.ExternalStream(h.stream())
+
+    # inputs resident in HBM before timing
+    tok_dev = torch.from_numpy(np.ascontiguousarray(prompts[:, :T0])).cuda()
+    uni_dev = torch.from_numpy(np.ascontiguousarray(uni)).cuda()
+    S = w.max_seq_len
+    force_tok = np.zeros((S, B), np.int32)
+    force_mask = np.zeros((S, B), np.uint8)
+    for b in range(B):
+        force_tok[:lens[b], b] = prompts[b, :lens[b]]
+        force_mask[T0:lens[b], b] = 1
+    force_tok_dev = torch.from_numpy(force_tok).cuda()
+    force_mask_dev = torch.from_numpy(force_mask).cuda()
+    torch.cuda.synchronize()
+
+    def generate(ev=None):
+        h.prefill_d(tok_dev.data_ptr(), B, T0)
+        h.sample_d(temp, top_p, uni_dev.data_ptr() if temp > 0 else 0, 0)
+        if ev is not None:
+            ev.record(stream)
+        for i in range(steps):
+            p = T0 + i
+            if ragged and force_mask[p].any():
+                h.set_tokens_d(p, force_tok_dev[p].data_ptr(), force_mask_dev[p].data_ptr())
+            h.decode(p)
+            h.sample_d(temp, top_p, uni_dev[i + 1].data_ptr() if temp > 0 else 0, 0)
+
+    for _ in range(args.warmup):
+        generate()
+    h.sync()
+    torch.cuda.synchronize()
+
+    ev_start = torch.cuda.Event(enable_timing=True)
+    ev_end = torch.cuda.Event(enable_timing=True)
+    ev_pf = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_st = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev_start.record(stream)
+    for k in range(args.steps):
+        ev_st[k].record(stream)
+        generate(ev_pf[k])
+    ev_end.record(stream)
+    h.sync()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev_start.elapsed_time(ev_end)
+    prefill_ms = float(np.mean([ev_st[k].elapsed_time(ev_pf[k]) for k in range(args.steps)]))
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = B * steps / (ms_per_step / 1e3)
+    decode_ms = ms_per_step - prefill_ms
+    decode_tok_s = B * steps / (decode_ms / 1e3)
+
+    # live per-kernel-class timing of one decode step (HIP events on the
+    # library's stream), at the last position of the generate pass
+    prof = h.profile_decode(T0 + steps - 1, args.profile_reps)
+    skinny_ms = prof["projections"] + prof["head"]
+    launches = 4 * w.n_layers + 1
+    wbytes = w.weight_bytes()
+    achieved = wbytes / (skinny_ms / 1e3) / 1e9
+    L_avg = T0 + steps / 2
+    step_bytes = decode_bytes_per_step(w, B, L_avg)
+    step_roof_tok_s = B * HBM_PEAK_GBS * 1e9 / step_bytes
+
+    pf_flops = prefill_flops(w, B, T0)
+    prefill_tok_s = B * T0 / (prefill_ms / 1e3)
+
+    out = {
+        "metric": "decode tok/s",
+        "value": round(value, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if w.dtype == configs.F16 else "f32",
+        "data": "synthetic: seeded SplitMix64 weights ~N(0,0.02), uniform prompt tokens",
+        "config": {"workload": w.name, "batch": B, "prompt": T0 if not ragged else f"ragged {w.prompt_range}, prefill {T0}",
+                   "decode_steps": steps, "temperature": temp, "top_p": top_p,
+                   "layers": w.n_layers, "dim": w.dim, "heads": f"{w.n_heads}/{w.n_kv_heads}",
+                   "ffn": w.ffn_hidden(), "vocab": w.vocab_size, "max_seq_len": S},
+        "roofline": {"bound": "hbm", "kernel": "gemm_skinny_kernel (all decode projections + head)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": round(wbytes / launches),
+                     "avg_launch_us": round(skinny_ms * 1e3 / launches, 3),
+                     "launches_per_step": launches},
+        "detail": {
+            "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
+            "prefill_ms": round(prefill_ms, 3),
+            "prefill_tok_s": round(prefill_tok_s, 1),
+            "prefill_tflops": round(pf_flops / (prefill_ms / 1e3) / 1e12, 2),
+            "decode_tok_s_incl_sampling": round(decode_tok_s, 2),
+            "decode_step_bytes": int(step_bytes),
+            "decode_roofline_tok_s": round(step_roof_tok_s, 1),
+            "decode_frac_of_roofline": round(decode_tok_s / step_roof_tok_s, 4),
+            "profile_ms_per_decode_step": {k: round(v, 4) for k, v in prof.items()},
+            "create_s": round(t_create, 2),
+        },
+    }
+    h.destroy()
+    del tok_dev, uni_dev, force_tok_dev, force_mask_dev
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, prompts[0].tolist())
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,8 +54,8 @@ typedef enum { LLM_F32 = 0, LLM_F16 = 1 } llm_dtype;
  *  dtype LLM_F16 stores weights, activations and cache in binary16 with fp32
  *    accumulation; LLM_F32 stores them in binary32.
  * Supported shapes: dim divisible by n_heads, n_heads by n_kv_heads,
- * max_batch_size <= 4096.  LLM_F16 models need head_dim 128, dim and the
- * FFN width multiples of 64, vocab_size a multiple of 16, max_seq_len a
+ * max_batch_size <= 4096.  LLM_F16 models need head_dim 128, dim <= 8192,
+ * dim and the FFN width multiples of 64, vocab_size a multiple of 16, max_seq_len a
  * multiple of 64 and n_heads / n_kv_heads <= 16.  LLM_F32 models are limited
  * to dim <= 4096 and max_seq_len <= 8192.  Other shapes give LLM_EINVAL. */
 typedef struct {
@@ -147,6 +147,11 @@ int llm_sample_d(llm_t *h, float temperature, float top_p, const float *uniforms
  * Requires 0 <= pos < max_seq_len, tokens in [0, vocab). */
 int llm_set_tokens(llm_t *h, int32_t pos, const int32_t *tokens, const uint8_t *mask);
 
+/* Same with tokens[B] and mask[B] (or NULL) in device memory; asynchronous.
+ * Token ids are not range-checked on the host: the caller guarantees
+ * [0, vocab). */
+int llm_set_tokens_d(llm_t *h, int32_t pos, const int32_t *tokens_d, const uint8_t *mask_d);
+
 /* Copy fp32 logits[B][vocab] of the last forward into host memory (syncs). */
 int llm_get_logits(llm_t *h, float *out);
 /* Same into device memory (async). */
@@ -199,6 +204,14 @@ int llm_op_kv_write(llm_t *h, int32_t layer, const void *k_d, const void *v_d, i
  * kernel. */
 int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_t T,
                      int32_t pos0, void *out_d);
+
+/* Run `reps` decode steps at prev_pos without the captured graph, with HIP
+ * events on the handle's stream around every kernel, and write the mean
+ * milliseconds per step of each kernel class to ms_out[6]: 0 embedding,
+ * 1 RMSNorm, 2 layer projections (QKV, O, W1/W3, W2 with their epilogues),
+ * 3 attention (split-K and combine), 4 output head, 5 first-to-last event.
+ * Same preconditions and effects as llm_decode; synchronises. */
+int llm_profile_decode(llm_t *h, int32_t prev_pos, int32_t reps, float *ms_out);
 
 #ifdef __cplusplus
 }

@@ -57,6 +57,8 @@ EXPORTS = {
     "llm_sample": (C.c_int, [_vp, C.c_float, C.c_float, _vp, _vp]),
     "llm_sample_d": (C.c_int, [_vp, C.c_float, C.c_float, _vp, _vp]),
     "llm_set_tokens": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
+    "llm_set_tokens_d": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
+    "llm_profile_decode": (C.c_int, [_vp, C.c_int32, C.c_int32, _vp]),
     "llm_get_logits": (C.c_int, [_vp, _vp]),
     "llm_get_logits_d": (C.c_int, [_vp, _vp]),
     "llm_get_tokens": (C.c_int, [_vp, C.c_int32, _vp]),
@@ -163,6 +165,16 @@ class Handle:
         if mask is not None:
             m, mp = _arr(np.asarray(mask).astype(np.uint8), np.uint8)
         self._ck(_lib.llm_set_tokens(self.ptr, pos, tp, mp))
+
+    def set_tokens_d(self, pos: int, tokens_ptr: int, mask_ptr: int = 0):
+        self._ck(_lib.llm_set_tokens_d(self.ptr, pos, C.c_void_p(tokens_ptr), C.c_void_p(mask_ptr or None)))
+
+    PROFILE_CLASSES = ("embed", "rmsnorm", "projections", "attention", "head", "step")
+
+    def profile_decode(self, prev_pos: int, reps: int) -> dict:
+        out = np.zeros(6, np.float32)
+        self._ck(_lib.llm_profile_decode(self.ptr, prev_pos, reps, out.ctypes.data_as(C.c_void_p)))
+        return dict(zip(self.PROFILE_CLASSES, out.tolist()))
 
     def get_logits(self) -> np.ndarray:
         out = np.empty((self.B, self.V), np.float32)

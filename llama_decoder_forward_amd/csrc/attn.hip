@@ -28,36 +28,34 @@ __device__ __forceinline__ int perm_key(int t, int r) { return 8 * (r >> 2) + 4 
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp(m_old - m_new) is never NaN
 
 // ---------------------------------------------------------------------------
-// Decode: split-K over the attended length.  Grid (B*Hkv, ceil(S/256)); each
-// of the 4 waves handles 64 keys for all n_rep query heads of the KV head,
-// so every K/V byte is read once per query group.  Partials (unnormalised
-// o, running max, running sum) go to part[(b*H + h)][sub] and are merged in
-// sub order by attn_combine_kernel.
+// Decode: one work-group of 8 waves per (row b, KV head).  The attended
+// length L = pos + 1 is walked in 32-key steps, wave w taking steps w, w+8,
+// ...; each wave keeps the running max / sum / unnormalised output of all
+// n_rep query heads of the group, so every K/V byte is read once per query
+// group.  The 8 waves are merged in LDS in three halving rounds (fixed
+// order), and the normalised output written.
 // ---------------------------------------------------------------------------
-constexpr int DEC_KEYS_PER_WAVE = 64;
+constexpr int DEC_WAVES = 8;
 
-__global__ __launch_bounds__(256) void attn_decode_kernel(const half_t *__restrict__ q,
-                                                          const half_t *__restrict__ kc,
-                                                          const half_t *__restrict__ vc, int H,
-                                                          int Hkv, int S, const int *pos_dev,
-                                                          int pos_imm, float *part, int nsub)
+__global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
+    const half_t *__restrict__ q, const half_t *__restrict__ kc, const half_t *__restrict__ vc,
+    int H, int Hkv, int S, const int *pos_dev, int pos_imm, half_t *__restrict__ out)
 {
-    const int hd = 128;
+    constexpr int hd = 128;
+    __shared__ floatx4 so[DEC_WAVES / 2][8][64];
+    __shared__ float sm[DEC_WAVES / 2][16], sl[DEC_WAVES / 2][16];
     const int bk = blockIdx.x, b = bk / Hkv, kvh = bk % Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int L = (pos_dev ? *pos_dev : pos_imm) + 1;
-    const int sub = blockIdx.y * 4 + wave;
-    const int key0 = sub * DEC_KEYS_PER_WAVE;
-    if (key0 >= L) return;
     const int n_rep = H / Hkv;
     const int r = lane & 15, g = lane >> 4;
     const bool qv = r < n_rep;
     const int h = kvh * n_rep + r;
     const float scale = 1.0f / sqrtf((float)hd);
-
-    // Q^T as B operand: column r (query head), k-group g over the 4 d-steps.
-    half8 qb[4];
+    const int nsteps = (L + 31) / 32;
     const half8 z = {};
+
+    half8 qb[4];
     const half_t *qrow = q + ((int64_t)b * H + (qv ? h : 0)) * hd;
 #pragma unroll
     for (int s = 0; s < 4; s++) qb[s] = qv ? *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g) : z;
@@ -70,25 +68,38 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const half_t *__restri
     for (int dt = 0; dt < 8; dt++) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     float mrun = kNegBig, lrun = 0.f;
 
-    for (int st = 0; st < DEC_KEYS_PER_WAVE / 32; st++) {
-        const int k0 = key0 + 32 * st;
-        if (k0 >= L) break;
-        // S^T for the two permuted sub-tiles
-        floatx4 sc[2];
+    for (int st = wave; st < nsteps; st += DEC_WAVES) {
+        const int k0 = 32 * st;
+        // all K and V operands of the step are loaded before any arithmetic
+        half8 kf[2][4], vf[8];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
             const int key = k0 + perm_key(t, r);
-            const bool kv_ok = key < L;
-            const half_t *krow = K + (int64_t)(kv_ok ? key : 0) * hd + 8 * g;
+            const bool ok = key < L;
+            const half_t *krow = K + (int64_t)(ok ? key : 0) * hd + 8 * g;
+#pragma unroll
+            for (int s = 0; s < 4; s++) kf[t][s] = ok ? *reinterpret_cast<const half8 *>(krow + 32 * s) : z;
+        }
+        const int kk = k0 + 8 * g;
+        const bool vok = kk + 8 <= L;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) {
+            const half_t *vrow = V + (int64_t)(16 * dt + r) * S + kk;
+            if (vok) {
+                vf[dt] = *reinterpret_cast<const half8 *>(vrow);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; e++) vf[dt][e] = (kk + e < L) ? vrow[e] : (half_t)0.f;
+            }
+        }
+        floatx4 sc[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
             floatx4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; s++) {
-                half8 kf = kv_ok ? *reinterpret_cast<const half8 *>(krow + 32 * s) : z;
-                a = mfma16(kf, qb[s], a);
-            }
+            for (int s = 0; s < 4; s++) a = mfma16(kf[t][s], qb[s], a);
             sc[t] = a;
         }
-        // lane group g holds keys k0 + 8g + 4t + i for its query column
         float p[8];
         float mx = kNegBig;
 #pragma unroll
@@ -116,53 +127,43 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const half_t *__restri
         ls += __shfl_xor(ls, 32);
         lrun = lrun * fac + ls;
         mrun = mnew;
-        // O^T += V^T P^T over 8 d-tiles of 16
-        const int kk = k0 + 8 * g;
-        const bool vok = kk + 8 <= L;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) acc[dt] = mfma16(vf[dt], pb, acc[dt] * fac);
+    }
+
+    // merge: in each round the upper half of the live waves hands its state to
+    // the lower half (lane (r, g) holds O^T[16 dt + 4 g + i][head r])
+    for (int half = DEC_WAVES / 2; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half) {
+#pragma unroll
+            for (int dt = 0; dt < 8; dt++) so[wave - half][dt][lane] = acc[dt];
+            if (g == 0) {
+                sm[wave - half][r] = mrun;
+                sl[wave - half][r] = lrun;
+            }
+        }
+        __syncthreads();
+        if (wave < half) {
+            const float mo = sm[wave][r], lo = sl[wave][r];
+            const float M = fmaxf(mrun, mo);
+            const float fa = expf(mrun - M), fb = expf(mo - M);
+#pragma unroll
+            for (int dt = 0; dt < 8; dt++) acc[dt] = acc[dt] * fa + so[wave][dt][lane] * fb;
+            lrun = lrun * fa + lo * fb;
+            mrun = M;
+        }
+        __syncthreads();
+    }
+    if (wave == 0 && qv) {
+        half_t *orow = out + ((int64_t)b * H + h) * hd;
+        const float inv = 1.0f / lrun;
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) {
-            const half_t *vrow = V + (int64_t)(16 * dt + r) * S + kk;
-            half8 vf;
-            if (vok) {
-                vf = *reinterpret_cast<const half8 *>(vrow);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; e++) vf[e] = (kk + e < L) ? vrow[e] : (half_t)0.f;
-            }
-            acc[dt] = mfma16(vf, pb, acc[dt] * fac);
+            half4 hv;
+            for (int i = 0; i < 4; i++) hv[i] = (half_t)(acc[dt][i] * inv);
+            *reinterpret_cast<half4 *>(orow + 16 * dt + 4 * g) = hv;
         }
     }
-    if (!qv) return;
-    float *pp = part + (((int64_t)b * H + h) * nsub + sub) * (hd + 2);
-#pragma unroll
-    for (int dt = 0; dt < 8; dt++)
-        *reinterpret_cast<float4 *>(pp + 16 * dt + 4 * g) =
-            make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (g == 0) {
-        pp[hd] = mrun;
-        pp[hd + 1] = lrun;
-    }
-}
-
-// Merge the per-wave partials of one (b, h) in sub order; out = round(o / l).
-__global__ void attn_combine_kernel(const float *part, int H, int nsub, const int *pos_dev,
-                                    int pos_imm, half_t *out)
-{
-    const int hd = 128;
-    const int bh = blockIdx.x, d = threadIdx.x;
-    const int L = (pos_dev ? *pos_dev : pos_imm) + 1;
-    const int used = (L + DEC_KEYS_PER_WAVE - 1) / DEC_KEYS_PER_WAVE;
-    const float *pp = part + (int64_t)bh * nsub * (hd + 2);
-    float M = kNegBig;
-    for (int s = 0; s < used; s++) M = fmaxf(M, pp[(int64_t)s * (hd + 2) + hd]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < used; s++) {
-        const float *p = pp + (int64_t)s * (hd + 2);
-        float w = expf(p[hd] - M);
-        num += w * p[d];
-        den += w * p[hd + 1];
-    }
-    out[(int64_t)bh * hd + d] = (half_t)(num / den);
 }
 
 // ---------------------------------------------------------------------------
@@ -378,15 +379,9 @@ __global__ void kv_write_kernel(const Tv *k, const Tv *v, int T, int pos0, int H
 
 hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s)
 {
-    const int nsub = (a.S + DEC_KEYS_PER_WAVE - 1) / DEC_KEYS_PER_WAVE;
-    const int chunks = (a.S + 4 * DEC_KEYS_PER_WAVE - 1) / (4 * DEC_KEYS_PER_WAVE);
-    hipLaunchKernelGGL(attn_decode_kernel, dim3(a.B * a.Hkv, chunks), dim3(256), 0, s,
-                       (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache,
-                       a.H, a.Hkv, a.S, a.pos_dev, a.pos_imm, a.part, nsub);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.H), dim3(128), 0, s, (const float *)a.part,
-                       a.H, nsub, a.pos_dev, a.pos_imm, (half_t *)a.out);
+    hipLaunchKernelGGL(attn_decode_kernel, dim3(a.B * a.Hkv), dim3(DEC_WAVES * 64), 0, s,
+                       (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache, a.H,
+                       a.Hkv, a.S, a.pos_dev, a.pos_imm, (half_t *)a.out);
     return hipGetLastError();
 }
 

@@ -64,9 +64,13 @@ struct GemmArgs {
     int64_t ldx;
     int M, N, K;
     Epilogue ep;
-    float *partials;   // split-K scratch for the skinny path
-    int *counters;     // per-n-tile arrival counters (zeroed, self-resetting)
+    const void *norm_w;  // RMSNorm weight applied to the X rows first (only where
+                         // skinny_can_normalise(M, K)), or NULL
+    float eps;
 };
+
+// Whether the fp16 product normalises its own input rows for M rows of K.
+bool skinny_can_normalise(int M, int K);
 
 hipError_t launch_gen_weights_f16(half_t *dst, int mat, int64_t N, int64_t K, uint64_t seed,
                                   int layer, int H, int Hkv, int hd, int F, bool tiled,
@@ -96,8 +100,6 @@ struct AttnArgs {
     int B, T, H, Hkv, hd, S;
     const int *pos_dev;    // decode: device position, else NULL
     int pos_imm;
-    float *part;           // decode split-K partials
-    int max_chunks;
 };
 hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s);
@@ -116,5 +118,3 @@ hipError_t launch_set_int(int *dst, int v, hipStream_t s);
 hipError_t launch_set_tokens(int32_t *tok, int64_t tok_ld, int B, int col, const int32_t *vals,
                              const uint8_t *mask, hipStream_t s);
 
-// Attention split size for the decode kernel (keys per work-group).
-constexpr int ATTN_DEC_CHUNK = 256;

@@ -107,59 +107,138 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
 
 // ---------------------------------------------------------------------------
 // Skinny product for M <= 32 rows (decode steps, short prompts): weight
-// streaming.  One work-group per 16-row tile of W; its NW waves split K into
-// contiguous ranges, each streaming 1 KiB tiles straight into VGPRs with U
-// loads in flight, and the fragments are summed in wave order through LDS.
+// streaming.  A work-group owns TPB consecutive 16-row tiles of W and its NW
+// waves interleave over K: in each round the work-group reads NW*U
+// consecutive 1 KiB tiles of every owned row block (wave w the U tiles
+// starting at w*U) straight into VGPRs.  The per-wave fragments are summed in
+// wave order through LDS.
+//
+// STAGE (M <= 2): the activation rows are first copied into LDS by the whole
+// work-group while the first round of weight tiles is in flight; with NORM
+// they are RMS-normalised there (walkthrough section 3.2: r = 1/sqrt(mean
+// x^2 + eps), round(round(x r) w)), so the normalisation costs no launch.
+// Without STAGE, activation fragments are loaded from global memory (cache)
+// once per round and reused for the TPB row blocks.
 // ---------------------------------------------------------------------------
-template <int NW, int U>
+constexpr int STAGE_MAX_BYTES = 48 * 1024;
+
+template <int NW, int U, int TPB, bool TWO, bool STAGE, bool NORM>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__restrict__ W,
                                                               const half_t *__restrict__ X,
                                                               int64_t ldx, int M, int N, int K,
-                                                              Epilogue ep)
+                                                              Epilogue ep, const half_t *__restrict__ nw,
+                                                              float eps)
 {
-    __shared__ floatx4 red[NW][2][64];
-    const int nt = blockIdx.x;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int KT = K >> 5;
-    const int kt0 = (KT * wave) / NW, kt1 = (KT * (wave + 1)) / NW;
-    const half8 *Wt = reinterpret_cast<const half8 *>(W) + (int64_t)nt * KT * 64 + lane;
+    extern __shared__ half8 xs[];  // STAGE: [M][K/8]
+    __shared__ floatx4 red[NW][TPB][TWO ? 2 : 1][64];
+    __shared__ float pss[NW][2];
+    const int nt0 = blockIdx.x * TPB;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int KT = K >> 5, K8 = K >> 3;
+    const half8 *Wt = reinterpret_cast<const half8 *>(W) + (int64_t)nt0 * KT * 64 + lane;
     const int mc = lane & 15, g = lane >> 4;
-    const bool two = M > 16;
     const bool h0 = mc < M, h1 = mc + 16 < M;
+    const half8 z = {};
+
+    int base = wave * U;
+    half8 w[TPB][U];
+#pragma unroll
+    for (int t = 0; t < TPB; t++)
+#pragma unroll
+        for (int u = 0; u < U; u++) w[t][u] = (base + u < KT) ? Wt[((int64_t)t * KT + base + u) * 64] : z;
+
+    if (STAGE) {
+        for (int m = 0; m < M; m++) {
+            float ss = 0.f;
+            for (int i = tid; i < K8; i += NW * 64) {
+                half8 v = reinterpret_cast<const half8 *>(X + (int64_t)m * ldx)[i];
+                xs[m * K8 + i] = v;
+                if (NORM) {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) { float f = (float)v[e]; ss += f * f; }
+                }
+            }
+            if (NORM) {
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+                if (lane == 0) pss[wave][m] = ss;
+            }
+        }
+        __syncthreads();
+        if (NORM) {
+#pragma clang fp contract(off)
+            for (int m = 0; m < M; m++) {
+                float t = 0.f;
+                for (int ww = 0; ww < NW; ww++) t += pss[ww][m];
+                const float r = __frcp_rn(__fsqrt_rn(t / (float)K + eps));
+                for (int i = tid; i < K8; i += NW * 64) {
+                    half8 v = xs[m * K8 + i], wv = reinterpret_cast<const half8 *>(nw)[i];
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        float n = (float)(half_t)((float)v[e] * r);
+                        v[e] = (half_t)(n * (float)wv[e]);
+                    }
+                    xs[m * K8 + i] = v;
+                }
+            }
+            __syncthreads();
+        }
+    }
     const half_t *x0 = X + (int64_t)(h0 ? mc : 0) * ldx + 8 * g;
     const half_t *x1 = X + (int64_t)(h1 ? mc + 16 : 0) * ldx + 8 * g;
-    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    const half8 z = {};
-    for (int kt = kt0; kt < kt1; kt += U) {
-        half8 w[U], b0[U], b1[U];
+    const half8 *xl = STAGE ? xs + (h0 ? mc : 0) * K8 + g : nullptr;
+
+    floatx4 acc[TPB][TWO ? 2 : 1];
 #pragma unroll
-        for (int u = 0; u < U; u++) w[u] = (kt + u < kt1) ? Wt[(int64_t)(kt + u) * 64] : z;
+    for (int t = 0; t < TPB; t++)
 #pragma unroll
-        for (int u = 0; u < U; u++)
-            b0[u] = (h0 && kt + u < kt1) ? *reinterpret_cast<const half8 *>(x0 + (kt + u) * 32) : z;
-        if (two) {
+        for (int c = 0; c < (TWO ? 2 : 1); c++) acc[t][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (; base < KT; base += NW * U) {
+        half8 b0[U], b1[TWO ? U : 1];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const bool ok = h0 && base + u < KT;
+            if (STAGE) b0[u] = ok ? xl[(base + u) * 4] : z;
+            else b0[u] = ok ? *reinterpret_cast<const half8 *>(x0 + (base + u) * 32) : z;
+        }
+        if (TWO) {
 #pragma unroll
             for (int u = 0; u < U; u++)
-                b1[u] = (h1 && kt + u < kt1) ? *reinterpret_cast<const half8 *>(x1 + (kt + u) * 32) : z;
+                b1[u] = (h1 && base + u < KT) ? *reinterpret_cast<const half8 *>(x1 + (base + u) * 32) : z;
         }
 #pragma unroll
-        for (int u = 0; u < U; u++) acc0 = mfma16(w[u], b0[u], acc0);
-        if (two) {
+        for (int t = 0; t < TPB; t++)
 #pragma unroll
-            for (int u = 0; u < U; u++) acc1 = mfma16(w[u], b1[u], acc1);
+            for (int u = 0; u < U; u++) {
+                acc[t][0] = mfma16(w[t][u], b0[u], acc[t][0]);
+                if (TWO) acc[t][TWO ? 1 : 0] = mfma16(w[t][u], b1[TWO ? u : 0], acc[t][TWO ? 1 : 0]);
+            }
+        const int nb = base + NW * U;
+        if (nb < KT) {
+#pragma unroll
+            for (int t = 0; t < TPB; t++)
+#pragma unroll
+                for (int u = 0; u < U; u++) w[t][u] = (nb + u < KT) ? Wt[((int64_t)t * KT + nb + u) * 64] : z;
         }
     }
-    red[wave][0][lane] = acc0;
-    red[wave][1][lane] = acc1;
+#pragma unroll
+    for (int t = 0; t < TPB; t++)
+#pragma unroll
+        for (int c = 0; c < (TWO ? 2 : 1); c++) red[wave][t][c][lane] = acc[t][c];
     __syncthreads();
     if (wave != 0) return;
-    floatx4 s0 = red[0][0][lane], s1 = red[0][1][lane];
-    for (int w = 1; w < NW; w++) {
-        s0 += red[w][0][lane];
-        s1 += red[w][1][lane];
+#pragma unroll
+    for (int t = 0; t < TPB; t++) {
+        floatx4 s0 = red[0][t][0][lane];
+        for (int ww = 1; ww < NW; ww++) s0 += red[ww][t][0][lane];
+        epilogue_frag(ep, (nt0 + t) * 16, mc, h0, s0, lane);
+        if (TWO) {
+            floatx4 s1 = red[0][t][TWO ? 1 : 0][lane];
+            for (int ww = 1; ww < NW; ww++) s1 += red[ww][t][TWO ? 1 : 0][lane];
+            epilogue_frag(ep, (nt0 + t) * 16, mc + 16, h1, s1, lane);
+        }
     }
-    epilogue_frag(ep, nt * 16, mc, h0, s0, lane);
-    if (two) epilogue_frag(ep, nt * 16, mc + 16, h1, s1, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -336,16 +415,36 @@ __global__ void linear_f32_kernel(const float *W, const float *X, int64_t ldx, i
 
 }  // namespace
 
+bool skinny_can_normalise(int M, int K) { return M <= 2 && (int64_t)M * K * 2 <= STAGE_MAX_BYTES; }
+
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
 {
     if (a.M <= 0) return hipSuccess;
-    if (a.M <= 32) {
-        hipLaunchKernelGGL((gemm_skinny_kernel<8, 8>), dim3(a.N / 16), dim3(512), 0, s,
-                           (const half_t *)a.W, (const half_t *)a.X, a.ldx, a.M, a.N, a.K, a.ep);
+    const half_t *W = (const half_t *)a.W, *X = (const half_t *)a.X, *nw = (const half_t *)a.norm_w;
+    if (nw && !skinny_can_normalise(a.M, a.K)) return hipErrorInvalidValue;
+    const dim3 blk(512);
+    if (a.M <= 2 && (int64_t)a.M * a.K * 2 <= STAGE_MAX_BYTES) {
+        const size_t lds = (size_t)a.M * a.K * 2;
+        if (nw)
+            hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, true, true>), dim3(a.N / 16), blk, lds, s, W, X,
+                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
+        else
+            hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, true, false>), dim3(a.N / 16), blk, lds, s, W,
+                               X, a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
+    } else if (a.M <= 16) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, false, false>), dim3(a.N / 16), blk, 0, s, W, X,
+                           a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
+    } else if (a.M <= 32) {
+        // two row blocks per work-group reuse each activation fragment twice
+        if ((a.N / 16) % 2 == 0)
+            hipLaunchKernelGGL((gemm_skinny_kernel<8, 4, 2, true, false, false>), dim3(a.N / 32), blk, 0, s, W, X,
+                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
+        else
+            hipLaunchKernelGGL((gemm_skinny_kernel<8, 4, 1, true, false, false>), dim3(a.N / 16), blk, 0, s, W, X,
+                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
     } else {
         int NB = (a.N + BIG_BN - 1) / BIG_BN, MB = (a.M + BIG_BM - 1) / BIG_BM;
-        hipLaunchKernelGGL(gemm_big_kernel, dim3(NB * MB), dim3(256), 0, s, (const half_t *)a.W,
-                           (const half_t *)a.X, a.ldx, a.M, a.N, a.K, a.ep);
+        hipLaunchKernelGGL(gemm_big_kernel, dim3(NB * MB), dim3(256), 0, s, W, X, a.ldx, a.M, a.N, a.K, a.ep);
     }
     return hipGetLastError();
 }

@@ -1,5 +1,6 @@
 // Host side of the library: parameter checks, call-protocol state, device
 // memory plan, and the order of kernels for a prefill and a decode step.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -49,7 +50,7 @@ std::string check(const llm_params *p, Dims *d)
     if (F < 1 || F > (1 << 24)) return "ffn width out of range";
     if (p->dtype == LLM_F16) {
         if (hd != 128) return "fp16 models need head_dim 128";
-        if (p->dim % 64) return "fp16 models need dim % 64 == 0";
+        if (p->dim % 64 || p->dim > 8192) return "fp16 models need dim % 64 == 0 and dim <= 8192";
         if (F % 64) return "fp16 models need the ffn width to be a multiple of 64";
         if (p->vocab_size % 16) return "fp16 models need vocab_size % 16 == 0";
         if (p->max_seq_len % 64) return "fp16 models need max_seq_len % 64 == 0";
@@ -87,7 +88,7 @@ struct llm {
     int64_t kv_layer_bytes = 0;  // K part then V part
     float *rope = nullptr;
     int32_t *tok = nullptr;
-    float *logits = nullptr, *probs = nullptr, *uni = nullptr, *attn_part = nullptr;
+    float *logits = nullptr, *probs = nullptr, *uni = nullptr;
     int32_t *outtok = nullptr, *stage_i32 = nullptr;
     uint8_t *stage_mask = nullptr;
     int *pos_dev = nullptr;
@@ -209,7 +210,7 @@ const char *mat_ptr(llm_t *h, int layer, int mat)
 }
 
 hipError_t run_linear(llm_t *h, int layer, int mat, const void *X, int64_t ldx, int M,
-                      const Epilogue &ep)
+                      const Epilogue &ep, const void *norm_w = nullptr)
 {
     GemmArgs a{};
     a.W = mat_ptr(h, layer, mat);
@@ -219,8 +220,15 @@ hipError_t run_linear(llm_t *h, int layer, int mat, const void *X, int64_t ldx, 
     a.N = (int)mat_rows(h->d, mat);
     a.K = (int)mat_cols(h->d, mat);
     a.ep = ep;
+    a.norm_w = norm_w;
+    a.eps = h->p.norm_eps;
     return h->d.dtype == LLM_F16 ? launch_gemm_f16(a, h->stream) : launch_linear_f32(a, h->stream);
 }
+
+// RMSNorm followed by a product: folded into the product (rows staged and
+// normalised in LDS) for one or two fp16 rows, else a normalisation kernel
+// writing xn and the product on xn.
+bool fuse_norm(const llm_t *h, int M) { return h->d.dtype == LLM_F16 && skinny_can_normalise(M, h->d.D); }
 
 Epilogue make_ep(int kind, void *out, int64_t ldo)
 {
@@ -232,27 +240,66 @@ Epilogue make_ep(int kind, void *out, int64_t ldo)
     return e;
 }
 
+// Optional per-launch timing: events recorded around every kernel of a
+// forward pass, attributed to a kernel class.
+struct Prof {
+    std::vector<hipEvent_t> ev;  // pairs
+    std::vector<int> cls;
+    size_t used = 0;
+};
+
+enum ProfClass { PC_EMBED = 0, PC_NORM = 1, PC_PROJ = 2, PC_ATTN = 3, PC_HEAD = 4, PC_N = 6 };
+
+hipError_t prof_mark(Prof *pf, int cls, hipStream_t s)
+{
+    if (!pf) return hipSuccess;
+    if (pf->used + 2 > pf->ev.size()) {
+        for (int i = 0; i < 64; i++) {
+            hipEvent_t e;
+            hipError_t r = hipEventCreate(&e);
+            if (r != hipSuccess) return r;
+            pf->ev.push_back(e);
+        }
+    }
+    pf->cls.resize(pf->used / 2 + 1);
+    pf->cls[pf->used / 2] = cls;
+    return hipEventRecord(pf->ev[pf->used++], s);
+}
+
+hipError_t prof_end(Prof *pf, hipStream_t s)
+{
+    if (!pf) return hipSuccess;
+    return hipEventRecord(pf->ev[pf->used++], s);
+}
+
 // The forward pass over B rows of T tokens (walkthrough sections 2, 3.5-3.8).
 // Decode (pos_dev != NULL, T == 1) reads its position from device memory so
 // that the launch sequence can be captured once and replayed.
-hipError_t forward(llm_t *h, int B, int T, const int *pos_dev)
+hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullptr)
 {
     const Dims &d = h->d;
     const int M = B * T;
     const int64_t qd = (int64_t)d.H * d.hd;
     hipStream_t s = h->stream;
     hipError_t e;
-#define TRY(x)                        \
+#define TRY_RAW(x)                    \
     do {                              \
         if ((e = (x)) != hipSuccess) \
             return e;                 \
     } while (0)
-    TRY(launch_embed(h->emb, h->tok, d.S, B, T, pos_dev, d.D, d.dtype, h->x, s));
+#define TRYC(cls, x)                       \
+    do {                                   \
+        TRY_RAW(prof_mark(pf, (cls), s)); \
+        TRY_RAW(x);                        \
+        TRY_RAW(prof_end(pf, s));          \
+    } while (0)
+    TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, B, T, pos_dev, d.D, d.dtype, h->x, s));
     for (int l = 0; l < d.NL; l++) {
         const char *nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
         const char *nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
+        const bool fused = fuse_norm(h, M);
         // attention_norm -> wq|wk|wv with RoPE and the KV-cache write
-        TRY(launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s));
+        if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s));
         Epilogue eq = make_ep(EP_QKV, h->q, qd);
         eq.kcache = layer_kc(h, l);
         eq.vcache = layer_vc(h, l);
@@ -261,28 +308,39 @@ hipError_t forward(llm_t *h, int B, int T, const int *pos_dev)
         eq.pos_imm = 0;
         eq.T = T;
         eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = d.S;
-        TRY(run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq));
+        if (fused) TRYC(PC_PROJ, run_linear(h, l, MAT_QKV, h->x, d.D, M, eq, nw_attn));
+        else TRYC(PC_PROJ, run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq));
         // attention over the cache
         AttnArgs aa{};
         aa.q = h->q; aa.kcache = eq.kcache; aa.vcache = eq.vcache; aa.out = h->o;
         aa.B = B; aa.T = T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
-        aa.pos_dev = pos_dev; aa.pos_imm = 0; aa.part = h->attn_part;
-        if (d.dtype == LLM_F32) TRY(launch_attn_f32(aa, s));
-        else if (pos_dev) TRY(launch_attn_decode_f16(aa, s));
-        else TRY(launch_attn_prefill_f16(aa, s));
+        aa.pos_dev = pos_dev; aa.pos_imm = 0;
+        if (d.dtype == LLM_F32) TRYC(PC_ATTN, launch_attn_f32(aa, s));
+        else if (pos_dev) TRYC(PC_ATTN, launch_attn_decode_f16(aa, s));
+        else TRYC(PC_ATTN, launch_attn_prefill_f16(aa, s));
         // wo + residual
-        TRY(run_linear(h, l, MAT_O, h->o, qd, M, make_ep(EP_RESID, h->x, d.D)));
+        TRYC(PC_PROJ, run_linear(h, l, MAT_O, h->o, qd, M, make_ep(EP_RESID, h->x, d.D)));
         // ffn_norm -> w1|w3 with SwiGLU -> w2 + residual
-        TRY(launch_rmsnorm(h->x, d.D, nw_ffn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s));
-        TRY(run_linear(h, l, MAT_W13, h->xn, d.D, M, make_ep(EP_SWIGLU, h->g, d.F)));
-        TRY(run_linear(h, l, MAT_W2, h->g, d.F, M, make_ep(EP_RESID, h->x, d.D)));
+        if (fused) {
+            TRYC(PC_PROJ, run_linear(h, l, MAT_W13, h->x, d.D, M, make_ep(EP_SWIGLU, h->g, d.F), nw_ffn));
+        } else {
+            TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_ffn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s));
+            TRYC(PC_PROJ, run_linear(h, l, MAT_W13, h->xn, d.D, M, make_ep(EP_SWIGLU, h->g, d.F)));
+        }
+        TRYC(PC_PROJ, run_linear(h, l, MAT_W2, h->g, d.F, M, make_ep(EP_RESID, h->x, d.D)));
     }
     // final norm on the last position of each row, output head, fp32 logits
     const char *nw_final = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
-    TRY(launch_rmsnorm(h->x + (int64_t)(T - 1) * d.D * d.es, (int64_t)T * d.D, nw_final, B, d.D,
-                       h->p.norm_eps, d.dtype, h->xn, s));
-    TRY(run_linear(h, 0, MAT_HEAD, h->xn, d.D, B, make_ep(EP_LOGITS, h->logits, d.V)));
-#undef TRY
+    const char *xlast = h->x + (int64_t)(T - 1) * d.D * d.es;
+    if (fuse_norm(h, B)) {
+        TRYC(PC_HEAD, run_linear(h, 0, MAT_HEAD, xlast, (int64_t)T * d.D, B, make_ep(EP_LOGITS, h->logits, d.V),
+                                 nw_final));
+    } else {
+        TRYC(PC_NORM, launch_rmsnorm(xlast, (int64_t)T * d.D, nw_final, B, d.D, h->p.norm_eps, d.dtype, h->xn, s));
+        TRYC(PC_HEAD, run_linear(h, 0, MAT_HEAD, h->xn, d.D, B, make_ep(EP_LOGITS, h->logits, d.V)));
+    }
+#undef TRYC
+#undef TRY_RAW
     return hipSuccess;
 }
 
@@ -384,11 +442,6 @@ int create_impl(llm_t *h, uint64_t seed)
     h->outtok = (int32_t *)(h->uni + d.maxB);
     h->stage_i32 = h->outtok + d.maxB;
     h->stage_mask = (uint8_t *)(h->stage_i32 + d.maxB);
-    const int nsub = (d.S + 63) / 64;
-    if (d.dtype == LLM_F16) {
-        HIPM(h, hipMalloc(&p, (int64_t)d.maxB * d.H * nsub * (d.hd + 2) * sizeof(float)));
-        h->attn_part = (float *)p;
-    }
     int rc = ensure_ws(h, d.maxB);
     if (rc) return rc;
     rc = build_weights(h, seed);
@@ -401,7 +454,7 @@ void release(llm_t *h)
 {
     if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
     void *bufs[] = {h->wts, h->emb, h->norm_w, h->kv, h->rope, h->tok, h->logits, h->probs,
-                    h->pos_dev, h->attn_part, h->ws};
+                    h->pos_dev, h->ws};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (h->own_stream && h->stream) (void)hipStreamDestroy(h->stream);
@@ -694,6 +747,54 @@ int llm_set_tokens(llm_t *h, int32_t pos, const int32_t *tokens, const uint8_t *
     return LLM_OK;
 }
 
+int llm_set_tokens_d(llm_t *h, int32_t pos, const int32_t *tokens_d, const uint8_t *mask_d)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!h->prefilled) return fail(h, LLM_ESTATE, "set_tokens before prefill");
+    if (pos < 0 || pos >= h->d.S) return fail(h, LLM_EINVAL, "pos must be in [0, max_seq_len)");
+    if (!tokens_d) return fail(h, LLM_EINVAL, "tokens is NULL");
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    HIPC(h, launch_set_tokens(h->tok, h->d.S, h->cur_B, pos, tokens_d, mask_d, h->stream));
+    if (!mask_d) h->col_written[pos] = 1;
+    return LLM_OK;
+}
+
+int llm_profile_decode(llm_t *h, int32_t prev_pos, int32_t reps, float *ms_out)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!ms_out || reps < 1) return fail(h, LLM_EINVAL, "bad arguments");
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    if (!h->prefilled) return fail(h, LLM_ESTATE, "decode before prefill");
+    if (prev_pos < 1 || prev_pos >= h->d.S) return fail(h, LLM_EINVAL, "prev_pos must be in [1, max_seq_len)");
+    if (prev_pos > h->last_pos + 1) return fail(h, LLM_ESTATE, "prev_pos skips positions whose KV is not written");
+    if (!h->col_written[prev_pos]) return fail(h, LLM_ESTATE, "token column prev_pos has not been written");
+    Prof pf;
+    double acc[PC_N] = {0};
+    hipError_t e = hipSuccess;
+    for (int r = 0; r < reps && e == hipSuccess; r++) {
+        pf.used = 0;
+        e = launch_set_int(h->pos_dev, prev_pos, h->stream);
+        if (e == hipSuccess) e = forward(h, h->cur_B, 1, h->pos_dev, &pf);
+        if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+        for (size_t i = 0; e == hipSuccess && i + 1 < pf.used; i += 2) {
+            float ms = 0.f;
+            e = hipEventElapsedTime(&ms, pf.ev[i], pf.ev[i + 1]);
+            acc[pf.cls[i / 2]] += ms;
+        }
+        float all = 0.f;
+        if (e == hipSuccess && pf.used >= 2) e = hipEventElapsedTime(&all, pf.ev[0], pf.ev[pf.used - 1]);
+        acc[PC_N - 1] += all;
+    }
+    for (hipEvent_t ev : pf.ev) (void)hipEventDestroy(ev);
+    if (e != hipSuccess) return fail(h, LLM_EDEVICE, std::string("profile: ") + hipGetErrorString(e));
+    for (int c = 0; c < PC_N; c++) ms_out[c] = (float)(acc[c] / reps);
+    h->last_pos = prev_pos;
+    h->logits_valid = true;
+    return LLM_OK;
+}
+
 int llm_get_logits(llm_t *h, float *out)
 {
     int rc = guard(h);
@@ -846,7 +947,7 @@ int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_
     AttnArgs aa{};
     aa.q = q_d; aa.kcache = layer_kc(h, layer); aa.vcache = layer_vc(h, layer); aa.out = out_d;
     aa.B = B; aa.T = T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
-    aa.pos_dev = nullptr; aa.pos_imm = pos0; aa.part = h->attn_part;
+    aa.pos_dev = nullptr; aa.pos_imm = pos0;
     hipError_t e;
     if (d.dtype == LLM_F32) e = launch_attn_f32(aa, h->stream);
     else if (T == 1) e = launch_attn_decode_f16(aa, h->stream);

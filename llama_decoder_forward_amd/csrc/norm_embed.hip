@@ -33,31 +33,46 @@ __device__ __forceinline__ float block_sum(float v, float *red)
 }
 
 // RMSNorm (walkthrough section 3.2): r = 1/sqrt(mean(x^2) + eps) in fp32,
-// y = round(round(x * r) * w).  One work-group per row, 16-byte loads.
-__global__ void rmsnorm_f16_kernel(const half_t *x, int64_t ldx, const half_t *w, int D, float eps,
-                                   half_t *y)
+// y = round(round(x * r) * w).  One wave per row: 16-byte loads kept in
+// registers (D <= 64 * 8 * RMS_VEC), a shuffle-only reduction, no barrier.
+constexpr int RMS_VEC = 16;  // D up to 8192
+
+__global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64_t ldx, const half_t *w,
+                                                          int M, int D, float eps, half_t *y)
 {
-    __shared__ float red[kThreads / 64];
-    const half8 *xr = reinterpret_cast<const half8 *>(x + (int64_t)blockIdx.x * ldx);
-    half8 *yr = reinterpret_cast<half8 *>(y + (int64_t)blockIdx.x * D);
+#pragma clang fp contract(off)
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (row >= M) return;
+    const half8 *xr = reinterpret_cast<const half8 *>(x + (int64_t)row * ldx);
+    half8 *yr = reinterpret_cast<half8 *>(y + (int64_t)row * D);
     const half8 *wr = reinterpret_cast<const half8 *>(w);
-    int nv = D / 8;
+    const int nv = D / 8;
+    half8 v[RMS_VEC];
     float ss = 0.f;
-    for (int i = threadIdx.x; i < nv; i += blockDim.x) {
-        half8 v = xr[i];
 #pragma unroll
-        for (int e = 0; e < 8; e++) { float f = (float)v[e]; ss += f * f; }
-    }
-    float tot = block_sum(ss, red);
-    float r = __frcp_rn(__fsqrt_rn(tot / (float)D + eps));
-    for (int i = threadIdx.x; i < nv; i += blockDim.x) {
-        half8 v = xr[i], wv = wr[i], o;
+    for (int j = 0; j < RMS_VEC; j++) {
+        const int i = lane + 64 * j;
+        if (i < nv) {
+            v[j] = xr[i];
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            half_t n = (half_t)((float)v[e] * r);
-            o[e] = (half_t)((float)n * (float)wv[e]);
+            for (int e = 0; e < 8; e++) { float f = (float)v[j][e]; ss += f * f; }
         }
-        yr[i] = o;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const float r = __frcp_rn(__fsqrt_rn(ss / (float)D + eps));
+#pragma unroll
+    for (int j = 0; j < RMS_VEC; j++) {
+        const int i = lane + 64 * j;
+        if (i < nv) {
+            half8 wv = wr[i], o;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                half_t n = (half_t)((float)v[j][e] * r);
+                o[e] = (half_t)((float)n * (float)wv[e]);
+            }
+            yr[i] = o;
+        }
     }
 }
 
@@ -90,8 +105,8 @@ hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int 
 {
     if (M <= 0) return hipSuccess;
     if (dtype == 1)
-        hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(M), dim3(kThreads), 0, s, (const half_t *)x, ldx,
-                           (const half_t *)w, D, eps, (half_t *)y);
+        hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((M + 3) / 4), dim3(256), 0, s, (const half_t *)x, ldx,
+                           (const half_t *)w, M, D, eps, (half_t *)y);
     else
         hipLaunchKernelGGL(rmsnorm_f32_kernel, dim3(M), dim3(kThreads), 0, s, (const float *)x, ldx,
                            (const float *)w, D, eps, (float *)y);

@@ -124,6 +124,24 @@ def test_linear(B, small, mat, M):
     assert np.mean(d == 0) > 0.9
 
 
+def test_linear_odd_tile_count(B):
+    """A head of 1040 rows (65 row tiles, odd) for M in the two-column-group
+    range."""
+    kw = small_f16(vocab_size=1040)
+    h = B.llm_create(B.make_params(**kw), 79)
+    W = packed_weights(kw, 79, 0, 4)
+    rng = np.random.default_rng(16)
+    for M in (20, 32):
+        say("odd tiles", M)
+        x = randn_f16(rng, (M, kw["dim"]), 0.5)
+        xd, yd = dev(x), empty((M, 1040), np.float16)
+        h.op_linear(0, 4, xd.data_ptr(), M, yd.data_ptr())
+        y = host(yd).astype(np.float32)
+        want = oracle.linear(W, x.astype(np.float32), F16)
+        assert np.all(accumulation_close(y, want, W, x))
+    h.destroy()
+
+
 def accumulation_close(got, want, W, x):
     """Two results of the same fp32 dot products summed in different orders:
     within one fp16 rounding step, or within the fp32 accumulation error
@@ -205,6 +223,27 @@ def test_attention_decode(B, small, L):
     want = attention_reference(q, K, V, [L - 1], H // Hkv)
     assert np.max(np.abs(got - want)) < 4e-3, np.max(np.abs(got - want))
     assert cosine(got.reshape(-1, d), want.reshape(-1, d)).min() > 0.9999
+
+
+def test_attention_decode_single_split(B):
+    """B * n_kv_heads = 512 work-groups: one split per KV head, no merge."""
+    kw = small_f16(max_batch_size=256, max_seq_len=128)
+    h = B.llm_create(B.make_params(**kw), 78)
+    Bn, H, Hkv, d, L = 256, kw["n_heads"], kw["n_kv_heads"], 128, 77
+    rng = np.random.default_rng(15)
+    K = randn_f16(rng, (Bn, L, Hkv, d))
+    V = randn_f16(rng, (Bn, L, Hkv, d))
+    q = randn_f16(rng, (Bn, 1, H, d), 0.3)
+    say("attention decode single split")
+    kd, vd = dev(K), dev(V)
+    h.op_kv_write(0, kd.data_ptr(), vd.data_ptr(), Bn, L, 0)
+    qd, od = dev(q), empty((Bn, 1, H, d), np.float16)
+    h.op_attention(0, qd.data_ptr(), Bn, 1, L - 1, od.data_ptr())
+    got = host(od).astype(np.float32)
+    rows = [0, 77, 255]
+    want = attention_reference(q[rows], K[rows], V[rows], [L - 1], H // Hkv)
+    assert np.max(np.abs(got[rows] - want)) < 4e-3
+    h.destroy()
 
 
 @pytest.mark.parametrize("T", [1, 2, 63, 129, 200])

@@ -108,14 +108,15 @@ def small_kw(**kw):
     return base
 
 
-@pytest.mark.parametrize("T0", [5, 40])
-def test_small_fp16_forced(B, T0):
-    """GQA fp16 model, 3 rows: prompt 5 (M = 15, skinny products) and 40
-    (M = 120, tiled products), then 12 decode steps."""
+@pytest.mark.parametrize("rows,T0", [(3, 5), (3, 40), (1, 9), (2, 9), (1, 33)])
+def test_small_fp16_forced(B, rows, T0):
+    """GQA fp16 model: prompt 5 x 3 rows (M = 15, skinny products), 40 x 3
+    (M = 120, tiled products), one or two rows (decode products that
+    normalise their own input), then 12 decode steps."""
     kw = small_kw()
     steps = 12
-    toks = synth.tokens(41, 3, T0 + steps, kw["vocab_size"])
-    say("small fp16 forced", T0)
+    toks = synth.tokens(41, rows, T0 + steps, kw["vocab_size"])
+    say("small fp16 forced", rows, T0)
     h = B.llm_create(B.make_params(**kw), 91)
     got, _ = gpu_forced_logits(h, toks, T0, steps)
     want = oracle.forward_stream(ocfg(kw), 91, toks, T0 - 1)
