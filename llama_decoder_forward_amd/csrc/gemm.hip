@@ -345,6 +345,125 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const half_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Large prefill product (M >= 1024): block tile 256 (W rows) x 256 (tokens) x
+// 32 (K), four waves each owning a 128 x 128 quadrant (64 accumulator
+// fragments, held in AGPRs).  Operands travel global -> LDS with direct
+// loads (global_load_lds_dwordx4): each wave copies four 1 KiB W tiles (the
+// stored layout is already the operand order) and four X tiles gathered row
+// by row into operand order, through a ring of T256_NS stages so that
+// T256_NS-2 stages of loads stay in flight while one is multiplied.  Waits
+// are explicit counter waits plus a bare s_barrier (a full __syncthreads
+// would drain the in-flight stages every step).  Each wave reads all 16
+// operand fragments of a k-tile before its 64 MFMAs (a scheduling barrier
+// keeps the reads together).  Rows past N or M are clamped on load (never
+// stored).
+// ---------------------------------------------------------------------------
+constexpr int T256_NS = 4;
+constexpr int T256_LDS = T256_NS * 2 * 1024 * 16;  // bytes
+
+__device__ __forceinline__ void wait_vm_in_flight(bool keep)
+{
+    // keep: the T256_NS-2 newest stages (8 loads each per wave) stay in flight
+    if (keep) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_tile256_kernel(const half_t *__restrict__ W,
+                                                              const half_t *__restrict__ X, int64_t ldx,
+                                                              int M, int N, int K, Epilogue ep)
+{
+    static_assert(T256_NS == 4, "the counter waits assume four stages");
+    extern __shared__ half8 lds[];
+    half8 *lw = lds;                  // [NS][16 tiles][64 lanes]
+    half8 *lx = lds + T256_NS * 1024;  // [NS][16 tiles][64 lanes]
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wn = wave >> 1, wm = wave & 1;
+    const int NB = (N + 255) / 256, MB = (M + 255) / 256;
+    const int total = NB * MB;
+    int pid = blockIdx.x;
+    {  // XCD-aware remap, then groups of 4 token blocks per W block column
+        int per = total / 8, rem = total % 8, xcd = pid % 8, local = pid / 8;
+        pid = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+    }
+    const int group = 4 * NB;
+    const int first_mb = (pid / group) * 4;
+    const int gm = min(MB - first_mb, 4);
+    const int mb = first_mb + (pid % group) % gm;
+    const int nb = (pid % group) / gm;
+
+    const int KT = K >> 5, NT = N >> 4;
+    const half8 *Wv = reinterpret_cast<const half8 *>(W);
+    const half8 *wsrc[4];
+    const half_t *xsrc[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const int tile = wave * 4 + q;
+        wsrc[q] = Wv + (int64_t)min(nb * 16 + tile, NT - 1) * KT * 64 + lane;
+        const int m = min(mb * 256 + tile * 16 + (lane & 15), M - 1);
+        xsrc[q] = X + (int64_t)m * ldx + 8 * (lane >> 4);
+    }
+    floatx4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int st = 0; st < T256_NS - 1; st++) {
+        if (st < KT) {
+            const int buf = st % T256_NS;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int tile = wave * 4 + q;
+                __builtin_amdgcn_global_load_lds((const void *)(wsrc[q] + (int64_t)st * 64),
+                                                 (void *)(lw + buf * 1024 + tile * 64), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(xsrc[q] + st * 32),
+                                                 (void *)(lx + buf * 1024 + tile * 64), 16, 0, 0);
+            }
+        }
+    }
+    for (int kt = 0; kt < KT; kt++) {
+        // stage kt landed (own loads), then visible to every wave
+        wait_vm_in_flight(kt + T256_NS - 2 < KT);
+        __builtin_amdgcn_s_barrier();
+        const int nk = kt + T256_NS - 1;  // refill the slot read in step kt-1
+        if (nk < KT) {
+            const int buf = nk % T256_NS;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int tile = wave * 4 + q;
+                __builtin_amdgcn_global_load_lds((const void *)(wsrc[q] + (int64_t)nk * 64),
+                                                 (void *)(lw + buf * 1024 + tile * 64), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(xsrc[q] + nk * 32),
+                                                 (void *)(lx + buf * 1024 + tile * 64), 16, 0, 0);
+            }
+        }
+        const int cur = kt % T256_NS;
+        half8 a[8], b[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) a[i] = lw[cur * 1024 + (wn * 8 + i) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 8; j++) b[j] = lx[cur * 1024 + (wm * 8 + j) * 64 + lane];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+        // this wave's reads of slot `cur` are complete before anyone refills it
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int n0 = (nb * 16 + wn * 8 + i) * 16;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int m = (mb * 16 + wm * 8 + j) * 16 + (lane & 15);
+            epilogue_frag(ep, n0, m, m < M && n0 < N, acc[i][j], lane);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 models: plain row-major weights, one thread per output unit (a row, a
 // RoPE pair, or a w1/w3 pair), fp32 accumulation in k order.
 // ---------------------------------------------------------------------------
@@ -442,9 +561,13 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
         else
             hipLaunchKernelGGL((gemm_skinny_kernel<8, 4, 1, true, false, false>), dim3(a.N / 16), blk, 0, s, W, X,
                                a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
-    } else {
+    } else if (a.M < 1024) {
         int NB = (a.N + BIG_BN - 1) / BIG_BN, MB = (a.M + BIG_BM - 1) / BIG_BM;
         hipLaunchKernelGGL(gemm_big_kernel, dim3(NB * MB), dim3(256), 0, s, W, X, a.ldx, a.M, a.N, a.K, a.ep);
+    } else {
+        int NB = (a.N + 255) / 256, MB = (a.M + 255) / 256;
+        hipLaunchKernelGGL(gemm_tile256_kernel, dim3(NB * MB), dim3(256), T256_LDS, s, W, X, a.ldx, a.M, a.N,
+                           a.K, a.ep);
     }
     return hipGetLastError();
 }

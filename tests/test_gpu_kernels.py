@@ -106,7 +106,7 @@ def packed_weights(kw, seed, layer, mat):
 
 
 @pytest.mark.parametrize("mat", [0, 1, 2, 3, 4])
-@pytest.mark.parametrize("M", [1, 7, 16, 17, 32, 33, 200, 300])
+@pytest.mark.parametrize("M", [1, 2, 7, 16, 17, 32, 33, 200, 300, 1100, 2048])
 def test_linear(B, small, mat, M):
     h, kw = small
     W = packed_weights(kw, 77, 1, mat)
@@ -246,7 +246,7 @@ def test_attention_decode_single_split(B):
     h.destroy()
 
 
-@pytest.mark.parametrize("T", [1, 2, 63, 129, 200])
+@pytest.mark.parametrize("T", [1, 2, 63, 129, 200, 500])
 def test_attention_prefill(B, small, T):
     h, kw = small
     Bn, H, Hkv, d = 2, kw["n_heads"], kw["n_kv_heads"], kw["dim"] // kw["n_heads"]
