@@ -4,8 +4,8 @@
 // subtracted, weighted sum of values; query head h reads KV head h / n_rep
 // (repeat_kv, section 3.4).
 //
-// Cache layout (per layer): K[b][kvh][s][d] (key-major), V[b][kvh][d][s]
-// (d-major).  Both kernels compute S^T = K Q^T and O^T = V^T P^T with
+// Cache layout (per layer): K[b][kvh][s][d] (key-major), V in blocks of 32
+// keys, d-major inside a block (common.h).  Both kernels compute S^T = K Q^T and O^T = V^T P^T with
 // v_mfma_f32_16x16x32_f16, so the query is the MFMA column (lane % 16) and
 // each lane owns its query's running max / sum with no cross-lane moves.
 //
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
     for (int s = 0; s < 4; s++) qb[s] = qv ? *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g) : z;
 
     const half_t *K = kc + ((int64_t)b * Hkv + kvh) * S * hd;
-    const half_t *V = vc + ((int64_t)b * Hkv + kvh) * hd * S;
+    const half_t *V = vc + ((int64_t)b * Hkv + kvh) * S * hd;  // S/32 blocks of 32 x hd
 
     floatx4 acc[8];
 #pragma unroll
@@ -82,9 +82,10 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
         }
         const int kk = k0 + 8 * g;
         const bool vok = kk + 8 <= L;
+        const half_t *vblk = V + (int64_t)st * (32 * hd) + 8 * g;
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) {
-            const half_t *vrow = V + (int64_t)(16 * dt + r) * S + kk;
+            const half_t *vrow = vblk + (16 * dt + r) * 32;
             if (vok) {
                 vf[dt] = *reinterpret_cast<const half8 *>(vrow);
             } else {
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
     }
 
     const half_t *K = kc + ((int64_t)b * Hkv + kvh) * S * hd;
-    const half_t *V = vc + ((int64_t)b * Hkv + kvh) * hd * S;
+    const half_t *V = vc + ((int64_t)b * Hkv + kvh) * S * hd;  // S/32 blocks of 32 x hd
 
     floatx4 acc[2][8];
 #pragma unroll
@@ -225,13 +226,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
             const int key = c >> 4, dch = c & 15;  // K: 64 keys x 16 chunks of 8 d
             rk[j] = base + key < T ? *reinterpret_cast<const half8 *>(K + (int64_t)(base + key) * hd + dch * 8) : z;
             const int d = c >> 3, kch = c & 7;     // V^T: 128 d x 8 chunks of 8 keys
-            rv[j] = base + kch * 8 + 8 <= T
-                        ? *reinterpret_cast<const half8 *>(V + (int64_t)d * S + base + kch * 8)
-                        : z;
-            if (base + kch * 8 < T && base + kch * 8 + 8 > T) {
+            const int key0 = base + kch * 8;
+            const half_t *vp = V + (int64_t)(key0 >> 5) * (32 * hd) + d * 32 + (key0 & 31);
+            rv[j] = key0 + 8 <= T ? *reinterpret_cast<const half8 *>(vp) : z;
+            if (key0 < T && key0 + 8 > T) {
                 half8 t8;
-                for (int e = 0; e < 8; e++)
-                    t8[e] = base + kch * 8 + e < T ? V[(int64_t)d * S + base + kch * 8 + e] : (half_t)0.f;
+                for (int e = 0; e < 8; e++) t8[e] = key0 + e < T ? vp[e] : (half_t)0.f;
                 rv[j] = t8;
             }
         }
@@ -372,7 +372,10 @@ __global__ void kv_write_kernel(const Tv *k, const Tv *v, int T, int pos0, int H
     const int d = (int)(i % hd), kvh = (int)((i / hd) % Hkv), t = (int)(i / ((int64_t)hd * Hkv));
     const int pos = pos0 + t;
     kc[(((int64_t)b * Hkv + kvh) * S + pos) * hd + d] = k[(int64_t)b * per_row + i];
-    vc[(((int64_t)b * Hkv + kvh) * hd + d) * S + pos] = v[(int64_t)b * per_row + i];
+    if (sizeof(Tv) == 2)
+        vc[vblk_offset(b, kvh, d, pos, Hkv, S, hd)] = v[(int64_t)b * per_row + i];
+    else
+        vc[(((int64_t)b * Hkv + kvh) * hd + d) * S + pos] = v[(int64_t)b * per_row + i];
 }
 
 }  // namespace

@@ -28,6 +28,17 @@ __host__ __device__ inline int64_t tiled_offset(int64_t n, int64_t k, int64_t K)
     return (nt * (K >> 5) + kt) * 512 + lane * 8 + (k & 7);
 }
 
+// KV cache (per layer), fp16 models:
+//   K[b][kvh][s][d]            key-major: a key's 128 values are contiguous;
+//   V[b][kvh][s/32][d][s%32]   blocks of 32 keys, d-major inside a block, so a
+//                              32-key step reads one contiguous 8 KiB block and
+//                              a lane's 8 consecutive keys of one d are 16 bytes.
+// fp32 models use K[b][kvh][s][d] and V[b][kvh][d][s].
+__host__ __device__ inline int64_t vblk_offset(int64_t b, int kvh, int d, int pos, int Hkv, int S, int hd)
+{
+    return ((b * Hkv + kvh) * (int64_t)(S / 32) + pos / 32) * (int64_t)(hd * 32) + d * 32 + (pos & 31);
+}
+
 // Packed matrices of one layer, in stored row order.
 enum Mat { MAT_QKV = 0, MAT_O = 1, MAT_W13 = 2, MAT_W2 = 3, MAT_HEAD = 4, MAT_EMB = 5 };
 
@@ -46,8 +57,8 @@ struct Epilogue {
     void *out;            // STORE / RESID / LOGITS / QKV (q) / SWIGLU (g)
     int64_t ldo;          // row stride of out in elements
     // EP_QKV
-    void *kcache;         // this layer's K cache: [maxB][Hkv][S][hd]
-    void *vcache;         // this layer's V cache: [maxB][Hkv][hd][S]
+    void *kcache;         // this layer's K cache (layout above)
+    void *vcache;         // this layer's V cache (layout above)
     const float *rope;    // [S][hd/2][2] cos, sin
     const int *pos_dev;   // device position of token 0 (decode) or NULL
     int pos_imm;          // position of token 0 when pos_dev is NULL
@@ -94,8 +105,8 @@ hipError_t launch_linear_f32(const GemmArgs &a, hipStream_t s);
 
 struct AttnArgs {
     const void *q;         // [B*T][H][hd]
-    const void *kcache;    // [maxB][Hkv][S][hd]
-    const void *vcache;    // [maxB][Hkv][hd][S]
+    const void *kcache;    // layout above
+    const void *vcache;    // layout above
     void *out;             // [B*T][H][hd]
     int B, T, H, Hkv, hd, S;
     const int *pos_dev;    // decode: device position, else NULL

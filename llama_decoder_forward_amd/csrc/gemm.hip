@@ -81,8 +81,8 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
             }
         } else {
             const int r = n - qrows - krows, kvh = r / hd, d0 = r % hd;
-            half_t *vc = (half_t *)ep.vcache + (((int64_t)b * ep.Hkv + kvh) * hd + d0) * ep.S + pos;
-            for (int i = 0; i < 4; i++) vc[(int64_t)i * ep.S] = (half_t)acc[i];
+            half_t *vc = (half_t *)ep.vcache + vblk_offset(b, kvh, d0, pos, ep.Hkv, ep.S, hd);
+            for (int i = 0; i < 4; i++) vc[i * 32] = (half_t)acc[i];
         }
         break;
     }
