@@ -36,6 +36,23 @@ def decode_bytes_per_step(w, B, L_avg):
     return w.weight_bytes() + kv_read + kv_write
 
 
+def product_bytes(w, B):
+    """Algorithmic HBM bytes of one launch of each decode weight product at
+    batch B (fp16): the weight matrix once, the B activation rows in (plus
+    the RMSNorm weight where the norm runs inside the product), the outputs
+    out (the residual read and written back for wo and w2, q and the K/V
+    cache entries for wq|wk|wv, fp32 logits for the head)."""
+    D, hd, F, V = w.dim, w.head_dim, w.ffn_hidden(), w.vocab_size
+    qd, kvd = w.n_heads * hd, w.n_kv_heads * hd
+    return {
+        "qkv": 2 * ((qd + 2 * kvd) * D + B * D + D + B * (qd + 2 * kvd)),
+        "o": 2 * (D * qd + B * qd + 2 * B * D),
+        "w13": 2 * (2 * F * D + B * D + D + B * F),
+        "w2": 2 * (D * F + B * F + 2 * B * D),
+        "head": 2 * (V * D + B * D + D) + 4 * B * V,
+    }
+
+
 def prefill_flops(w, B, T):
     """2 * params * tokens for the layer matrices, causal attention
     2 * B * H * d * T (T + 1) per layer, head at the last position."""
@@ -78,10 +95,27 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default=configs.L7B_BS1.name, choices=sorted(configs.WORKLOADS))
+    ap.add_argument("--workload", default=configs.L7B_BS1.name,
+                    choices=sorted(k for k, v in configs.WORKLOADS.items() if v.dtype == configs.F16))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-reps", type=int, default=5)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device to device three times (a known-size kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -170,10 +204,17 @@ def main():
     # live per-kernel-class timing of one decode step (HIP events on the
     # library's stream), at the last position of the generate pass
     prof = h.profile_decode(T0 + steps - 1, args.profile_reps)
-    skinny_ms = prof["projections"] + prof["head"]
-    launches = 4 * w.n_layers + 1
-    wbytes = w.weight_bytes()
-    achieved = wbytes / (skinny_ms / 1e3) / 1e9
+    # the dominant kernel, the skinny GEMV of the decode weight products:
+    # the products of a decode step in forward order, replayed from a
+    # captured graph between two HIP events on the library's stream (and
+    # each kind on its own for the breakdown)
+    prod_us = h.profile_projections(args.profile_reps)
+    pbytes = product_bytes(w, B)
+    per_step = {k: (1 if k == "head" else w.n_layers) for k in pbytes}
+    launches = sum(per_step.values())
+    step_prod_bytes = sum(per_step[k] * pbytes[k] for k in pbytes)
+    step_prod_us = prod_us["step_order"] * launches
+    achieved = step_prod_bytes / (step_prod_us / 1e6) / 1e9
     L_avg = T0 + steps / 2
     step_bytes = decode_bytes_per_step(w, B, L_avg)
     step_roof_tok_s = B * HBM_PEAK_GBS * 1e9 / step_bytes
@@ -198,12 +239,16 @@ def main():
                    "decode_steps": steps, "temperature": temp, "top_p": top_p,
                    "layers": w.n_layers, "dim": w.dim, "heads": f"{w.n_heads}/{w.n_kv_heads}",
                    "ffn": w.ffn_hidden(), "vocab": w.vocab_size, "max_seq_len": S},
-        "roofline": {"bound": "hbm", "kernel": "gemm_skinny_kernel (all decode projections + head)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "gemm_skinny_kernel (decode weight products: wq|wk|wv, wo, w1|w3, w2, head)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": round(wbytes / launches),
-                     "avg_launch_us": round(skinny_ms * 1e3 / launches, 3),
-                     "launches_per_step": launches},
+                     "bytes_per_launch": round(step_prod_bytes / launches),
+                     "avg_launch_us": round(step_prod_us / launches, 3),
+                     "launches_per_step": launches,
+                     "us_per_launch_by_product": {k: round(v, 3) for k, v in prod_us.items()
+                                                  if k != "step_order"},
+                     "bytes_per_launch_by_product": pbytes},
         "detail": {
             "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
             "prefill_ms": round(prefill_ms, 3),

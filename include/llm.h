@@ -200,8 +200,8 @@ int llm_op_kv_write(llm_t *h, int32_t layer, const void *k_d, const void *v_d, i
 
 /* Attention of q[B][T][n_heads][head_dim] at positions pos0..pos0+T-1 over
  * the layer's cached keys 0..pos (causal), out in the same shape.  T == 1
- * runs the split-K decode kernel, T > 1 with pos0 == 0 the causal prefill
- * kernel. */
+ * runs the decode kernel (keys split over the waves of one workgroup per
+ * (row, KV head)), T > 1 with pos0 == 0 the causal prefill kernel. */
 int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_t T,
                      int32_t pos0, void *out_d);
 
@@ -209,9 +209,22 @@ int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_
  * events on the handle's stream around every kernel, and write the mean
  * milliseconds per step of each kernel class to ms_out[6]: 0 embedding,
  * 1 RMSNorm, 2 layer projections (QKV, O, W1/W3, W2 with their epilogues),
- * 3 attention (split-K and combine), 4 output head, 5 first-to-last event.
- * Same preconditions and effects as llm_decode; synchronises. */
+ * 3 attention, 4 output head, 5 first-to-last event.  Same preconditions
+ * and effects as llm_decode; synchronises. */
 int llm_profile_decode(llm_t *h, int32_t prev_pos, int32_t reps, float *ms_out);
+
+/* Time the decode step's weight products on their own, at the current
+ * batch and in the launch configuration, epilogue and RMSNorm fusion of a
+ * decode step.  Six passes, each captured once as a HIP graph and replayed
+ * between two HIP events on the handle's stream: pass k < 5 launches product
+ * kind k (0 wq|wk|wv, 1 wo, 2 w1|w3, 3 w2, 4 output head) over every layer
+ * (the head once) `reps` times; pass 5 launches all the products of a decode
+ * step in forward order `reps` times.  us_out[6] receives the mean
+ * microseconds per launch of each pass.  The launches read and write the
+ * workspace, the logits and the KV cache at the last decoded position with
+ * meaningless values, so the handle needs a new prefill before the next
+ * decode.  Requires a prefilled fp16 handle; synchronises. */
+int llm_profile_projections(llm_t *h, int32_t reps, float *us_out);
 
 #ifdef __cplusplus
 }

@@ -59,6 +59,7 @@ EXPORTS = {
     "llm_set_tokens": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
     "llm_set_tokens_d": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
     "llm_profile_decode": (C.c_int, [_vp, C.c_int32, C.c_int32, _vp]),
+    "llm_profile_projections": (C.c_int, [_vp, C.c_int32, _vp]),
     "llm_get_logits": (C.c_int, [_vp, _vp]),
     "llm_get_logits_d": (C.c_int, [_vp, _vp]),
     "llm_get_tokens": (C.c_int, [_vp, C.c_int32, _vp]),
@@ -175,6 +176,16 @@ class Handle:
         out = np.zeros(6, np.float32)
         self._ck(_lib.llm_profile_decode(self.ptr, prev_pos, reps, out.ctypes.data_as(C.c_void_p)))
         return dict(zip(self.PROFILE_CLASSES, out.tolist()))
+
+    PRODUCT_KINDS = ("qkv", "o", "w13", "w2", "head", "step_order")
+
+    def profile_projections(self, reps: int) -> dict:
+        """Mean microseconds per launch of each decode weight product and of
+        all of them in forward order, replayed from captured graphs; the
+        handle needs a new prefill afterwards."""
+        out = np.zeros(6, np.float32)
+        self._ck(_lib.llm_profile_projections(self.ptr, reps, out.ctypes.data_as(C.c_void_p)))
+        return dict(zip(self.PRODUCT_KINDS, out.tolist()))
 
     def get_logits(self) -> np.ndarray:
         out = np.empty((self.B, self.V), np.float32)

@@ -39,7 +39,7 @@ constexpr int DEC_WAVES = 8;
 
 __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
     const half_t *__restrict__ q, const half_t *__restrict__ kc, const half_t *__restrict__ vc,
-    int H, int Hkv, int S, const int *pos_dev, int pos_imm, half_t *__restrict__ out)
+    int H, int Hkv, int S, const int *pos_dev, int pos_imm, half_t *__restrict__ out, int out_mh)
 {
     constexpr int hd = 128;
     __shared__ floatx4 so[DEC_WAVES / 2][8][64];
@@ -162,7 +162,9 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
         for (int dt = 0; dt < 8; dt++) {
             half4 hv;
             for (int i = 0; i < 4; i++) hv[i] = (half_t)(acc[dt][i] * inv);
-            *reinterpret_cast<half4 *>(orow + 16 * dt + 4 * g) = hv;
+            const int c = 16 * dt + 4 * g;  // 4 consecutive columns inside one 8-column group
+            if (out_mh) *reinterpret_cast<half4 *>(out + xt_offset(b, (int64_t)h * hd + c, out_mh)) = hv;
+            else *reinterpret_cast<half4 *>(orow + c) = hv;
         }
     }
 }
@@ -382,9 +384,10 @@ __global__ void kv_write_kernel(const Tv *k, const Tv *v, int T, int pos0, int H
 
 hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s)
 {
+    if (a.out_mh && (a.out_mh > 2 || a.B > 16 * a.out_mh || a.T != 1)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_decode_kernel, dim3(a.B * a.Hkv), dim3(DEC_WAVES * 64), 0, s,
                        (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache, a.H,
-                       a.Hkv, a.S, a.pos_dev, a.pos_imm, (half_t *)a.out);
+                       a.Hkv, a.S, a.pos_dev, a.pos_imm, (half_t *)a.out, a.out_mh);
     return hipGetLastError();
 }
 

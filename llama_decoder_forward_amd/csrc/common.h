@@ -39,6 +39,17 @@ __host__ __device__ inline int64_t vblk_offset(int64_t b, int kvh, int d, int po
     return ((b * Hkv + kvh) * (int64_t)(S / 32) + pos / 32) * (int64_t)(hd * 32) + d * 32 + (pos & 31);
 }
 
+// Decode activations of 2 < M <= 32 rows, "fragment-major": the B operand of
+// v_mfma_f32_16x16x32_f16 for 16 rows and 32 columns is one contiguous
+// 1 KiB block, so a product's activation load is as coalesced as its weight
+// load.  Layout [K/32][mh][64 lanes][8] with mh = ceil(M/16) row halves;
+// element (m, k) lies in lane (m%16) + 16*((k%32)/8) of block (k/32, m/16).
+// Rows m >= M of the last half are never read.
+__host__ __device__ inline int64_t xt_offset(int m, int64_t k, int mh)
+{
+    return (((k >> 5) * mh + (m >> 4)) * 64 + (m & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
+}
+
 // Packed matrices of one layer, in stored row order.
 enum Mat { MAT_QKV = 0, MAT_O = 1, MAT_W13 = 2, MAT_W2 = 3, MAT_HEAD = 4, MAT_EMB = 5 };
 
@@ -64,6 +75,7 @@ struct Epilogue {
     int pos_imm;          // position of token 0 when pos_dev is NULL
     int T;                // tokens per batch row (m = b*T + t)
     int H, Hkv, hd, S;
+    int out_mh;           // EP_SWIGLU: g fragment-major with this many row halves, 0: row-major
 };
 
 // ---------------------------------------------------------------------------
@@ -71,8 +83,9 @@ struct Epilogue {
 // ---------------------------------------------------------------------------
 struct GemmArgs {
     const void *W;     // packed weights (tiled fp16 / row-major fp32)
-    const void *X;     // activations [M][K] (row stride ldx)
+    const void *X;     // activations [M][K] (row stride ldx), or fragment-major
     int64_t ldx;
+    int x_mh;          // > 0: X is fragment-major with this many row halves (M <= 32)
     int M, N, K;
     Epilogue ep;
     const void *norm_w;  // RMSNorm weight applied to the X rows first (only where
@@ -97,8 +110,9 @@ hipError_t launch_read_weights(const void *src, int dtype, int mat, int64_t N, i
 
 hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int B, int T,
                         const int *pos_dev, int D, int dtype, void *x, hipStream_t s);
+// y_mh > 0 writes y fragment-major (fp16, M <= 32) with that many row halves.
 hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int D, float eps,
-                          int dtype, void *y, hipStream_t s);
+                          int dtype, void *y, hipStream_t s, int y_mh = 0);
 
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s);
 hipError_t launch_linear_f32(const GemmArgs &a, hipStream_t s);
@@ -111,6 +125,7 @@ struct AttnArgs {
     int B, T, H, Hkv, hd, S;
     const int *pos_dev;    // decode: device position, else NULL
     int pos_imm;
+    int out_mh;            // decode: > 0 writes out fragment-major ([B][H*hd] rows)
 };
 hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s);

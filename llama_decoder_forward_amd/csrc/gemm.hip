@@ -99,7 +99,8 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
             float s = r16(a / (1.0f + expf(-a)));
             o[i] = (half_t)(s * r16(bv[i]));
         }
-        *reinterpret_cast<half4 *>((half_t *)ep.out + (int64_t)m * ep.ldo + f0) = o;
+        half_t *gp = (half_t *)ep.out + (ep.out_mh ? xt_offset(m, f0, ep.out_mh) : (int64_t)m * ep.ldo + f0);
+        *reinterpret_cast<half4 *>(gp) = o;
         break;
     }
     }
@@ -122,7 +123,7 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
 // ---------------------------------------------------------------------------
 constexpr int STAGE_MAX_BYTES = 48 * 1024;
 
-template <int NW, int U, int TPB, bool TWO, bool STAGE, bool NORM>
+template <int NW, int U, int TPB, bool TWO, bool STAGE, bool NORM, bool XT = false>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__restrict__ W,
                                                               const half_t *__restrict__ X,
                                                               int64_t ldx, int M, int N, int K,
@@ -187,6 +188,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
     const half_t *x0 = X + (int64_t)(h0 ? mc : 0) * ldx + 8 * g;
     const half_t *x1 = X + (int64_t)(h1 ? mc + 16 : 0) * ldx + 8 * g;
     const half8 *xl = STAGE ? xs + (h0 ? mc : 0) * K8 + g : nullptr;
+    // fragment-major X: block (kt, half) is 64 lanes x 16 bytes
+    const half8 *xt = reinterpret_cast<const half8 *>(X) + lane;
+    constexpr int MH = TWO ? 2 : 1;
 
     floatx4 acc[TPB][TWO ? 2 : 1];
 #pragma unroll
@@ -200,12 +204,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
         for (int u = 0; u < U; u++) {
             const bool ok = h0 && base + u < KT;
             if (STAGE) b0[u] = ok ? xl[(base + u) * 4] : z;
+            else if (XT) b0[u] = ok ? xt[(int64_t)(base + u) * MH * 64] : z;
             else b0[u] = ok ? *reinterpret_cast<const half8 *>(x0 + (base + u) * 32) : z;
         }
         if (TWO) {
 #pragma unroll
-            for (int u = 0; u < U; u++)
-                b1[u] = (h1 && base + u < KT) ? *reinterpret_cast<const half8 *>(x1 + (base + u) * 32) : z;
+            for (int u = 0; u < U; u++) {
+                const bool ok = h1 && base + u < KT;
+                if (XT) b1[u] = ok ? xt[((int64_t)(base + u) * MH + 1) * 64] : z;
+                else b1[u] = ok ? *reinterpret_cast<const half8 *>(x1 + (base + u) * 32) : z;
+            }
         }
 #pragma unroll
         for (int t = 0; t < TPB; t++)
@@ -227,17 +235,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
 #pragma unroll
         for (int c = 0; c < (TWO ? 2 : 1); c++) red[wave][t][c][lane] = acc[t][c];
     __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int t = 0; t < TPB; t++) {
-        floatx4 s0 = red[0][t][0][lane];
-        for (int ww = 1; ww < NW; ww++) s0 += red[ww][t][0][lane];
-        epilogue_frag(ep, (nt0 + t) * 16, mc, h0, s0, lane);
-        if (TWO) {
-            floatx4 s1 = red[0][t][TWO ? 1 : 0][lane];
-            for (int ww = 1; ww < NW; ww++) s1 += red[ww][t][TWO ? 1 : 0][lane];
-            epilogue_frag(ep, (nt0 + t) * 16, mc + 16, h1, s1, lane);
-        }
+    // one accumulator fragment (row block t, row half c) per wave
+    constexpr int C = TWO ? 2 : 1;
+    for (int pi = wave; pi < TPB * C; pi += NW) {
+        const int t = pi / C, c = pi % C;
+        floatx4 s0 = red[0][t][c][lane];
+        for (int ww = 1; ww < NW; ww++) s0 += red[ww][t][c][lane];
+        epilogue_frag(ep, (nt0 + t) * 16, mc + 16 * c, c ? h1 : h0, s0, lane);
     }
 }
 
@@ -542,6 +546,26 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
     const half_t *W = (const half_t *)a.W, *X = (const half_t *)a.X, *nw = (const half_t *)a.norm_w;
     if (nw && !skinny_can_normalise(a.M, a.K)) return hipErrorInvalidValue;
     const dim3 blk(512);
+    if (a.x_mh) {
+        // fragment-major activations of a decode step, 2 < M <= 32
+        if (nw || a.M > 16 * a.x_mh || a.x_mh > 2) return hipErrorInvalidValue;
+        const int tiles = a.N / 16;
+        if (a.x_mh == 1)
+            hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, false, false, true>), dim3(tiles), blk, 0, s, W,
+                               X, 0, a.M, a.N, a.K, a.ep, nw, a.eps);
+        else if (tiles >= 640 && tiles < 1024 && tiles % 4 == 0)
+            // tall products: four row blocks per work-group share each activation fragment
+            hipLaunchKernelGGL((gemm_skinny_kernel<8, 2, 4, true, false, false, true>), dim3(tiles / 4), blk, 0, s,
+                               W, X, 0, a.M, a.N, a.K, a.ep, nw, a.eps);
+        else if (tiles >= 320 && tiles % 2 == 0)
+            hipLaunchKernelGGL((gemm_skinny_kernel<8, 4, 2, true, false, false, true>), dim3(tiles / 2), blk, 0, s,
+                               W, X, 0, a.M, a.N, a.K, a.ep, nw, a.eps);
+        else
+            // few row blocks: one per work-group keeps every CU streaming
+            hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, true, false, false, true>), dim3(tiles), blk, 0, s, W,
+                               X, 0, a.M, a.N, a.K, a.ep, nw, a.eps);
+        return hipGetLastError();
+    }
     if (a.M <= 2 && (int64_t)a.M * a.K * 2 <= STAGE_MAX_BYTES) {
         const size_t lds = (size_t)a.M * a.K * 2;
         if (nw)

@@ -149,6 +149,7 @@ char *layer_vc(llm_t *h, int l) { return h->kv + (int64_t)l * h->kv_layer_bytes 
 // Activation workspace for `rows` token rows (grows, never shrinks).
 int ensure_ws(llm_t *h, int64_t rows)
 {
+    rows = rows < 32 ? 32 : rows;  // fragment-major activations span 16 or 32 rows
     if (rows <= h->ws_rows) return LLM_OK;
     const Dims &d = h->d;
     int64_t bx = align256(rows * d.D * d.es), bq = align256(rows * (int64_t)d.H * d.hd * d.es),
@@ -210,12 +211,13 @@ const char *mat_ptr(llm_t *h, int layer, int mat)
 }
 
 hipError_t run_linear(llm_t *h, int layer, int mat, const void *X, int64_t ldx, int M,
-                      const Epilogue &ep, const void *norm_w = nullptr)
+                      const Epilogue &ep, const void *norm_w = nullptr, int x_mh = 0)
 {
     GemmArgs a{};
     a.W = mat_ptr(h, layer, mat);
     a.X = X;
     a.ldx = ldx;
+    a.x_mh = x_mh;
     a.M = M;
     a.N = (int)mat_rows(h->d, mat);
     a.K = (int)mat_cols(h->d, mat);
@@ -229,6 +231,15 @@ hipError_t run_linear(llm_t *h, int layer, int mat, const void *X, int64_t ldx, 
 // normalised in LDS) for one or two fp16 rows, else a normalisation kernel
 // writing xn and the product on xn.
 bool fuse_norm(const llm_t *h, int M) { return h->d.dtype == LLM_F16 && skinny_can_normalise(M, h->d.D); }
+
+// Decode steps of 3..32 fp16 rows pass the normalised rows, the attention
+// output and the SwiGLU output to the products fragment-major (row halves
+// of 16); other shapes use row-major activations.
+int act_mh(const llm_t *h, int B, int T, const int *pos_dev)
+{
+    if (h->d.dtype != LLM_F16 || !pos_dev || T != 1 || B <= 2 || B > 32) return 0;
+    return (B + 15) / 16;
+}
 
 Epilogue make_ep(int kind, void *out, int64_t ldo)
 {
@@ -272,6 +283,50 @@ hipError_t prof_end(Prof *pf, hipStream_t s)
     return hipEventRecord(pf->ev[pf->used++], s);
 }
 
+// One weight product of the forward pass with its epilogue: layer l's
+// wq|wk|wv (RoPE and the KV-cache write), wo and w2 (residual add), w1|w3
+// (SwiGLU), or the output head on the last position of each row (fp32
+// logits).  With `fused` the RMSNorm in front of wq|wk|wv, w1|w3 and the
+// head runs inside the product on x; otherwise the product reads xn.
+hipError_t product(llm_t *h, int l, int mat, int B, int T, const int *pos_dev, bool fused)
+{
+    const Dims &d = h->d;
+    const int M = B * T;
+    const int64_t qd = (int64_t)d.H * d.hd;
+    const int mh = act_mh(h, B, T, pos_dev);
+    switch (mat) {
+    case MAT_QKV: {
+        Epilogue eq = make_ep(EP_QKV, h->q, qd);
+        eq.kcache = layer_kc(h, l);
+        eq.vcache = layer_vc(h, l);
+        eq.rope = h->rope;
+        eq.pos_dev = pos_dev;
+        eq.pos_imm = 0;
+        eq.T = T;
+        eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = d.S;
+        const char *nw = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
+        return fused ? run_linear(h, l, MAT_QKV, h->x, d.D, M, eq, nw)
+                     : run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq, nullptr, mh);
+    }
+    case MAT_O: return run_linear(h, l, MAT_O, h->o, qd, M, make_ep(EP_RESID, h->x, d.D), nullptr, mh);
+    case MAT_W13: {
+        const char *nw = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
+        Epilogue eg = make_ep(EP_SWIGLU, h->g, d.F);
+        eg.out_mh = mh;
+        return fused ? run_linear(h, l, MAT_W13, h->x, d.D, M, eg, nw)
+                     : run_linear(h, l, MAT_W13, h->xn, d.D, M, eg, nullptr, mh);
+    }
+    case MAT_W2: return run_linear(h, l, MAT_W2, h->g, d.F, M, make_ep(EP_RESID, h->x, d.D), nullptr, mh);
+    default: {
+        const char *nw = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
+        const char *xlast = h->x + (int64_t)(T - 1) * d.D * d.es;
+        Epilogue el = make_ep(EP_LOGITS, h->logits, d.V);
+        return fused ? run_linear(h, 0, MAT_HEAD, xlast, (int64_t)T * d.D, B, el, nw)
+                     : run_linear(h, 0, MAT_HEAD, h->xn, d.D, B, el, nullptr, mh);
+    }
+    }
+}
+
 // The forward pass over B rows of T tokens (walkthrough sections 2, 3.5-3.8).
 // Decode (pos_dev != NULL, T == 1) reads its position from device memory so
 // that the launch sequence can be captured once and replayed.
@@ -279,7 +334,6 @@ hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullpt
 {
     const Dims &d = h->d;
     const int M = B * T;
-    const int64_t qd = (int64_t)d.H * d.hd;
     hipStream_t s = h->stream;
     hipError_t e;
 #define TRY_RAW(x)                    \
@@ -294,51 +348,38 @@ hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullpt
         TRY_RAW(prof_end(pf, s));          \
     } while (0)
     TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, B, T, pos_dev, d.D, d.dtype, h->x, s));
+    const bool fused = fuse_norm(h, M);
+    const int mh = act_mh(h, B, T, pos_dev);
     for (int l = 0; l < d.NL; l++) {
         const char *nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
         const char *nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
-        const bool fused = fuse_norm(h, M);
         // attention_norm -> wq|wk|wv with RoPE and the KV-cache write
-        if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s));
-        Epilogue eq = make_ep(EP_QKV, h->q, qd);
-        eq.kcache = layer_kc(h, l);
-        eq.vcache = layer_vc(h, l);
-        eq.rope = h->rope;
-        eq.pos_dev = pos_dev;
-        eq.pos_imm = 0;
-        eq.T = T;
-        eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = d.S;
-        if (fused) TRYC(PC_PROJ, run_linear(h, l, MAT_QKV, h->x, d.D, M, eq, nw_attn));
-        else TRYC(PC_PROJ, run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq));
+        if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, mh));
+        TRYC(PC_PROJ, product(h, l, MAT_QKV, B, T, pos_dev, fused));
         // attention over the cache
         AttnArgs aa{};
-        aa.q = h->q; aa.kcache = eq.kcache; aa.vcache = eq.vcache; aa.out = h->o;
+        aa.q = h->q; aa.kcache = layer_kc(h, l); aa.vcache = layer_vc(h, l); aa.out = h->o;
         aa.B = B; aa.T = T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
         aa.pos_dev = pos_dev; aa.pos_imm = 0;
+        aa.out_mh = mh;
         if (d.dtype == LLM_F32) TRYC(PC_ATTN, launch_attn_f32(aa, s));
         else if (pos_dev) TRYC(PC_ATTN, launch_attn_decode_f16(aa, s));
         else TRYC(PC_ATTN, launch_attn_prefill_f16(aa, s));
         // wo + residual
-        TRYC(PC_PROJ, run_linear(h, l, MAT_O, h->o, qd, M, make_ep(EP_RESID, h->x, d.D)));
+        TRYC(PC_PROJ, product(h, l, MAT_O, B, T, pos_dev, fused));
         // ffn_norm -> w1|w3 with SwiGLU -> w2 + residual
-        if (fused) {
-            TRYC(PC_PROJ, run_linear(h, l, MAT_W13, h->x, d.D, M, make_ep(EP_SWIGLU, h->g, d.F), nw_ffn));
-        } else {
-            TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_ffn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s));
-            TRYC(PC_PROJ, run_linear(h, l, MAT_W13, h->xn, d.D, M, make_ep(EP_SWIGLU, h->g, d.F)));
-        }
-        TRYC(PC_PROJ, run_linear(h, l, MAT_W2, h->g, d.F, M, make_ep(EP_RESID, h->x, d.D)));
+        if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_ffn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, mh));
+        TRYC(PC_PROJ, product(h, l, MAT_W13, B, T, pos_dev, fused));
+        TRYC(PC_PROJ, product(h, l, MAT_W2, B, T, pos_dev, fused));
     }
     // final norm on the last position of each row, output head, fp32 logits
-    const char *nw_final = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
-    const char *xlast = h->x + (int64_t)(T - 1) * d.D * d.es;
-    if (fuse_norm(h, B)) {
-        TRYC(PC_HEAD, run_linear(h, 0, MAT_HEAD, xlast, (int64_t)T * d.D, B, make_ep(EP_LOGITS, h->logits, d.V),
-                                 nw_final));
-    } else {
-        TRYC(PC_NORM, launch_rmsnorm(xlast, (int64_t)T * d.D, nw_final, B, d.D, h->p.norm_eps, d.dtype, h->xn, s));
-        TRYC(PC_HEAD, run_linear(h, 0, MAT_HEAD, h->xn, d.D, B, make_ep(EP_LOGITS, h->logits, d.V)));
+    const bool fused_head = fuse_norm(h, B);
+    if (!fused_head) {
+        const char *nw_final = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
+        const char *xlast = h->x + (int64_t)(T - 1) * d.D * d.es;
+        TRYC(PC_NORM, launch_rmsnorm(xlast, (int64_t)T * d.D, nw_final, B, d.D, h->p.norm_eps, d.dtype, h->xn, s, mh));
     }
+    TRYC(PC_HEAD, product(h, 0, MAT_HEAD, B, T, pos_dev, fused_head));
 #undef TRYC
 #undef TRY_RAW
     return hipSuccess;
@@ -792,6 +833,77 @@ int llm_profile_decode(llm_t *h, int32_t prev_pos, int32_t reps, float *ms_out)
     for (int c = 0; c < PC_N; c++) ms_out[c] = (float)(acc[c] / reps);
     h->last_pos = prev_pos;
     h->logits_valid = true;
+    return LLM_OK;
+}
+
+// Launches of one timing pass of llm_profile_projections: kind 0..4 is that
+// product over every layer (the head once) `reps` times; kind 5 the whole
+// decode sequence of products in forward order `reps` times.
+hipError_t projection_pass(llm_t *h, int kind, int reps, bool fused, int *launches)
+{
+    const int kinds[5] = {MAT_QKV, MAT_O, MAT_W13, MAT_W2, MAT_HEAD};
+    const int B = h->cur_B, NL = h->d.NL;
+    hipError_t e = hipSuccess;
+    *launches = 0;
+    for (int r = 0; r < reps && e == hipSuccess; r++) {
+        if (kind < 5) {
+            const int per_rep = kinds[kind] == MAT_HEAD ? 1 : NL;
+            for (int l = 0; l < per_rep && e == hipSuccess; l++, ++*launches)
+                e = product(h, l, kinds[kind], B, 1, h->pos_dev, fused);
+        } else {
+            for (int l = 0; l < NL && e == hipSuccess; l++)
+                for (int k = 0; k < 4 && e == hipSuccess; k++, ++*launches)
+                    e = product(h, l, kinds[k], B, 1, h->pos_dev, fused);
+            if (e == hipSuccess) e = product(h, 0, MAT_HEAD, B, 1, h->pos_dev, fused);
+            ++*launches;
+        }
+    }
+    return e;
+}
+
+int llm_profile_projections(llm_t *h, int32_t reps, float *us_out)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!us_out || reps < 1) return fail(h, LLM_EINVAL, "bad arguments");
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    if (h->d.dtype != LLM_F16) return fail(h, LLM_EINVAL, "projection timing is for fp16 models");
+    if (!h->prefilled) return fail(h, LLM_ESTATE, "projection timing before prefill");
+    const bool fused = fuse_norm(h, h->cur_B);
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    hipError_t e = hipEventCreate(&ev[0]);
+    if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+    if (e == hipSuccess) e = launch_set_int(h->pos_dev, h->last_pos, h->stream);
+    // each pass is captured once and replayed, as a decode step is, so the
+    // host's launch rate does not pace the short products
+    for (int k = 0; k < 6 && e == hipSuccess; k++) {
+        hipGraph_t graph = nullptr;
+        hipGraphExec_t exec = nullptr;
+        int launches = 0;
+        e = hipStreamBeginCapture(h->stream, hipStreamCaptureModeRelaxed);
+        if (e == hipSuccess) {
+            hipError_t pe = projection_pass(h, k, reps, fused, &launches);
+            e = hipStreamEndCapture(h->stream, &graph);
+            if (pe != hipSuccess) e = pe;
+        }
+        if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        if (e == hipSuccess) e = hipGraphLaunch(exec, h->stream);  // warm-up
+        if (e == hipSuccess) e = hipEventRecord(ev[0], h->stream);
+        if (e == hipSuccess) e = hipGraphLaunch(exec, h->stream);
+        if (e == hipSuccess) e = hipEventRecord(ev[1], h->stream);
+        if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+        us_out[k] = launches ? ms * 1e3f / (float)launches : 0.f;
+        if (exec) (void)hipGraphExecDestroy(exec);
+        if (graph) (void)hipGraphDestroy(graph);
+    }
+    for (hipEvent_t x : ev)
+        if (x) (void)hipEventDestroy(x);
+    // the workspace, logits and the cache entry at last_pos now hold junk
+    h->prefilled = false;
+    h->logits_valid = false;
+    if (e != hipSuccess) return fail(h, LLM_EDEVICE, std::string("profile: ") + hipGetErrorString(e));
     return LLM_OK;
 }
 

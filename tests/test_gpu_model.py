@@ -124,6 +124,24 @@ def test_small_fp16_forced(B, rows, T0):
     h.destroy()
 
 
+@pytest.mark.parametrize("rows", [5, 16, 17, 32])
+def test_wide_batch_decode(B, rows):
+    """Decode batches of 3..32 rows hand fragment-major activations between
+    the RMSNorm, attention, SwiGLU and the products; dims chosen so that the
+    head (768 row blocks), w1|w3 (352) and the rest (< 320) take the four-,
+    two- and one-block-per-work-group products."""
+    kw = small_kw(dim=1024, n_heads=8, n_kv_heads=2, vocab_size=12288, multiple_of=256,
+                  max_batch_size=32, max_seq_len=64)
+    T0, steps = 6, 6
+    toks = synth.tokens(46, rows, T0 + steps, kw["vocab_size"])
+    say("wide batch decode", rows)
+    h = B.llm_create(B.make_params(**kw), 95)
+    got, _ = gpu_forced_logits(h, toks, T0, steps)
+    want = oracle.forward_stream(ocfg(kw), 95, toks, T0 - 1)
+    check_logits(got, want)
+    h.destroy()
+
+
 def test_small_fp16_sampled_and_deterministic(B):
     kw = small_kw()
     T0, steps = 9, 10
@@ -161,3 +179,22 @@ def test_mha_and_gqa_paths(B):
         got, _ = gpu_forced_logits(h, toks, 12, 8)
         check_logits(got, oracle.forward_stream(ocfg(kw), 93, toks, 11))
         h.destroy()
+
+
+def test_profile_hooks(B):
+    """The timing hooks run, report finite positive times, leave the weights
+    alone, and the projection timer demands a fresh prefill afterwards."""
+    kw = small_kw()
+    toks = synth.tokens(45, 2, 16, kw["vocab_size"])
+    h = B.llm_create(B.make_params(**kw), 94)
+    want, _ = gpu_forced_logits(h, toks, 10, 5)
+    prof = h.profile_decode(14, 2)
+    assert all(np.isfinite(v) and v >= 0 for v in prof.values()) and prof["step"] > 0
+    us = h.profile_projections(2)
+    say("  us per launch", us)
+    assert all(np.isfinite(v) and v > 0 for v in us.values())
+    with pytest.raises(B.LlmError):
+        h.decode(15)
+    got, _ = gpu_forced_logits(h, toks, 10, 5)
+    assert np.array_equal(got, want)
+    h.destroy()
