@@ -39,7 +39,7 @@ constexpr int DEC_WAVES = 8;
 
 __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
     const half_t *__restrict__ q, const half_t *__restrict__ kc, const half_t *__restrict__ vc,
-    int H, int Hkv, int S, const int *pos_dev, int pos_imm, half_t *__restrict__ out, int out_mh)
+    int H, int Hkv, int S, const int *pos_dev, int pos_imm, half_t *__restrict__ out, int out_lay)
 {
     constexpr int hd = 128;
     __shared__ floatx4 so[DEC_WAVES / 2][8][64];
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
             half4 hv;
             for (int i = 0; i < 4; i++) hv[i] = (half_t)(acc[dt][i] * inv);
             const int c = 16 * dt + 4 * g;  // 4 consecutive columns inside one 8-column group
-            if (out_mh) *reinterpret_cast<half4 *>(out + xt_offset(b, (int64_t)h * hd + c, out_mh)) = hv;
+            if (out_lay) *reinterpret_cast<half4 *>(out + act_offset(b, (int64_t)h * hd + c, (int64_t)H * hd, 0, out_lay)) = hv;
             else *reinterpret_cast<half4 *>(orow + c) = hv;
         }
     }
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
                                                            const half_t *__restrict__ kc,
                                                            const half_t *__restrict__ vc, int T,
                                                            int H, int Hkv, int S,
-                                                           half_t *__restrict__ out)
+                                                           half_t *__restrict__ out, int out_lay)
 {
     const int hd = 128;
     __shared__ half8 kl[PF_K * hd / 8];  // 4 sub-tiles x 4 d-steps x 64 lanes
@@ -325,7 +325,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
             half4 o;
 #pragma unroll
             for (int i = 0; i < 4; i++) o[i] = (half_t)(acc[c][dt][i] * inv);
-            *reinterpret_cast<half4 *>(orow + 16 * dt + 4 * g) = o;
+            const int col = 16 * dt + 4 * g;  // 4 consecutive columns inside one 8-column group
+            if (out_lay)
+                *reinterpret_cast<half4 *>(out + act_offset(b * T + t, (int64_t)h * hd + col, (int64_t)H * hd, 0, out_lay)) = o;
+            else
+                *reinterpret_cast<half4 *>(orow + col) = o;
         }
     }
 }
@@ -384,18 +388,19 @@ __global__ void kv_write_kernel(const Tv *k, const Tv *v, int T, int pos0, int H
 
 hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s)
 {
-    if (a.out_mh && (a.out_mh > 2 || a.B > 16 * a.out_mh || a.T != 1)) return hipErrorInvalidValue;
+    if (a.out_lay && (a.out_lay > 2 || a.B > 16 * a.out_lay || a.T != 1)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_decode_kernel, dim3(a.B * a.Hkv), dim3(DEC_WAVES * 64), 0, s,
                        (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache, a.H,
-                       a.Hkv, a.S, a.pos_dev, a.pos_imm, (half_t *)a.out, a.out_mh);
+                       a.Hkv, a.S, a.pos_dev, a.pos_imm, (half_t *)a.out, a.out_lay);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s)
 {
+    if (a.out_lay != ACT_ROWS && a.out_lay != ACT_TILED) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.B * a.H, (a.T + PF_Q - 1) / PF_Q), dim3(256), 0,
                        s, (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache,
-                       a.T, a.H, a.Hkv, a.S, (half_t *)a.out);
+                       a.T, a.H, a.Hkv, a.S, (half_t *)a.out, a.out_lay);
     return hipGetLastError();
 }
 

@@ -50,6 +50,21 @@ __host__ __device__ inline int64_t xt_offset(int m, int64_t k, int mh)
     return (((k >> 5) * mh + (m >> 4)) * 64 + (m & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
 }
 
+// Activation layouts handed between kernels (fp16 models):
+//   ACT_ROWS   row-major [M][K] with a row stride;
+//   1, 2       the fragment-major decode layout above with that many row halves;
+//   ACT_TILED  the weight tile layout applied to activation rows,
+//              [ceil(M/16)][K/32][64 lanes][8] (prefill products of >= 1024
+//              rows): a stage of the 256 x 256 product loads each 16-row
+//              block as one contiguous 1 KiB piece.
+enum { ACT_ROWS = 0, ACT_TILED = 3 };
+__host__ __device__ inline int64_t act_offset(int m, int64_t k, int64_t K, int64_t ld, int lay)
+{
+    if (lay == ACT_TILED) return tiled_offset(m, k, K);
+    if (lay) return xt_offset(m, k, lay);
+    return (int64_t)m * ld + k;
+}
+
 // Packed matrices of one layer, in stored row order.
 enum Mat { MAT_QKV = 0, MAT_O = 1, MAT_W13 = 2, MAT_W2 = 3, MAT_HEAD = 4, MAT_EMB = 5 };
 
@@ -75,7 +90,7 @@ struct Epilogue {
     int pos_imm;          // position of token 0 when pos_dev is NULL
     int T;                // tokens per batch row (m = b*T + t)
     int H, Hkv, hd, S;
-    int out_mh;           // EP_SWIGLU: g fragment-major with this many row halves, 0: row-major
+    int out_lay;          // EP_SWIGLU: layout of g (ACT_ROWS with ldo, 1/2 fragment-major, ACT_TILED)
 };
 
 // ---------------------------------------------------------------------------
@@ -85,7 +100,7 @@ struct GemmArgs {
     const void *W;     // packed weights (tiled fp16 / row-major fp32)
     const void *X;     // activations [M][K] (row stride ldx), or fragment-major
     int64_t ldx;
-    int x_mh;          // > 0: X is fragment-major with this many row halves (M <= 32)
+    int x_lay;         // layout of X: ACT_ROWS, 1/2 (fragment-major, M <= 32) or ACT_TILED (M >= 1024)
     int M, N, K;
     Epilogue ep;
     const void *norm_w;  // RMSNorm weight applied to the X rows first (only where
@@ -110,9 +125,9 @@ hipError_t launch_read_weights(const void *src, int dtype, int mat, int64_t N, i
 
 hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int B, int T,
                         const int *pos_dev, int D, int dtype, void *x, hipStream_t s);
-// y_mh > 0 writes y fragment-major (fp16, M <= 32) with that many row halves.
+// y_lay: layout of y (fp16 only for non-row-major layouts).
 hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int D, float eps,
-                          int dtype, void *y, hipStream_t s, int y_mh = 0);
+                          int dtype, void *y, hipStream_t s, int y_lay = ACT_ROWS);
 
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s);
 hipError_t launch_linear_f32(const GemmArgs &a, hipStream_t s);
@@ -125,7 +140,7 @@ struct AttnArgs {
     int B, T, H, Hkv, hd, S;
     const int *pos_dev;    // decode: device position, else NULL
     int pos_imm;
-    int out_mh;            // decode: > 0 writes out fragment-major ([B][H*hd] rows)
+    int out_lay;           // layout of out as [B*T][H*hd] rows (fp16)
 };
 hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s);

@@ -99,7 +99,7 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
             float s = r16(a / (1.0f + expf(-a)));
             o[i] = (half_t)(s * r16(bv[i]));
         }
-        half_t *gp = (half_t *)ep.out + (ep.out_mh ? xt_offset(m, f0, ep.out_mh) : (int64_t)m * ep.ldo + f0);
+        half_t *gp = (half_t *)ep.out + act_offset(m, f0, ep.ldo, ep.ldo, ep.out_lay);
         *reinterpret_cast<half4 *>(gp) = o;
         break;
     }
@@ -372,6 +372,24 @@ __device__ __forceinline__ void wait_vm_in_flight(bool keep)
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// One 16-byte global -> LDS copy per lane (LDS address m0 + 16 * lane).  It
+// is issued from inline assembly: with the compiler's own LDS-DMA builtin in
+// the loop, its wait-count model stops trusting the in-order completion of
+// LDS reads and waits for all of them before the first MFMA of a step.  The
+// kernel tracks these copies itself with explicit vmcnt waits; m0 is used by
+// nothing else in the kernel.
+__device__ __forceinline__ void lds_copy16(const void *gsrc, const void *ldst)
+{
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(l) : "memory", "m0");
+}
+
+// Prefill product for M >= 1024: 256 x 256 output tile per work-group, four
+// waves of 128 x 128.  W tiles and X rows stream into a four-stage LDS ring
+// by direct global -> LDS copies; each stage is one 32-wide K slice.  XT: X
+// is stored in the weight tile layout (ACT_TILED), so its copies are as
+// contiguous as the weights'; otherwise X is row-major with stride ldx.
+template <bool XT>
 __global__ __launch_bounds__(256, 1) void gemm_tile256_kernel(const half_t *__restrict__ W,
                                                               const half_t *__restrict__ X, int64_t ldx,
                                                               int M, int N, int K, Epilogue ep)
@@ -395,7 +413,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile256_kernel(const half_t *__re
     const int mb = first_mb + (pid % group) % gm;
     const int nb = (pid % group) / gm;
 
-    const int KT = K >> 5, NT = N >> 4;
+    const int KT = K >> 5, NT = N >> 4, MT = (M + 15) >> 4;
     const half8 *Wv = reinterpret_cast<const half8 *>(W);
     const half8 *wsrc[4];
     const half_t *xsrc[4];
@@ -403,9 +421,22 @@ __global__ __launch_bounds__(256, 1) void gemm_tile256_kernel(const half_t *__re
     for (int q = 0; q < 4; q++) {
         const int tile = wave * 4 + q;
         wsrc[q] = Wv + (int64_t)min(nb * 16 + tile, NT - 1) * KT * 64 + lane;
-        const int m = min(mb * 256 + tile * 16 + (lane & 15), M - 1);
-        xsrc[q] = X + (int64_t)m * ldx + 8 * (lane >> 4);
+        if (XT) {
+            xsrc[q] = X + ((int64_t)min(mb * 16 + tile, MT - 1) * KT * 64 + lane) * 8;
+        } else {
+            const int m = min(mb * 256 + tile * 16 + (lane & 15), M - 1);
+            xsrc[q] = X + (int64_t)m * ldx + 8 * (lane >> 4);
+        }
     }
+    auto issue = [&](int st) {
+        const int buf = st % T256_NS;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int tile = wave * 4 + q;
+            lds_copy16(wsrc[q] + (int64_t)st * 64, lw + buf * 1024 + tile * 64);
+            lds_copy16(xsrc[q] + (XT ? (int64_t)st * 512 : (int64_t)st * 32), lx + buf * 1024 + tile * 64);
+        }
+    };
     floatx4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; i++)
@@ -413,35 +444,18 @@ __global__ __launch_bounds__(256, 1) void gemm_tile256_kernel(const half_t *__re
         for (int j = 0; j < 8; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-    for (int st = 0; st < T256_NS - 1; st++) {
-        if (st < KT) {
-            const int buf = st % T256_NS;
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int tile = wave * 4 + q;
-                __builtin_amdgcn_global_load_lds((const void *)(wsrc[q] + (int64_t)st * 64),
-                                                 (void *)(lw + buf * 1024 + tile * 64), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(xsrc[q] + st * 32),
-                                                 (void *)(lx + buf * 1024 + tile * 64), 16, 0, 0);
-            }
-        }
-    }
+    for (int st = 0; st < T256_NS - 1; st++)
+        if (st < KT) issue(st);
+    // Retire the scalar loads of the epilogue arguments here (lgkmcnt(0),
+    // vmcnt and expcnt untouched): with one still pending, the compiler cannot
+    // count LDS reads in order inside the loop and waits for all of them.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     for (int kt = 0; kt < KT; kt++) {
-        // stage kt landed (own loads), then visible to every wave
+        // stage kt landed (own copies), then visible to every wave
         wait_vm_in_flight(kt + T256_NS - 2 < KT);
         __builtin_amdgcn_s_barrier();
         const int nk = kt + T256_NS - 1;  // refill the slot read in step kt-1
-        if (nk < KT) {
-            const int buf = nk % T256_NS;
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int tile = wave * 4 + q;
-                __builtin_amdgcn_global_load_lds((const void *)(wsrc[q] + (int64_t)nk * 64),
-                                                 (void *)(lw + buf * 1024 + tile * 64), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(xsrc[q] + nk * 32),
-                                                 (void *)(lx + buf * 1024 + tile * 64), 16, 0, 0);
-            }
-        }
+        if (nk < KT) issue(nk);
         const int cur = kt % T256_NS;
         half8 a[8], b[8];
 #pragma unroll
@@ -449,13 +463,27 @@ __global__ __launch_bounds__(256, 1) void gemm_tile256_kernel(const half_t *__re
 #pragma unroll
         for (int j = 0; j < 8; j++) b[j] = lx[cur * 1024 + (wm * 8 + j) * 64 + lane];
         __builtin_amdgcn_sched_barrier(0);
+        // column group j starts as soon as its fragment (and the eight of W) is in
 #pragma unroll
-        for (int j = 0; j < 8; j++)
+        for (int j = 0; j < 8; j++) {
+            switch (j) {
+            case 0: asm volatile("s_waitcnt lgkmcnt(7)" ::: "memory"); break;
+            case 1: asm volatile("s_waitcnt lgkmcnt(6)" ::: "memory"); break;
+            case 2: asm volatile("s_waitcnt lgkmcnt(5)" ::: "memory"); break;
+            case 3: asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory"); break;
+            case 4: asm volatile("s_waitcnt lgkmcnt(3)" ::: "memory"); break;
+            case 5: asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory"); break;
+            case 6: asm volatile("s_waitcnt lgkmcnt(1)" ::: "memory"); break;
+            default: asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); break;
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 8; i++) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
-        // this wave's reads of slot `cur` are complete before anyone refills it
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    // no copy may still be writing LDS when the work-group ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         const int n0 = (nb * 16 + wn * 8 + i) * 16;
@@ -546,11 +574,11 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
     const half_t *W = (const half_t *)a.W, *X = (const half_t *)a.X, *nw = (const half_t *)a.norm_w;
     if (nw && !skinny_can_normalise(a.M, a.K)) return hipErrorInvalidValue;
     const dim3 blk(512);
-    if (a.x_mh) {
+    if (a.x_lay == 1 || a.x_lay == 2) {
         // fragment-major activations of a decode step, 2 < M <= 32
-        if (nw || a.M > 16 * a.x_mh || a.x_mh > 2) return hipErrorInvalidValue;
+        if (nw || a.M > 16 * a.x_lay || a.x_lay > 2) return hipErrorInvalidValue;
         const int tiles = a.N / 16;
-        if (a.x_mh == 1)
+        if (a.x_lay == 1)
             hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, false, false, true>), dim3(tiles), blk, 0, s, W,
                                X, 0, a.M, a.N, a.K, a.ep, nw, a.eps);
         else if (tiles >= 640 && tiles < 1024 && tiles % 4 == 0)
@@ -566,6 +594,14 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
                                X, 0, a.M, a.N, a.K, a.ep, nw, a.eps);
         return hipGetLastError();
     }
+    if (a.x_lay == ACT_TILED) {
+        if (nw || a.M < 1024) return hipErrorInvalidValue;
+        int NB = (a.N + 255) / 256, MB = (a.M + 255) / 256;
+        hipLaunchKernelGGL(gemm_tile256_kernel<true>, dim3(NB * MB), dim3(256), T256_LDS, s, W, X, 0, a.M, a.N,
+                           a.K, a.ep);
+        return hipGetLastError();
+    }
+    if (a.x_lay != ACT_ROWS) return hipErrorInvalidValue;
     if (a.M <= 2 && (int64_t)a.M * a.K * 2 <= STAGE_MAX_BYTES) {
         const size_t lds = (size_t)a.M * a.K * 2;
         if (nw)
@@ -590,8 +626,8 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
         hipLaunchKernelGGL(gemm_big_kernel, dim3(NB * MB), dim3(256), 0, s, W, X, a.ldx, a.M, a.N, a.K, a.ep);
     } else {
         int NB = (a.N + 255) / 256, MB = (a.M + 255) / 256;
-        hipLaunchKernelGGL(gemm_tile256_kernel, dim3(NB * MB), dim3(256), T256_LDS, s, W, X, a.ldx, a.M, a.N,
-                           a.K, a.ep);
+        hipLaunchKernelGGL(gemm_tile256_kernel<false>, dim3(NB * MB), dim3(256), T256_LDS, s, W, X, a.ldx, a.M,
+                           a.N, a.K, a.ep);
     }
     return hipGetLastError();
 }

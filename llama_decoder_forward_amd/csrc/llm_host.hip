@@ -149,7 +149,7 @@ char *layer_vc(llm_t *h, int l) { return h->kv + (int64_t)l * h->kv_layer_bytes 
 // Activation workspace for `rows` token rows (grows, never shrinks).
 int ensure_ws(llm_t *h, int64_t rows)
 {
-    rows = rows < 32 ? 32 : rows;  // fragment-major activations span 16 or 32 rows
+    rows = rows < 32 ? 32 : (rows + 15) / 16 * 16;  // laid-out activations span whole 16-row blocks
     if (rows <= h->ws_rows) return LLM_OK;
     const Dims &d = h->d;
     int64_t bx = align256(rows * d.D * d.es), bq = align256(rows * (int64_t)d.H * d.hd * d.es),
@@ -211,13 +211,13 @@ const char *mat_ptr(llm_t *h, int layer, int mat)
 }
 
 hipError_t run_linear(llm_t *h, int layer, int mat, const void *X, int64_t ldx, int M,
-                      const Epilogue &ep, const void *norm_w = nullptr, int x_mh = 0)
+                      const Epilogue &ep, const void *norm_w = nullptr, int x_lay = ACT_ROWS)
 {
     GemmArgs a{};
     a.W = mat_ptr(h, layer, mat);
     a.X = X;
     a.ldx = ldx;
-    a.x_mh = x_mh;
+    a.x_lay = x_lay;
     a.M = M;
     a.N = (int)mat_rows(h->d, mat);
     a.K = (int)mat_cols(h->d, mat);
@@ -232,14 +232,22 @@ hipError_t run_linear(llm_t *h, int layer, int mat, const void *X, int64_t ldx, 
 // writing xn and the product on xn.
 bool fuse_norm(const llm_t *h, int M) { return h->d.dtype == LLM_F16 && skinny_can_normalise(M, h->d.D); }
 
-// Decode steps of 3..32 fp16 rows pass the normalised rows, the attention
-// output and the SwiGLU output to the products fragment-major (row halves
-// of 16); other shapes use row-major activations.
-int act_mh(const llm_t *h, int B, int T, const int *pos_dev)
+// Layout of the activations a forward pass hands to its layer products
+// (normalised rows, attention output, SwiGLU output): decode steps of 3..32
+// fp16 rows use the fragment-major layout (row halves of 16), fp16 prefills
+// of >= 1024 rows the weight tile layout; everything else is row-major.
+// Row-major always for the output head, whose M is the batch.
+constexpr int kTiledMinRows = 1024;  // the 256 x 256 product takes M >= 1024
+
+int act_layout(const llm_t *h, int B, int T, const int *pos_dev)
 {
-    if (h->d.dtype != LLM_F16 || !pos_dev || T != 1 || B <= 2 || B > 32) return 0;
-    return (B + 15) / 16;
+    if (h->d.dtype != LLM_F16) return ACT_ROWS;
+    if (pos_dev && T == 1) return B > 2 && B <= 32 ? (B + 15) / 16 : ACT_ROWS;
+    if (!pos_dev && (int64_t)B * T >= kTiledMinRows) return ACT_TILED;
+    return ACT_ROWS;
 }
+
+int head_layout(int lay) { return lay == ACT_TILED ? ACT_ROWS : lay; }
 
 Epilogue make_ep(int kind, void *out, int64_t ldo)
 {
@@ -293,7 +301,7 @@ hipError_t product(llm_t *h, int l, int mat, int B, int T, const int *pos_dev, b
     const Dims &d = h->d;
     const int M = B * T;
     const int64_t qd = (int64_t)d.H * d.hd;
-    const int mh = act_mh(h, B, T, pos_dev);
+    const int lay = act_layout(h, B, T, pos_dev);
     switch (mat) {
     case MAT_QKV: {
         Epilogue eq = make_ep(EP_QKV, h->q, qd);
@@ -306,23 +314,23 @@ hipError_t product(llm_t *h, int l, int mat, int B, int T, const int *pos_dev, b
         eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = d.S;
         const char *nw = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
         return fused ? run_linear(h, l, MAT_QKV, h->x, d.D, M, eq, nw)
-                     : run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq, nullptr, mh);
+                     : run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq, nullptr, lay);
     }
-    case MAT_O: return run_linear(h, l, MAT_O, h->o, qd, M, make_ep(EP_RESID, h->x, d.D), nullptr, mh);
+    case MAT_O: return run_linear(h, l, MAT_O, h->o, qd, M, make_ep(EP_RESID, h->x, d.D), nullptr, lay);
     case MAT_W13: {
         const char *nw = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
         Epilogue eg = make_ep(EP_SWIGLU, h->g, d.F);
-        eg.out_mh = mh;
+        eg.out_lay = lay;
         return fused ? run_linear(h, l, MAT_W13, h->x, d.D, M, eg, nw)
-                     : run_linear(h, l, MAT_W13, h->xn, d.D, M, eg, nullptr, mh);
+                     : run_linear(h, l, MAT_W13, h->xn, d.D, M, eg, nullptr, lay);
     }
-    case MAT_W2: return run_linear(h, l, MAT_W2, h->g, d.F, M, make_ep(EP_RESID, h->x, d.D), nullptr, mh);
+    case MAT_W2: return run_linear(h, l, MAT_W2, h->g, d.F, M, make_ep(EP_RESID, h->x, d.D), nullptr, lay);
     default: {
         const char *nw = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
         const char *xlast = h->x + (int64_t)(T - 1) * d.D * d.es;
         Epilogue el = make_ep(EP_LOGITS, h->logits, d.V);
         return fused ? run_linear(h, 0, MAT_HEAD, xlast, (int64_t)T * d.D, B, el, nw)
-                     : run_linear(h, 0, MAT_HEAD, h->xn, d.D, B, el, nullptr, mh);
+                     : run_linear(h, 0, MAT_HEAD, h->xn, d.D, B, el, nullptr, head_layout(lay));
     }
     }
 }
@@ -349,26 +357,26 @@ hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullpt
     } while (0)
     TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, B, T, pos_dev, d.D, d.dtype, h->x, s));
     const bool fused = fuse_norm(h, M);
-    const int mh = act_mh(h, B, T, pos_dev);
+    const int lay = act_layout(h, B, T, pos_dev);
     for (int l = 0; l < d.NL; l++) {
         const char *nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
         const char *nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
         // attention_norm -> wq|wk|wv with RoPE and the KV-cache write
-        if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, mh));
+        if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay));
         TRYC(PC_PROJ, product(h, l, MAT_QKV, B, T, pos_dev, fused));
         // attention over the cache
         AttnArgs aa{};
         aa.q = h->q; aa.kcache = layer_kc(h, l); aa.vcache = layer_vc(h, l); aa.out = h->o;
         aa.B = B; aa.T = T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
         aa.pos_dev = pos_dev; aa.pos_imm = 0;
-        aa.out_mh = mh;
+        aa.out_lay = lay;
         if (d.dtype == LLM_F32) TRYC(PC_ATTN, launch_attn_f32(aa, s));
         else if (pos_dev) TRYC(PC_ATTN, launch_attn_decode_f16(aa, s));
         else TRYC(PC_ATTN, launch_attn_prefill_f16(aa, s));
         // wo + residual
         TRYC(PC_PROJ, product(h, l, MAT_O, B, T, pos_dev, fused));
         // ffn_norm -> w1|w3 with SwiGLU -> w2 + residual
-        if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_ffn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, mh));
+        if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_ffn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay));
         TRYC(PC_PROJ, product(h, l, MAT_W13, B, T, pos_dev, fused));
         TRYC(PC_PROJ, product(h, l, MAT_W2, B, T, pos_dev, fused));
     }
@@ -377,7 +385,7 @@ hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullpt
     if (!fused_head) {
         const char *nw_final = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
         const char *xlast = h->x + (int64_t)(T - 1) * d.D * d.es;
-        TRYC(PC_NORM, launch_rmsnorm(xlast, (int64_t)T * d.D, nw_final, B, d.D, h->p.norm_eps, d.dtype, h->xn, s, mh));
+        TRYC(PC_NORM, launch_rmsnorm(xlast, (int64_t)T * d.D, nw_final, B, d.D, h->p.norm_eps, d.dtype, h->xn, s, head_layout(lay)));
     }
     TRYC(PC_HEAD, product(h, 0, MAT_HEAD, B, T, pos_dev, fused_head));
 #undef TRYC

@@ -38,7 +38,7 @@ __device__ __forceinline__ float block_sum(float v, float *red)
 constexpr int RMS_VEC = 16;  // D up to 8192
 
 __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64_t ldx, const half_t *w,
-                                                          int M, int D, float eps, half_t *y, int y_mh)
+                                                          int M, int D, float eps, half_t *y, int y_lay)
 {
 #pragma clang fp contract(off)
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64
                 half_t n = (half_t)((float)v[j][e] * r);
                 o[e] = (half_t)((float)n * (float)wv[e]);
             }
-            if (y_mh) *reinterpret_cast<half8 *>(y + xt_offset(row, 8 * (int64_t)i, y_mh)) = o;
+            if (y_lay) *reinterpret_cast<half8 *>(y + act_offset(row, 8 * (int64_t)i, D, D, y_lay)) = o;
             else yr[i] = o;
         }
     }
@@ -102,13 +102,14 @@ hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int B
 }
 
 hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int D, float eps,
-                          int dtype, void *y, hipStream_t s, int y_mh)
+                          int dtype, void *y, hipStream_t s, int y_lay)
 {
     if (M <= 0) return hipSuccess;
-    if (y_mh && (dtype != 1 || M > 16 * y_mh || y_mh > 2 || D % 32)) return hipErrorInvalidValue;
+    if (y_lay && (dtype != 1 || D % 32)) return hipErrorInvalidValue;
+    if ((y_lay == 1 || y_lay == 2) && M > 16 * y_lay) return hipErrorInvalidValue;
     if (dtype == 1)
         hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((M + 3) / 4), dim3(256), 0, s, (const half_t *)x, ldx,
-                           (const half_t *)w, M, D, eps, (half_t *)y, y_mh);
+                           (const half_t *)w, M, D, eps, (half_t *)y, y_lay);
     else
         hipLaunchKernelGGL(rmsnorm_f32_kernel, dim3(M), dim3(kThreads), 0, s, (const float *)x, ldx,
                            (const float *)w, D, eps, (float *)y);

@@ -142,6 +142,22 @@ def test_wide_batch_decode(B, rows):
     h.destroy()
 
 
+@pytest.mark.parametrize("rows,T0", [(1, 1040), (2, 600)])
+def test_long_prefill_tiled(B, rows, T0):
+    """Prefills of >= 1024 rows hand activations to the 256 x 256 products in
+    the weight tile layout; 1040 and 1200 rows leave ragged 256-row and
+    16-row tails."""
+    kw = small_kw(max_seq_len=1088, max_batch_size=2)
+    steps = 3
+    toks = synth.tokens(47, rows, T0 + steps, kw["vocab_size"])
+    say("long prefill", rows, T0)
+    h = B.llm_create(B.make_params(**kw), 96)
+    got, _ = gpu_forced_logits(h, toks, T0, steps)
+    want = oracle.forward_stream(ocfg(kw), 96, toks, T0 - 1)
+    check_logits(got, want)
+    h.destroy()
+
+
 def test_small_fp16_sampled_and_deterministic(B):
     kw = small_kw()
     T0, steps = 9, 10
