@@ -53,6 +53,15 @@ def product_bytes(w, B):
     }
 
 
+def prefill_product_flops(w, M):
+    """Flops of the layer weight products of a prefill of M rows, by kind
+    (all layers; the head runs on the last position only and is left out)."""
+    D, hd, F = w.dim, w.head_dim, w.ffn_hidden()
+    qd, kvd = w.n_heads * hd, w.n_kv_heads * hd
+    per = {"qkv": (qd + 2 * kvd) * D, "o": D * qd, "w13": 2 * F * D, "w2": D * F}
+    return {k: 2 * v * M * w.n_layers for k, v in per.items()}
+
+
 def prefill_flops(w, B, T):
     """2 * params * tokens for the layer matrices, causal attention
     2 * B * H * d * T (T + 1) per layer, head at the last position."""
@@ -209,6 +218,12 @@ def main():
     # captured graph between two HIP events on the library's stream (and
     # each kind on its own for the breakdown)
     prod_us = h.profile_projections(args.profile_reps)
+    # prefill kernels by class (eager, HIP events around every kernel); the
+    # weight products' share of the prefill flops against the MFMA peak
+    pf_prof = h.profile_prefill_d(tok_dev.data_ptr(), B, T0, 1)
+    pf_gemm = prefill_product_flops(w, B * T0)
+    pf_gemm_ms = sum(pf_prof[k] for k in pf_gemm)
+    pf_gemm_tflops = sum(pf_gemm.values()) / (pf_gemm_ms / 1e3) / 1e12
     pbytes = product_bytes(w, B)
     per_step = {k: (1 if k == "head" else w.n_layers) for k in pbytes}
     launches = sum(per_step.values())
@@ -259,6 +274,11 @@ def main():
             "decode_roofline_tok_s": round(step_roof_tok_s, 1),
             "decode_frac_of_roofline": round(decode_tok_s / step_roof_tok_s, 4),
             "profile_ms_per_decode_step": {k: round(v, 4) for k, v in prof.items()},
+            "profile_ms_per_prefill": {k: round(v, 3) for k, v in pf_prof.items()},
+            "prefill_products_tflops": round(pf_gemm_tflops, 1),
+            "prefill_products_frac_of_mfma": round(pf_gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "prefill_products_tflops_by_kind": {k: round(pf_gemm[k] / (pf_prof[k] / 1e3) / 1e12, 1)
+                                                for k in pf_gemm},
             "create_s": round(t_create, 2),
         },
     }

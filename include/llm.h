@@ -207,11 +207,17 @@ int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_
 
 /* Run `reps` decode steps at prev_pos without the captured graph, with HIP
  * events on the handle's stream around every kernel, and write the mean
- * milliseconds per step of each kernel class to ms_out[6]: 0 embedding,
- * 1 RMSNorm, 2 layer projections (QKV, O, W1/W3, W2 with their epilogues),
- * 3 attention, 4 output head, 5 first-to-last event.  Same preconditions
- * and effects as llm_decode; synchronises. */
+ * milliseconds per step of each kernel class to ms_out[9]: 0 embedding,
+ * 1 RMSNorm, 2 wq|wk|wv product (with RoPE and the KV write), 3 attention,
+ * 4 wo product, 5 w1|w3 product (with SwiGLU), 6 w2 product, 7 output head,
+ * 8 first-to-last event.  Same preconditions and effects as llm_decode;
+ * synchronises. */
 int llm_profile_decode(llm_t *h, int32_t prev_pos, int32_t reps, float *ms_out);
+
+/* As llm_prefill_d run `reps` times, with the same per-class event timing
+ * as llm_profile_decode (ms_out[9], mean per prefill).  Same arguments,
+ * preconditions and effects as llm_prefill_d; synchronises. */
+int llm_profile_prefill(llm_t *h, const int32_t *tokens_d, int32_t B, int32_t T, int32_t reps, float *ms_out);
 
 /* Time the decode step's weight products on their own, at the current
  * batch and in the launch configuration, epilogue and RMSNorm fusion of a

@@ -59,6 +59,7 @@ EXPORTS = {
     "llm_set_tokens": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
     "llm_set_tokens_d": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
     "llm_profile_decode": (C.c_int, [_vp, C.c_int32, C.c_int32, _vp]),
+    "llm_profile_prefill": (C.c_int, [_vp, _vp, C.c_int32, C.c_int32, C.c_int32, _vp]),
     "llm_profile_projections": (C.c_int, [_vp, C.c_int32, _vp]),
     "llm_get_logits": (C.c_int, [_vp, _vp]),
     "llm_get_logits_d": (C.c_int, [_vp, _vp]),
@@ -170,11 +171,18 @@ class Handle:
     def set_tokens_d(self, pos: int, tokens_ptr: int, mask_ptr: int = 0):
         self._ck(_lib.llm_set_tokens_d(self.ptr, pos, C.c_void_p(tokens_ptr), C.c_void_p(mask_ptr or None)))
 
-    PROFILE_CLASSES = ("embed", "rmsnorm", "projections", "attention", "head", "step")
+    PROFILE_CLASSES = ("embed", "rmsnorm", "qkv", "attention", "o", "w13", "w2", "head", "step")
 
     def profile_decode(self, prev_pos: int, reps: int) -> dict:
-        out = np.zeros(6, np.float32)
+        out = np.zeros(len(self.PROFILE_CLASSES), np.float32)
         self._ck(_lib.llm_profile_decode(self.ptr, prev_pos, reps, out.ctypes.data_as(C.c_void_p)))
+        return dict(zip(self.PROFILE_CLASSES, out.tolist()))
+
+    def profile_prefill_d(self, tokens_ptr: int, B: int, T: int, reps: int) -> dict:
+        out = np.zeros(len(self.PROFILE_CLASSES), np.float32)
+        self._ck(_lib.llm_profile_prefill(self.ptr, C.c_void_p(tokens_ptr), B, T, reps,
+                                          out.ctypes.data_as(C.c_void_p)))
+        self.B = B
         return dict(zip(self.PROFILE_CLASSES, out.tolist()))
 
     PRODUCT_KINDS = ("qkv", "o", "w13", "w2", "head", "step_order")

@@ -27,13 +27,16 @@ __device__ __forceinline__ float r16(float x) { return (float)(half_t)x; }
 // must call this together (EP_SWIGLU exchanges values between lanes);
 // `valid` masks the stores of lanes whose column is past M or whose rows are
 // past N.
+// KIND >= 0 fixes the epilogue kind at compile time (large kernels that
+// apply it to many fragments keep only that kind's code).
+template <int KIND = -1>
 __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m, bool valid,
                                               floatx4 acc, int lane)
 {
 #pragma clang fp contract(off)
     const int g = lane >> 4;
     const int n = n0 + 4 * g;
-    switch (ep.kind) {
+    switch (KIND >= 0 ? KIND : ep.kind) {
     case EP_STORE: {
         if (!valid) break;
         half4 o;
@@ -389,7 +392,7 @@ __device__ __forceinline__ void lds_copy16(const void *gsrc, const void *ldst)
 // by direct global -> LDS copies; each stage is one 32-wide K slice.  XT: X
 // is stored in the weight tile layout (ACT_TILED), so its copies are as
 // contiguous as the weights'; otherwise X is row-major with stride ldx.
-template <bool XT>
+template <bool XT, int KIND>
 __global__ __launch_bounds__(256, 1) void gemm_tile256_kernel(const half_t *__restrict__ W,
                                                               const half_t *__restrict__ X, int64_t ldx,
                                                               int M, int N, int K, Epilogue ep)
@@ -490,9 +493,37 @@ __global__ __launch_bounds__(256, 1) void gemm_tile256_kernel(const half_t *__re
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const int m = (mb * 16 + wm * 8 + j) * 16 + (lane & 15);
-            epilogue_frag(ep, n0, m, m < M && n0 < N, acc[i][j], lane);
+            epilogue_frag<KIND>(ep, n0, m, m < M && n0 < N, acc[i][j], lane);
         }
     }
+}
+
+template <bool XT>
+hipError_t launch_tile256(const GemmArgs &a, hipStream_t s)
+{
+    const int NB = (a.N + 255) / 256, MB = (a.M + 255) / 256;
+    const dim3 grid(NB * MB), blk(256);
+    const half_t *W = (const half_t *)a.W, *X = (const half_t *)a.X;
+    const int64_t ldx = XT ? 0 : a.ldx;
+    switch (a.ep.kind) {
+    case EP_STORE:
+        hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_STORE>), grid, blk, T256_LDS, s, W, X, ldx, a.M, a.N, a.K, a.ep);
+        break;
+    case EP_RESID:
+        hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_RESID>), grid, blk, T256_LDS, s, W, X, ldx, a.M, a.N, a.K, a.ep);
+        break;
+    case EP_LOGITS:
+        hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_LOGITS>), grid, blk, T256_LDS, s, W, X, ldx, a.M, a.N, a.K, a.ep);
+        break;
+    case EP_QKV:
+        hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_QKV>), grid, blk, T256_LDS, s, W, X, ldx, a.M, a.N, a.K, a.ep);
+        break;
+    case EP_SWIGLU:
+        hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_SWIGLU>), grid, blk, T256_LDS, s, W, X, ldx, a.M, a.N, a.K, a.ep);
+        break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -596,10 +627,7 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
     }
     if (a.x_lay == ACT_TILED) {
         if (nw || a.M < 1024) return hipErrorInvalidValue;
-        int NB = (a.N + 255) / 256, MB = (a.M + 255) / 256;
-        hipLaunchKernelGGL(gemm_tile256_kernel<true>, dim3(NB * MB), dim3(256), T256_LDS, s, W, X, 0, a.M, a.N,
-                           a.K, a.ep);
-        return hipGetLastError();
+        return launch_tile256<true>(a, s);
     }
     if (a.x_lay != ACT_ROWS) return hipErrorInvalidValue;
     if (a.M <= 2 && (int64_t)a.M * a.K * 2 <= STAGE_MAX_BYTES) {
@@ -625,9 +653,7 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
         int NB = (a.N + BIG_BN - 1) / BIG_BN, MB = (a.M + BIG_BM - 1) / BIG_BM;
         hipLaunchKernelGGL(gemm_big_kernel, dim3(NB * MB), dim3(256), 0, s, W, X, a.ldx, a.M, a.N, a.K, a.ep);
     } else {
-        int NB = (a.N + 255) / 256, MB = (a.M + 255) / 256;
-        hipLaunchKernelGGL(gemm_tile256_kernel<false>, dim3(NB * MB), dim3(256), T256_LDS, s, W, X, a.ldx, a.M,
-                           a.N, a.K, a.ep);
+        return launch_tile256<false>(a, s);
     }
     return hipGetLastError();
 }

@@ -267,7 +267,10 @@ struct Prof {
     size_t used = 0;
 };
 
-enum ProfClass { PC_EMBED = 0, PC_NORM = 1, PC_PROJ = 2, PC_ATTN = 3, PC_HEAD = 4, PC_N = 6 };
+enum ProfClass {
+    PC_EMBED = 0, PC_NORM = 1, PC_QKV = 2, PC_ATTN = 3, PC_O = 4, PC_W13 = 5, PC_W2 = 6, PC_HEAD = 7,
+    PC_N = 9  // the last slot holds the first-to-last event time
+};
 
 hipError_t prof_mark(Prof *pf, int cls, hipStream_t s)
 {
@@ -363,7 +366,7 @@ hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullpt
         const char *nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
         // attention_norm -> wq|wk|wv with RoPE and the KV-cache write
         if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay));
-        TRYC(PC_PROJ, product(h, l, MAT_QKV, B, T, pos_dev, fused));
+        TRYC(PC_QKV, product(h, l, MAT_QKV, B, T, pos_dev, fused));
         // attention over the cache
         AttnArgs aa{};
         aa.q = h->q; aa.kcache = layer_kc(h, l); aa.vcache = layer_vc(h, l); aa.out = h->o;
@@ -374,11 +377,11 @@ hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullpt
         else if (pos_dev) TRYC(PC_ATTN, launch_attn_decode_f16(aa, s));
         else TRYC(PC_ATTN, launch_attn_prefill_f16(aa, s));
         // wo + residual
-        TRYC(PC_PROJ, product(h, l, MAT_O, B, T, pos_dev, fused));
+        TRYC(PC_O, product(h, l, MAT_O, B, T, pos_dev, fused));
         // ffn_norm -> w1|w3 with SwiGLU -> w2 + residual
         if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_ffn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay));
-        TRYC(PC_PROJ, product(h, l, MAT_W13, B, T, pos_dev, fused));
-        TRYC(PC_PROJ, product(h, l, MAT_W2, B, T, pos_dev, fused));
+        TRYC(PC_W13, product(h, l, MAT_W13, B, T, pos_dev, fused));
+        TRYC(PC_W2, product(h, l, MAT_W2, B, T, pos_dev, fused));
     }
     // final norm on the last position of each row, output head, fp32 logits
     const bool fused_head = fuse_norm(h, B);
@@ -580,6 +583,39 @@ int sample_common(llm_t *h, float temperature, float top_p, const float *uniform
 // ===========================================================================
 // C ABI
 // ===========================================================================
+// `reps` eager forward passes with HIP events around every kernel; ms_out
+// receives the mean milliseconds per pass of each kernel class (ProfClass)
+// and, last, the first-to-last event time.  prev_pos < 0: a prefill of B x T
+// tokens at positions 0..T-1, else a decode step at prev_pos.
+int profiled_forward(llm_t *h, int B, int T, int prev_pos, int reps, float *ms_out)
+{
+    Prof pf;
+    double acc[PC_N] = {0};
+    hipError_t e = hipSuccess;
+    for (int r = 0; r < reps && e == hipSuccess; r++) {
+        pf.used = 0;
+        const int *pos = nullptr;
+        if (prev_pos >= 0) {
+            e = launch_set_int(h->pos_dev, prev_pos, h->stream);
+            pos = h->pos_dev;
+        }
+        if (e == hipSuccess) e = forward(h, B, T, pos, &pf);
+        if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+        for (size_t i = 0; e == hipSuccess && i + 1 < pf.used; i += 2) {
+            float ms = 0.f;
+            e = hipEventElapsedTime(&ms, pf.ev[i], pf.ev[i + 1]);
+            acc[pf.cls[i / 2]] += ms;
+        }
+        float all = 0.f;
+        if (e == hipSuccess && pf.used >= 2) e = hipEventElapsedTime(&all, pf.ev[0], pf.ev[pf.used - 1]);
+        acc[PC_N - 1] += all;
+    }
+    for (hipEvent_t ev : pf.ev) (void)hipEventDestroy(ev);
+    if (e != hipSuccess) return fail(h, LLM_EDEVICE, std::string("profile: ") + hipGetErrorString(e));
+    for (int c = 0; c < PC_N; c++) ms_out[c] = (float)(acc[c] / reps);
+    return LLM_OK;
+}
+
 extern "C" {
 
 int64_t llm_ffn_hidden(const llm_params *p)
@@ -819,28 +855,30 @@ int llm_profile_decode(llm_t *h, int32_t prev_pos, int32_t reps, float *ms_out)
     if (prev_pos < 1 || prev_pos >= h->d.S) return fail(h, LLM_EINVAL, "prev_pos must be in [1, max_seq_len)");
     if (prev_pos > h->last_pos + 1) return fail(h, LLM_ESTATE, "prev_pos skips positions whose KV is not written");
     if (!h->col_written[prev_pos]) return fail(h, LLM_ESTATE, "token column prev_pos has not been written");
-    Prof pf;
-    double acc[PC_N] = {0};
-    hipError_t e = hipSuccess;
-    for (int r = 0; r < reps && e == hipSuccess; r++) {
-        pf.used = 0;
-        e = launch_set_int(h->pos_dev, prev_pos, h->stream);
-        if (e == hipSuccess) e = forward(h, h->cur_B, 1, h->pos_dev, &pf);
-        if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
-        for (size_t i = 0; e == hipSuccess && i + 1 < pf.used; i += 2) {
-            float ms = 0.f;
-            e = hipEventElapsedTime(&ms, pf.ev[i], pf.ev[i + 1]);
-            acc[pf.cls[i / 2]] += ms;
-        }
-        float all = 0.f;
-        if (e == hipSuccess && pf.used >= 2) e = hipEventElapsedTime(&all, pf.ev[0], pf.ev[pf.used - 1]);
-        acc[PC_N - 1] += all;
-    }
-    for (hipEvent_t ev : pf.ev) (void)hipEventDestroy(ev);
-    if (e != hipSuccess) return fail(h, LLM_EDEVICE, std::string("profile: ") + hipGetErrorString(e));
-    for (int c = 0; c < PC_N; c++) ms_out[c] = (float)(acc[c] / reps);
+    rc = profiled_forward(h, h->cur_B, 1, prev_pos, reps, ms_out);
+    if (rc) return rc;
     h->last_pos = prev_pos;
     h->logits_valid = true;
+    return LLM_OK;
+}
+
+int llm_profile_prefill(llm_t *h, const int32_t *tokens_d, int32_t B, int32_t T, int32_t reps, float *ms_out)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if ((rc = check_prefill_args(h, B, T))) return rc;
+    if (!tokens_d || !ms_out || reps < 1) return fail(h, LLM_EINVAL, "bad arguments");
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    HIPC(h, hipMemcpy2DAsync(h->tok, (size_t)h->d.S * 4, tokens_d, (size_t)T * 4, (size_t)T * 4, B,
+                             hipMemcpyDeviceToDevice, h->stream));
+    if ((rc = ensure_ws(h, (int64_t)B * T))) return rc;
+    if ((rc = profiled_forward(h, B, T, -1, reps, ms_out))) return rc;
+    h->prefilled = true;
+    h->logits_valid = true;
+    h->cur_B = B;
+    h->last_pos = T - 1;
+    std::fill(h->col_written.begin(), h->col_written.end(), 0);
+    std::fill(h->col_written.begin(), h->col_written.begin() + T, 1);
     return LLM_OK;
 }
 

@@ -206,6 +206,7 @@ def test_profile_hooks(B):
     want, _ = gpu_forced_logits(h, toks, 10, 5)
     prof = h.profile_decode(14, 2)
     assert all(np.isfinite(v) and v >= 0 for v in prof.values()) and prof["step"] > 0
+    assert prof["qkv"] > 0 and prof["w13"] > 0 and prof["attention"] > 0
     us = h.profile_projections(2)
     say("  us per launch", us)
     assert all(np.isfinite(v) and v > 0 for v in us.values())
@@ -213,4 +214,10 @@ def test_profile_hooks(B):
         h.decode(15)
     got, _ = gpu_forced_logits(h, toks, 10, 5)
     assert np.array_equal(got, want)
+    # the profiled prefill is a prefill: same logits as the plain one
+    import torch
+    td = torch.from_numpy(np.ascontiguousarray(toks[:, :10])).cuda()
+    pp = h.profile_prefill_d(td.data_ptr(), 2, 10, 2)
+    assert pp["step"] > 0 and pp["qkv"] > 0
+    assert np.array_equal(h.get_logits(), want[:, 0])
     h.destroy()
