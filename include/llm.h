@@ -115,6 +115,21 @@ void *llm_get_stream(llm_t *h);
 int llm_prefill(llm_t *h, const int32_t *tokens, int32_t B, int32_t T);
 int llm_prefill_d(llm_t *h, const int32_t *tokens_d, int32_t B, int32_t T);
 
+/* Prefill at an offset (chunked prefill; Transformer.forward(tokens,
+ * start_pos) with T tokens, walkthrough section 3.8: the mask is a block of
+ * zeros over the cached positions followed by the causal triangle).  Runs
+ * tokens[B][T] at positions start_pos..start_pos+T-1 attending to the cache
+ * prefix [0, start_pos) and causally to themselves; writes the KV cache and
+ * token columns [start_pos, start_pos+T) and leaves the logits of position
+ * start_pos+T-1.  start_pos == 0 is llm_prefill.  start_pos > 0 requires an
+ * earlier prefill of the same B with KV written up to start_pos-1
+ * (start_pos <= last position + 1), else LLM_ESTATE; start_pos + T must not
+ * exceed max_seq_len (LLM_EINVAL).  Positions after start_pos+T-1 that an
+ * earlier pass wrote stay in the cache but are not attended to until
+ * rewritten. */
+int llm_prefill_at(llm_t *h, int32_t start_pos, const int32_t *tokens, int32_t B, int32_t T);
+int llm_prefill_at_d(llm_t *h, int32_t start_pos, const int32_t *tokens_d, int32_t B, int32_t T);
+
 /* One decode step (seqlen 1, no mask: the course notes on generate,
  * section 3): runs tok[:, prev_pos] at position prev_pos against cached keys
  * 0..prev_pos, writes the KV cache at prev_pos, leaves logits of position

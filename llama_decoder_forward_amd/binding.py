@@ -58,6 +58,8 @@ EXPORTS = {
     "llm_sample_d": (C.c_int, [_vp, C.c_float, C.c_float, _vp, _vp]),
     "llm_set_tokens": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
     "llm_set_tokens_d": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
+    "llm_prefill_at": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32, C.c_int32]),
+    "llm_prefill_at_d": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32, C.c_int32]),
     "llm_profile_decode": (C.c_int, [_vp, C.c_int32, C.c_int32, _vp]),
     "llm_profile_prefill": (C.c_int, [_vp, _vp, C.c_int32, C.c_int32, C.c_int32, _vp]),
     "llm_profile_projections": (C.c_int, [_vp, C.c_int32, _vp]),
@@ -143,6 +145,16 @@ class Handle:
 
     def prefill_d(self, tokens_ptr: int, B: int, T: int):
         self._ck(_lib.llm_prefill_d(self.ptr, C.c_void_p(tokens_ptr), B, T))
+        self.B = B
+
+    def prefill_at(self, start_pos: int, tokens):
+        t, p = _arr(tokens, np.int32)
+        B, T = t.shape
+        self._ck(_lib.llm_prefill_at(self.ptr, start_pos, p, B, T))
+        self.B = B
+
+    def prefill_at_d(self, start_pos: int, tokens_ptr: int, B: int, T: int):
+        self._ck(_lib.llm_prefill_at_d(self.ptr, start_pos, C.c_void_p(tokens_ptr), B, T))
         self.B = B
 
     def decode(self, prev_pos: int):

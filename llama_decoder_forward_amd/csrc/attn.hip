@@ -170,7 +170,9 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Causal prefill (positions 0..T-1 of every row): flash-style online
+// Causal prefill of T tokens at positions p0..p0+T-1 of every row over the
+// cache prefix 0..p0-1 and themselves (walkthrough section 3.8: a zero
+// block before the causal triangle when p0 > 0): flash-style online
 // softmax.  Grid (B*H, ceil(T/128)); 4 waves x 32 queries (two MFMA column
 // groups).  64-key tiles of K (in permuted operand order) and V^T are staged
 // in LDS with register prefetch of the next tile.  Tiles entirely above a
@@ -180,7 +182,7 @@ constexpr int PF_Q = 128, PF_K = 64;
 
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restrict__ q,
                                                            const half_t *__restrict__ kc,
-                                                           const half_t *__restrict__ vc, int T,
+                                                           const half_t *__restrict__ vc, int T, int p0,
                                                            int H, int Hkv, int S,
                                                            half_t *__restrict__ out, int out_lay)
 {
@@ -216,8 +218,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
         for (int dt = 0; dt < 8; dt++) acc[c][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     float mrun[2] = {kNegBig, kNegBig}, lrun[2] = {0.f, 0.f};
 
+    // query t sits at absolute position p0 + t and sees keys 0 .. p0 + t
+    // (the cache prefix written before, then the causal block)
+    const int Lk = p0 + T;
     const int qlast = min(q0 + PF_Q, T) - 1;
-    const int ntiles = qlast / PF_K + 1;
+    const int ntiles = (p0 + qlast) / PF_K + 1;
 
     half8 rk[4], rv[4];
     auto load_tile = [&](int kt) {
@@ -226,14 +231,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
         for (int j = 0; j < 4; j++) {
             const int c = tid + 256 * j;
             const int key = c >> 4, dch = c & 15;  // K: 64 keys x 16 chunks of 8 d
-            rk[j] = base + key < T ? *reinterpret_cast<const half8 *>(K + (int64_t)(base + key) * hd + dch * 8) : z;
+            rk[j] = base + key < Lk ? *reinterpret_cast<const half8 *>(K + (int64_t)(base + key) * hd + dch * 8) : z;
             const int d = c >> 3, kch = c & 7;     // V^T: 128 d x 8 chunks of 8 keys
             const int key0 = base + kch * 8;
             const half_t *vp = V + (int64_t)(key0 >> 5) * (32 * hd) + d * 32 + (key0 & 31);
-            rv[j] = key0 + 8 <= T ? *reinterpret_cast<const half8 *>(vp) : z;
-            if (key0 < T && key0 + 8 > T) {
+            rv[j] = key0 + 8 <= Lk ? *reinterpret_cast<const half8 *>(vp) : z;
+            if (key0 < Lk && key0 + 8 > Lk) {
                 half8 t8;
-                for (int e = 0; e < 8; e++) t8[e] = key0 + e < T ? vp[e] : (half_t)0.f;
+                for (int e = 0; e < 8; e++) t8[e] = key0 + e < Lk ? vp[e] : (half_t)0.f;
                 rv[j] = t8;
             }
         }
@@ -264,10 +269,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
         __syncthreads();
         if (kt + 1 < ntiles) load_tile(kt + 1);
         const int kbase = kt * PF_K;
-        if (kbase > wq0 + 31) continue;  // all keys after this wave's queries
+        if (kbase > p0 + wq0 + 31) continue;  // all keys after this wave's queries
 #pragma unroll
         for (int c = 0; c < 2; c++) {
-            const int qi = wq0 + 16 * c + r;  // this lane's query position
+            const int qi = p0 + wq0 + 16 * c + r;  // this lane's query position
             float p[2][8];
             float mx = kNegBig;
 #pragma unroll
@@ -400,7 +405,7 @@ hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s)
     if (a.out_lay != ACT_ROWS && a.out_lay != ACT_TILED) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.B * a.H, (a.T + PF_Q - 1) / PF_Q), dim3(256), 0,
                        s, (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache,
-                       a.T, a.H, a.Hkv, a.S, (half_t *)a.out, a.out_lay);
+                       a.T, a.pos_imm, a.H, a.Hkv, a.S, (half_t *)a.out, a.out_lay);
     return hipGetLastError();
 }
 

@@ -124,7 +124,7 @@ hipError_t launch_read_weights(const void *src, int dtype, int mat, int64_t N, i
                                int64_t count, void *out, hipStream_t s);
 
 hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int B, int T,
-                        const int *pos_dev, int D, int dtype, void *x, hipStream_t s);
+                        const int *pos_dev, int pos0, int D, int dtype, void *x, hipStream_t s);
 // y_lay: layout of y (fp16 only for non-row-major layouts).
 hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int D, float eps,
                           int dtype, void *y, hipStream_t s, int y_lay = ACT_ROWS);

@@ -299,7 +299,7 @@ hipError_t prof_end(Prof *pf, hipStream_t s)
 // (SwiGLU), or the output head on the last position of each row (fp32
 // logits).  With `fused` the RMSNorm in front of wq|wk|wv, w1|w3 and the
 // head runs inside the product on x; otherwise the product reads xn.
-hipError_t product(llm_t *h, int l, int mat, int B, int T, const int *pos_dev, bool fused)
+hipError_t product(llm_t *h, int l, int mat, int B, int T, const int *pos_dev, bool fused, int pos0 = 0)
 {
     const Dims &d = h->d;
     const int M = B * T;
@@ -312,7 +312,7 @@ hipError_t product(llm_t *h, int l, int mat, int B, int T, const int *pos_dev, b
         eq.vcache = layer_vc(h, l);
         eq.rope = h->rope;
         eq.pos_dev = pos_dev;
-        eq.pos_imm = 0;
+        eq.pos_imm = pos0;
         eq.T = T;
         eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = d.S;
         const char *nw = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
@@ -338,10 +338,11 @@ hipError_t product(llm_t *h, int l, int mat, int B, int T, const int *pos_dev, b
     }
 }
 
-// The forward pass over B rows of T tokens (walkthrough sections 2, 3.5-3.8).
-// Decode (pos_dev != NULL, T == 1) reads its position from device memory so
-// that the launch sequence can be captured once and replayed.
-hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullptr)
+// The forward pass over B rows of T tokens (walkthrough sections 2, 3.5-3.8)
+// at positions pos0..pos0+T-1.  Decode (pos_dev != NULL, T == 1) reads its
+// position from device memory so that the launch sequence can be captured
+// once and replayed.
+hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullptr, int pos0 = 0)
 {
     const Dims &d = h->d;
     const int M = B * T;
@@ -358,7 +359,7 @@ hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullpt
         TRY_RAW(x);                        \
         TRY_RAW(prof_end(pf, s));          \
     } while (0)
-    TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, B, T, pos_dev, d.D, d.dtype, h->x, s));
+    TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, B, T, pos_dev, pos0, d.D, d.dtype, h->x, s));
     const bool fused = fuse_norm(h, M);
     const int lay = act_layout(h, B, T, pos_dev);
     for (int l = 0; l < d.NL; l++) {
@@ -366,12 +367,12 @@ hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullpt
         const char *nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
         // attention_norm -> wq|wk|wv with RoPE and the KV-cache write
         if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay));
-        TRYC(PC_QKV, product(h, l, MAT_QKV, B, T, pos_dev, fused));
+        TRYC(PC_QKV, product(h, l, MAT_QKV, B, T, pos_dev, fused, pos0));
         // attention over the cache
         AttnArgs aa{};
         aa.q = h->q; aa.kcache = layer_kc(h, l); aa.vcache = layer_vc(h, l); aa.out = h->o;
         aa.B = B; aa.T = T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
-        aa.pos_dev = pos_dev; aa.pos_imm = 0;
+        aa.pos_dev = pos_dev; aa.pos_imm = pos0;
         aa.out_lay = lay;
         if (d.dtype == LLM_F32) TRYC(PC_ATTN, launch_attn_f32(aa, s));
         else if (pos_dev) TRYC(PC_ATTN, launch_attn_decode_f16(aa, s));
@@ -525,28 +526,34 @@ int after_forward(llm_t *h, hipError_t e)
     return LLM_OK;
 }
 
-int prefill_common(llm_t *h, int B, int T)
+int prefill_common(llm_t *h, int B, int T, int start = 0)
 {
     if (!h->dry) {
         int rc = ensure_ws(h, (int64_t)B * T);
         if (rc) return rc;
-        hipError_t e = forward(h, B, T, nullptr);
+        hipError_t e = forward(h, B, T, nullptr, nullptr, start);
         rc = after_forward(h, e);
         if (rc) return rc;
     }
     h->prefilled = true;
     h->logits_valid = true;
     h->cur_B = B;
-    h->last_pos = T - 1;
-    std::fill(h->col_written.begin(), h->col_written.end(), 0);
-    std::fill(h->col_written.begin(), h->col_written.begin() + T, 1);
+    h->last_pos = start + T - 1;
+    if (start == 0) std::fill(h->col_written.begin(), h->col_written.end(), 0);
+    std::fill(h->col_written.begin() + start, h->col_written.begin() + start + T, 1);
     return LLM_OK;
 }
 
-int check_prefill_args(llm_t *h, int B, int T)
+int check_prefill_args(llm_t *h, int B, int T, int start = 0)
 {
     if (B < 1 || B > h->d.maxB) return fail(h, LLM_EINVAL, "B must be in [1, max_batch_size]");
-    if (T < 1 || T > h->d.S) return fail(h, LLM_EINVAL, "T must be in [1, max_seq_len]");
+    if (start < 0) return fail(h, LLM_EINVAL, "start_pos must be >= 0");
+    if (T < 1 || (int64_t)start + T > h->d.S) return fail(h, LLM_EINVAL, "need 1 <= T and start_pos + T <= max_seq_len");
+    if (start > 0) {
+        if (!h->prefilled) return fail(h, LLM_ESTATE, "prefill at an offset needs the cache prefix of an earlier prefill");
+        if (B != h->cur_B) return fail(h, LLM_ESTATE, "prefill at an offset must keep the batch of the cache prefix");
+        if (start > h->last_pos + 1) return fail(h, LLM_ESTATE, "start_pos skips positions whose KV is not written");
+    }
     return LLM_OK;
 }
 
@@ -738,6 +745,33 @@ int llm_prefill_d(llm_t *h, const int32_t *tokens_d, int32_t B, int32_t T)
     HIPC(h, hipMemcpy2DAsync(h->tok, (size_t)h->d.S * 4, tokens_d, (size_t)T * 4, (size_t)T * 4, B,
                              hipMemcpyDeviceToDevice, h->stream));
     return prefill_common(h, B, T);
+}
+
+int llm_prefill_at(llm_t *h, int32_t start_pos, const int32_t *tokens, int32_t B, int32_t T)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if ((rc = check_prefill_args(h, B, T, start_pos))) return rc;
+    if (!tokens) return fail(h, LLM_EINVAL, "tokens is NULL");
+    if (!tokens_ok(tokens, (int64_t)B * T, h->d.V)) return fail(h, LLM_EINVAL, "token id out of [0, vocab)");
+    if (!h->dry) {
+        HIPC(h, hipMemcpy2DAsync(h->tok + start_pos, (size_t)h->d.S * 4, tokens, (size_t)T * 4, (size_t)T * 4, B,
+                                 hipMemcpyHostToDevice, h->stream));
+        HIPC(h, hipStreamSynchronize(h->stream));
+    }
+    return prefill_common(h, B, T, start_pos);
+}
+
+int llm_prefill_at_d(llm_t *h, int32_t start_pos, const int32_t *tokens_d, int32_t B, int32_t T)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if ((rc = check_prefill_args(h, B, T, start_pos))) return rc;
+    if (!tokens_d) return fail(h, LLM_EINVAL, "tokens is NULL");
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    HIPC(h, hipMemcpy2DAsync(h->tok + start_pos, (size_t)h->d.S * 4, tokens_d, (size_t)T * 4, (size_t)T * 4, B,
+                             hipMemcpyDeviceToDevice, h->stream));
+    return prefill_common(h, B, T, start_pos);
 }
 
 int llm_decode(llm_t *h, int32_t prev_pos)

@@ -6,14 +6,15 @@ namespace {
 constexpr int kThreads = 256;
 
 // Row m of x = row tok of E (the reference's tok_embeddings lookup,
-// walkthrough section 2).  Prefill: m = b*T + t reads tok[b][t]; decode
-// (pos_dev != NULL, T == 1): row b reads tok[b][*pos_dev].
+// walkthrough section 2).  Prefill at positions pos0..: m = b*T + t reads
+// tok[b][pos0 + t]; decode (pos_dev != NULL, T == 1): row b reads
+// tok[b][*pos_dev].
 __global__ void embed_kernel(const char *E, const int32_t *tok, int64_t tok_ld, int T,
-                             const int *pos_dev, int64_t row_bytes, char *x)
+                             const int *pos_dev, int pos0, int64_t row_bytes, char *x)
 {
     int m = blockIdx.x;
     int b = m / T, t = m % T;
-    int col = pos_dev ? *pos_dev : t;
+    int col = (pos_dev ? *pos_dev : pos0) + t;
     int32_t id = tok[(int64_t)b * tok_ld + col];
     const uint4 *src = reinterpret_cast<const uint4 *>(E + (int64_t)id * row_bytes);
     uint4 *dst = reinterpret_cast<uint4 *>(x + (int64_t)m * row_bytes);
@@ -93,11 +94,11 @@ __global__ void rmsnorm_f32_kernel(const float *x, int64_t ldx, const float *w, 
 }  // namespace
 
 hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int B, int T,
-                        const int *pos_dev, int D, int dtype, void *x, hipStream_t s)
+                        const int *pos_dev, int pos0, int D, int dtype, void *x, hipStream_t s)
 {
     int64_t row_bytes = (int64_t)D * (dtype == 1 ? 2 : 4);
     hipLaunchKernelGGL(embed_kernel, dim3(B * T), dim3(kThreads), 0, s, (const char *)E, tok,
-                       tok_ld, T, pos_dev, row_bytes, (char *)x);
+                       tok_ld, T, pos_dev, pos0, row_bytes, (char *)x);
     return hipGetLastError();
 }
 

@@ -100,6 +100,38 @@ def test_dry_handle_protocol():
     h.destroy()
 
 
+def test_dry_handle_prefill_at():
+    """Prefill at an offset: needs the cache prefix of the same batch and may
+    not skip positions or run past the cache."""
+    w = configs.TINY
+    h = b.llm_create_dry(b.params_for(w, max_batch_size=2))
+    S = w.max_seq_len
+
+    def code(fn, *a):
+        try:
+            fn(*a)
+            return b.LLM_OK
+        except b.LlmError as e:
+            return e.code
+
+    z = lambda B, T: np.zeros((B, T), np.int32)
+    assert code(h.prefill_at, 4, z(1, 4)) == b.LLM_ESTATE      # no prefix yet
+    assert code(h.prefill_at, -1, z(1, 4)) == b.LLM_EINVAL
+    assert code(h.prefill_at, 0, z(2, 6)) == b.LLM_OK          # start 0: a plain prefill
+    assert code(h.prefill_at, 7, z(2, 4)) == b.LLM_ESTATE      # skips position 6
+    assert code(h.prefill_at, 6, z(1, 4)) == b.LLM_ESTATE      # batch differs from the prefix
+    assert code(h.prefill_at, 6, z(2, S - 5)) == b.LLM_EINVAL  # runs past the cache
+    assert code(h.prefill_at, 6, np.full((2, 4), w.vocab_size, np.int32)) == b.LLM_EINVAL
+    assert code(h.prefill_at, 6, z(2, 4)) == b.LLM_OK          # positions 6..9
+    assert code(h.decode, 10) == b.LLM_ESTATE                  # column 10 not written
+    assert code(h.sample, 0.0, 1.0, None, False) == b.LLM_OK   # writes column 10
+    assert code(h.decode, 10) == b.LLM_OK
+    assert code(h.prefill_at, 3, z(2, 2)) == b.LLM_OK          # rewrite an earlier stretch
+    assert code(h.decode, 5) == b.LLM_OK
+    assert code(h.prefill_at, S - 2, z(2, 2)) == b.LLM_ESTATE  # beyond last position + 1
+    h.destroy()
+
+
 def test_dry_handle_last_slot():
     """With prompt 8 and 24 steps the last decode runs at position S-1 = 31
     and its sampled token has no column left (it is returned, not stored)."""

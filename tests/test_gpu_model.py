@@ -158,6 +158,57 @@ def test_long_prefill_tiled(B, rows, T0):
     h.destroy()
 
 
+def chunked_forced_logits(h, tokens, chunks, steps):
+    """Prefill tokens in consecutive chunks (prefill_at), then decode steps
+    with forced columns; returns the logits after each chunk and each step,
+    [B][len(chunks) + steps][V]."""
+    out, pos = [], 0
+    for c in chunks:
+        h.prefill_at(pos, tokens[:, pos:pos + c])
+        pos += c
+        out.append(h.get_logits())
+    h.sample(0.0)
+    for p in range(pos, pos + steps):
+        h.set_tokens(p, tokens[:, p])
+        h.decode(p)
+        out.append(h.get_logits())
+        h.sample(0.0)
+    return np.stack(out, 1)
+
+
+@pytest.mark.parametrize("case", ["fp32", "fp16", "fp16-tiled", "fp16-mha"])
+def test_prefill_at_offset(B, case):
+    """Chunked prefill: each chunk attends to the cache prefix of the earlier
+    chunks and causally to itself; logits at every chunk end and the decode
+    steps after it match the oracle's one-pass forward."""
+    if case == "fp32":
+        kw = dict(n_layers=2, dim=64, n_heads=4, n_kv_heads=2, vocab_size=256, multiple_of=32,
+                  ffn_dim_multiplier=0.0, max_batch_size=2, max_seq_len=32, dtype=0)
+        rows, chunks, steps = 2, [5, 1, 7], 4
+    elif case == "fp16":
+        kw = small_kw()
+        rows, chunks, steps = 3, [16, 24, 1, 9], 4
+    elif case == "fp16-tiled":   # a >= 1024-row chunk after a prefix, then short ones
+        kw = small_kw(max_seq_len=1216, max_batch_size=1)
+        rows, chunks, steps = 1, [100, 1040, 33], 3
+    else:
+        kw = small_kw(n_kv_heads=4)
+        rows, chunks, steps = 2, [63, 58], 3
+    N = sum(chunks) + steps
+    toks = synth.tokens(48, rows, N, kw["vocab_size"])
+    say("prefill at offset", case, chunks)
+    h = B.llm_create(B.make_params(**kw), 97)
+    got = chunked_forced_logits(h, toks, chunks, steps)
+    full = oracle.forward_stream(ocfg(kw), 97, toks, 0)
+    ends = list(np.cumsum(chunks) - 1) + list(range(sum(chunks), N))
+    want = full[:, ends]
+    if case == "fp32":
+        assert np.abs(got - want).max() <= 1e-3
+    else:
+        check_logits(got, want)
+    h.destroy()
+
+
 def test_small_fp16_sampled_and_deterministic(B):
     kw = small_kw()
     T0, steps = 9, 10
