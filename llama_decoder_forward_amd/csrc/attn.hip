@@ -28,22 +28,24 @@ __device__ __forceinline__ int perm_key(int t, int r) { return 8 * (r >> 2) + 4 
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp(m_old - m_new) is never NaN
 
 // ---------------------------------------------------------------------------
-// Decode: one work-group of 8 waves per (row b, KV head).  The attended
-// length L = pos + 1 is walked in 32-key steps, wave w taking steps w, w+8,
+// Decode: one work-group of NW waves per (row b, KV head).  The attended
+// length L = pos + 1 is walked in 32-key steps, wave w taking steps w, w+NW,
 // ...; each wave keeps the running max / sum / unnormalised output of all
 // n_rep query heads of the group, so every K/V byte is read once per query
-// group.  The 8 waves are merged in LDS in three halving rounds (fixed
-// order), and the normalised output written.
+// group.  PF: a wave's next step is loaded while the current one computes.
+// The NW waves are merged in LDS in halving rounds (fixed order), and the
+// normalised output written.  Few (row, KV head) pairs take 8 waves (the
+// work-group count, not the bandwidth, is the limit there); many pairs
+// take 2 or 4 so that more of them fit the CUs at once.
 // ---------------------------------------------------------------------------
-constexpr int DEC_WAVES = 8;
-
-__global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
+template <int NW, bool PF>
+__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
     const half_t *__restrict__ q, const half_t *__restrict__ kc, const half_t *__restrict__ vc,
     int H, int Hkv, int S, const int *pos_dev, int pos_imm, half_t *__restrict__ out, int out_lay)
 {
     constexpr int hd = 128;
-    __shared__ floatx4 so[DEC_WAVES / 2][8][64];
-    __shared__ float sm[DEC_WAVES / 2][16], sl[DEC_WAVES / 2][16];
+    __shared__ floatx4 so[NW / 2][8][64];
+    __shared__ float sm[NW / 2][16], sl[NW / 2][16];
     const int bk = blockIdx.x, b = bk / Hkv, kvh = bk % Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int L = (pos_dev ? *pos_dev : pos_imm) + 1;
@@ -68,10 +70,9 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
     for (int dt = 0; dt < 8; dt++) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     float mrun = kNegBig, lrun = 0.f;
 
-    for (int st = wave; st < nsteps; st += DEC_WAVES) {
+    // all K and V operands of a step are loaded before any of its arithmetic
+    auto load = [&](int st, half8 (&kf)[2][4], half8 (&vf)[8]) {
         const int k0 = 32 * st;
-        // all K and V operands of the step are loaded before any arithmetic
-        half8 kf[2][4], vf[8];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
             const int key = k0 + perm_key(t, r);
@@ -93,6 +94,9 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
                 for (int e = 0; e < 8; e++) vf[dt][e] = (kk + e < L) ? vrow[e] : (half_t)0.f;
             }
         }
+    };
+    auto compute = [&](int st, const half8 (&kf)[2][4], const half8 (&vf)[8]) {
+        const int k0 = 32 * st;
         floatx4 sc[2];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
@@ -130,11 +134,31 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void attn_decode_kernel(
         mrun = mnew;
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) acc[dt] = mfma16(vf[dt], pb, acc[dt] * fac);
+    };
+    half8 kf[2][4], vf[8];
+    int st = wave;
+    if (st < nsteps) load(st, kf, vf);
+    for (; st < nsteps; st += NW) {
+        const int nx = st + NW;
+        if (PF) {
+            half8 kn[2][4], vn[8];
+            if (nx < nsteps) load(nx, kn, vn);
+            compute(st, kf, vf);
+#pragma unroll
+            for (int t = 0; t < 2; t++)
+#pragma unroll
+                for (int s = 0; s < 4; s++) kf[t][s] = kn[t][s];
+#pragma unroll
+            for (int dt = 0; dt < 8; dt++) vf[dt] = vn[dt];
+        } else {
+            compute(st, kf, vf);
+            if (nx < nsteps) load(nx, kf, vf);
+        }
     }
 
     // merge: in each round the upper half of the live waves hands its state to
     // the lower half (lane (r, g) holds O^T[16 dt + 4 g + i][head r])
-    for (int half = DEC_WAVES / 2; half >= 1; half >>= 1) {
+    for (int half = NW / 2; half >= 1; half >>= 1) {
         if (wave >= half && wave < 2 * half) {
 #pragma unroll
             for (int dt = 0; dt < 8; dt++) so[wave - half][dt][lane] = acc[dt];
@@ -394,9 +418,18 @@ __global__ void kv_write_kernel(const Tv *k, const Tv *v, int T, int pos0, int H
 hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s)
 {
     if (a.out_lay && (a.out_lay > 2 || a.B > 16 * a.out_lay || a.T != 1)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_decode_kernel, dim3(a.B * a.Hkv), dim3(DEC_WAVES * 64), 0, s,
-                       (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache, a.H,
-                       a.Hkv, a.S, a.pos_dev, a.pos_imm, (half_t *)a.out, a.out_lay);
+    const int pairs = a.B * a.Hkv;
+    const half_t *q = (const half_t *)a.q, *kc = (const half_t *)a.kcache, *vc = (const half_t *)a.vcache;
+    half_t *o = (half_t *)a.out;
+    if (pairs >= 512)
+        hipLaunchKernelGGL((attn_decode_kernel<2, true>), dim3(pairs), dim3(128), 0, s, q, kc, vc, a.H, a.Hkv, a.S,
+                           a.pos_dev, a.pos_imm, o, a.out_lay);
+    else if (pairs >= 128)
+        hipLaunchKernelGGL((attn_decode_kernel<4, false>), dim3(pairs), dim3(256), 0, s, q, kc, vc, a.H, a.Hkv, a.S,
+                           a.pos_dev, a.pos_imm, o, a.out_lay);
+    else
+        hipLaunchKernelGGL((attn_decode_kernel<8, false>), dim3(pairs), dim3(512), 0, s, q, kc, vc, a.H, a.Hkv, a.S,
+                           a.pos_dev, a.pos_imm, o, a.out_lay);
     return hipGetLastError();
 }
 

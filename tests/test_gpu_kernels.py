@@ -225,22 +225,26 @@ def test_attention_decode(B, small, L):
     assert cosine(got.reshape(-1, d), want.reshape(-1, d)).min() > 0.9999
 
 
-def test_attention_decode_single_split(B):
-    """B * n_kv_heads = 512 work-groups: one split per KV head, no merge."""
-    kw = small_f16(max_batch_size=256, max_seq_len=128)
+@pytest.mark.parametrize("Bn,L", [(64, 300), (64, 33), (256, 77), (256, 1)])
+def test_attention_decode_many_pairs(B, Bn, L):
+    """Bn * n_kv_heads (row, KV head) pairs: 128 pairs take the four-wave
+    work-groups, 512 the two-wave ones with the next step prefetched; ragged
+    last steps and a single key included."""
+    kw = small_f16(max_batch_size=Bn, max_seq_len=320)
     h = B.llm_create(B.make_params(**kw), 78)
-    Bn, H, Hkv, d, L = 256, kw["n_heads"], kw["n_kv_heads"], 128, 77
-    rng = np.random.default_rng(15)
+    H, Hkv, d = kw["n_heads"], kw["n_kv_heads"], 128
+    assert Bn * Hkv in (128, 512)
+    rng = np.random.default_rng(15 + L)
     K = randn_f16(rng, (Bn, L, Hkv, d))
     V = randn_f16(rng, (Bn, L, Hkv, d))
     q = randn_f16(rng, (Bn, 1, H, d), 0.3)
-    say("attention decode single split")
+    say("attention decode many pairs", Bn, L)
     kd, vd = dev(K), dev(V)
     h.op_kv_write(0, kd.data_ptr(), vd.data_ptr(), Bn, L, 0)
     qd, od = dev(q), empty((Bn, 1, H, d), np.float16)
     h.op_attention(0, qd.data_ptr(), Bn, 1, L - 1, od.data_ptr())
     got = host(od).astype(np.float32)
-    rows = [0, 77, 255]
+    rows = [0, Bn // 2 + 1, Bn - 1]
     want = attention_reference(q[rows], K[rows], V[rows], [L - 1], H // Hkv)
     assert np.max(np.abs(got[rows] - want)) < 4e-3
     h.destroy()
