@@ -155,6 +155,11 @@ hipError_t launch_softmax_temp(const float *logits, int B, int V, float temperat
 hipError_t launch_top_p(const float *probs, int B, int V, float top_p, const float *uniforms,
                         int32_t *tok, int64_t tok_ld, int write_col, int32_t *out,
                         hipStream_t s);
+// Temperature softmax (from_logits) and top-p in one launch for V <= 32768,
+// else the two-launch path through probs_scratch[B][V].
+hipError_t launch_sample_top_p(const float *src, bool from_logits, float temperature, int B, int V, float top_p,
+                               const float *uniforms, int32_t *tok, int64_t tok_ld, int write_col, int32_t *out,
+                               float *probs_scratch, hipStream_t s);
 hipError_t launch_set_int(int *dst, int v, hipStream_t s);
 hipError_t launch_set_tokens(int32_t *tok, int64_t tok_ld, int B, int col, const int32_t *vals,
                              const uint8_t *mask, hipStream_t s);

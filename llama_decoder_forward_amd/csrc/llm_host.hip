@@ -573,10 +573,8 @@ int sample_common(llm_t *h, float temperature, float top_p, const float *uniform
         if (temperature <= 0.f) {
             e = launch_argmax(h->logits, h->cur_B, d.V, h->tok, d.S, col, out_d, h->stream);
         } else {
-            e = launch_softmax_temp(h->logits, h->cur_B, d.V, temperature, h->probs, h->stream);
-            if (e == hipSuccess)
-                e = launch_top_p(h->probs, h->cur_B, d.V, top_p, uniforms_d, h->tok, d.S, col, out_d,
-                                 h->stream);
+            e = launch_sample_top_p(h->logits, true, temperature, h->cur_B, d.V, top_p, uniforms_d, h->tok, d.S,
+                                    col, out_d, h->probs, h->stream);
         }
         int rc = after_forward(h, e);
         if (rc) return rc;
@@ -1034,7 +1032,8 @@ int llm_sample_probs(llm_t *h, const float *probs, int32_t B, float top_p, const
     if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
     HIPC(h, hipMemcpyAsync(h->probs, probs, (size_t)B * h->d.V * sizeof(float), hipMemcpyHostToDevice, h->stream));
     HIPC(h, hipMemcpyAsync(h->uni, uniforms, (size_t)B * sizeof(float), hipMemcpyHostToDevice, h->stream));
-    HIPC(h, launch_top_p(h->probs, B, h->d.V, top_p, h->uni, h->tok, h->d.S, -1, h->outtok, h->stream));
+    HIPC(h, launch_sample_top_p(h->probs, false, 1.f, B, h->d.V, top_p, h->uni, h->tok, h->d.S, -1, h->outtok,
+                                nullptr, h->stream));
     HIPC(h, hipMemcpyAsync(out, h->outtok, (size_t)B * sizeof(int32_t), hipMemcpyDeviceToHost, h->stream));
     HIPC(h, hipStreamSynchronize(h->stream));
     h->logits_valid = false;  // the probability buffer no longer matches the logits

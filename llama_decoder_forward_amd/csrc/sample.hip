@@ -228,6 +228,210 @@ __global__ __launch_bounds__(kSampThreads) void top_p_kernel(const float *probs,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Top-p for vocabularies of up to TP_MAXV tokens: one work-group per row with
+// the row's probability patterns resident in LDS (computed there from the
+// logits when the temperature softmax is fused in, with the same arithmetic
+// as softmax_temp_kernel).  Same definition and result as top_p_kernel; the
+// radix select runs in three passes over 11, 10 and 10 bits of the pattern
+// (bit 31 is zero for P >= 0), fine enough that few tokens share a bucket,
+// and the bucket scans are block-parallel instead of one thread's loop.
+// ---------------------------------------------------------------------------
+constexpr int TP_MAXV = 32768;
+constexpr int TP_NB = 2048;
+
+// floor(P * 2^48) from the pattern, in integers: P = m * 2^(e - 150) with the
+// 24-bit significand m (e = 0: subnormal, no hidden bit, exponent of e = 1).
+// The product in qmass() is exact in double, so the two agree.
+__device__ __forceinline__ uint64_t qmass_bits(uint32_t k)
+{
+    const int e = (int)(k >> 23);
+    const uint64_t m = e ? (uint64_t)((k & 0x7fffffu) | 0x800000u) : (uint64_t)(k & 0x7fffffu);
+    const int ee = e ? e : 1;
+    if (ee >= 102) return m << min(ee - 102, 39);  // P <= 1 keeps the shift <= 25
+    return 102 - ee < 64 ? m >> (102 - ee) : 0;
+
+}
+
+struct TpShared {
+    uint32_t hcnt[TP_NB];
+    uint64_t hsum[TP_NB];
+    uint32_t wcnt[kSampThreads / 64];
+    float wf[kSampThreads / 64];
+    SelectResult res;
+    int found;
+};
+
+
+
+// Smallest present key v with A(v) <= X over the LDS keys (as radix_select).
+__device__ __forceinline__ SelectResult radix_select_lds(const uint32_t *keys, int V, uint64_t X, TpShared &sh)
+{
+    uint32_t prefix = 0, pmask = 0;
+    uint64_t above = 0;
+    uint32_t cnt_last = 0;
+    for (int ps = 0; ps < 3; ps++) {
+        const int shift = ps == 0 ? 20 : (ps == 1 ? 10 : 0);
+        const int nb = ps == 0 ? 2048 : 1024;
+        for (int i = threadIdx.x; i < nb; i += blockDim.x) { sh.hcnt[i] = 0; sh.hsum[i] = 0; }
+        __syncthreads();
+        // four patterns per LDS read (V % 4 == 0)
+        const uint4 *k4 = reinterpret_cast<const uint4 *>(keys);
+        for (int i = threadIdx.x; i < V / 4; i += blockDim.x) {
+            const uint4 q4 = k4[i];
+            const uint32_t kk[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint32_t k = kk[j];
+                if ((k & pmask) == prefix) {
+                    const uint32_t dg = (k >> shift) & (uint32_t)(nb - 1);
+                    atomicAdd(&sh.hcnt[dg], 1u);
+                    atomicAdd((unsigned long long *)&sh.hsum[dg], (unsigned long long)qmass_bits(k));
+                }
+            }
+        }
+        __syncthreads();
+        // one wave scans the buckets: lane l owns [l*per, l*per + per), and
+        // G(d) = above + mass of buckets > d
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x, per = nb / 64, d0 = lane * per;
+            uint64_t mine = 0;
+            for (int j = 0; j < per; j++) mine += sh.hsum[d0 + j];
+            uint64_t incl = mine;  // inclusive suffix over lanes
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint64_t u = __shfl_down(incl, o);
+                if (lane + o < 64) incl += u;
+            }
+            uint64_t G = above + (incl - mine);
+            int cand = 0x7fffffff;
+            uint64_t gc = 0;
+            for (int j = per - 1; j >= 0; j--) {  // descending d, G grows
+                const int dd = d0 + j;
+                if (sh.hcnt[dd] > 0 && G <= X) { cand = dd; gc = G; }
+                G += sh.hsum[dd];
+            }
+            int pick = cand;  // exists: the highest present bucket has G = above <= X
+            for (int o = 32; o > 0; o >>= 1) pick = min(pick, __shfl_xor(pick, o));
+            if (cand == pick) {
+                sh.res.key = prefix | ((uint32_t)pick << shift);
+                sh.res.above = gc;
+                sh.res.count = sh.hcnt[pick];
+            }
+        }
+        __syncthreads();
+        prefix = sh.res.key;
+        pmask |= (uint32_t)(nb - 1) << shift;
+        above = sh.res.above;
+        cnt_last = sh.res.count;
+        __syncthreads();
+    }
+    SelectResult r;
+    r.key = prefix;
+    r.above = above;
+    r.count = cnt_last;
+    return r;
+}
+
+__global__ __launch_bounds__(kSampThreads) void top_p_lds_kernel(const float *src, int from_logits,
+                                                                 float temperature, int V, float top_p,
+                                                                 const float *uniforms, int32_t *tok,
+                                                                 int64_t tok_ld, int write_col, int32_t *out)
+{
+    __shared__ TpShared sh;
+    extern __shared__ uint32_t keys[];  // V patterns
+    const int b = blockIdx.x;
+    const float *row = src + (int64_t)b * V;
+    if (from_logits) {
+        // P = softmax(logits * (1/t)) in fp32 with the maximum subtracted; the
+        // scaling and the normalisation multiply by correctly rounded
+        // reciprocals (a division per token made this VALU-bound)
+        const float invt = 1.0f / temperature;
+        const float4 *r4 = reinterpret_cast<const float4 *>(row);
+        float mx = -INFINITY;
+        for (int i = threadIdx.x; i < V / 4; i += blockDim.x) {
+            const float4 v = r4[i];
+            mx = fmaxf(mx, fmaxf(fmaxf(v.x * invt, v.y * invt), fmaxf(v.z * invt, v.w * invt)));
+        }
+        mx = block_max(mx, sh.wf);
+        float s = 0.f;
+        uint4 *k4 = reinterpret_cast<uint4 *>(keys);
+        for (int i = threadIdx.x; i < V / 4; i += blockDim.x) {
+            const float4 v = r4[i];
+            const float e0 = expf(v.x * invt - mx), e1 = expf(v.y * invt - mx);
+            const float e2 = expf(v.z * invt - mx), e3 = expf(v.w * invt - mx);
+            k4[i] = make_uint4(__float_as_uint(e0), __float_as_uint(e1), __float_as_uint(e2), __float_as_uint(e3));
+            s += (e0 + e1) + (e2 + e3);
+        }
+        s = block_sumf(s, sh.wf);
+        const float invs = 1.0f / s;
+        for (int i = threadIdx.x; i < V / 4; i += blockDim.x) {
+            uint4 k = k4[i];
+            k.x = __float_as_uint(__uint_as_float(k.x) * invs) & 0x7fffffffu;
+            k.y = __float_as_uint(__uint_as_float(k.y) * invs) & 0x7fffffffu;
+            k.z = __float_as_uint(__uint_as_float(k.z) * invs) & 0x7fffffffu;
+            k.w = __float_as_uint(__uint_as_float(k.w) * invs) & 0x7fffffffu;
+            k4[i] = k;
+        }
+    } else {
+        for (int i = threadIdx.x; i < V; i += blockDim.x) keys[i] = __float_as_uint(row[i]) & 0x7fffffffu;
+    }
+    __syncthreads();
+
+    const uint64_t thr = (uint64_t)floor((double)top_p * 281474976710656.0);
+    const SelectResult s1 = radix_select_lds(keys, V, thr, sh);
+    const uint64_t q1 = qmass_bits(s1.key);
+    uint64_t kept = s1.count;
+    if (q1 > 0) {
+        const uint64_t lim = (thr - s1.above) / q1 + 1;
+        if (lim < kept) kept = lim;
+    }
+    const uint64_t S = s1.above + kept * q1;
+    const uint64_t U = (uint64_t)floor((double)uniforms[b] * 16777216.0);
+    const uint64_t lo = U * S, hi = __umul64hi(U, S);
+    const uint64_t t = (lo >> 24) | (hi << 40);
+
+    const SelectResult s2 = radix_select_lds(keys, V, t, sh);
+    const uint64_t q2 = qmass_bits(s2.key);
+    const uint32_t m = q2 > 0 ? (uint32_t)((t - s2.above) / q2) : 0u;
+
+    // id of the m-th token (in id order) whose pattern equals s2.key: wave w
+    // owns ids [w*chunk, (w+1)*chunk), lanes read consecutive patterns (no
+    // LDS bank conflicts) and count matches with ballots
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int chunk = (V + nw * 64 - 1) / (nw * 64) * 64;
+    const int w0 = w * chunk, w1 = min(V, w0 + chunk);
+    uint32_t c = 0;
+    for (int base = w0; base < w1; base += 64) {
+        const int i = base + lane;
+        c += (uint32_t)__popcll(__ballot(i < w1 && keys[i] == s2.key));
+    }
+    if (lane == 0) sh.wcnt[w] = c;
+    if (threadIdx.x == 0) sh.found = -1;
+    __syncthreads();
+    uint32_t excl = 0;
+    for (int k = 0; k < w; k++) excl += sh.wcnt[k];
+    if (m >= excl && m < excl + c) {  // wave-uniform
+        uint32_t need = m - excl;
+        for (int base = w0; base < w1; base += 64) {
+            const int i = base + lane;
+            uint64_t bal = __ballot(i < w1 && keys[i] == s2.key);
+            const uint32_t n = (uint32_t)__popcll(bal);
+            if (need < n) {
+                for (uint32_t j = 0; j < need; j++) bal &= bal - 1;  // drop the lowest set bits
+                if (lane == 0) sh.found = base + (int)__builtin_ctzll(bal);
+                break;
+            }
+            need -= n;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int id = sh.found >= 0 ? sh.found : 0;
+        if (write_col >= 0) tok[(int64_t)b * tok_ld + write_col] = id;
+        if (out) out[b] = id;
+    }
+}
+
 __global__ void set_int_kernel(int *dst, int v) { *dst = v; }
 
 __global__ void set_tokens_kernel(int32_t *tok, int64_t tok_ld, int B, int col, const int32_t *vals,
@@ -263,6 +467,24 @@ hipError_t launch_top_p(const float *probs, int B, int V, float top_p, const flo
     hipLaunchKernelGGL(top_p_kernel, dim3(B), dim3(kSampThreads), 0, s, probs, V, top_p, uniforms,
                        tok, tok_ld, write_col, out);
     return hipGetLastError();
+}
+
+hipError_t launch_sample_top_p(const float *src, bool from_logits, float temperature, int B, int V, float top_p,
+                               const float *uniforms, int32_t *tok, int64_t tok_ld, int write_col, int32_t *out,
+                               float *probs_scratch, hipStream_t s)
+{
+    if (V <= TP_MAXV && V % 4 == 0) {
+        hipLaunchKernelGGL(top_p_lds_kernel, dim3(B), dim3(kSampThreads), (size_t)V * 4, s, src, (int)from_logits,
+                           temperature, V, top_p, uniforms, tok, tok_ld, write_col, out);
+        return hipGetLastError();
+    }
+    const float *probs = src;
+    if (from_logits) {
+        hipError_t e = launch_softmax_temp(src, B, V, temperature, probs_scratch, s);
+        if (e != hipSuccess) return e;
+        probs = probs_scratch;
+    }
+    return launch_top_p(probs, B, V, top_p, uniforms, tok, tok_ld, write_col, out, s);
 }
 
 hipError_t launch_set_int(int *dst, int v, hipStream_t s)
