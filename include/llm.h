@@ -130,6 +130,31 @@ int llm_prefill_d(llm_t *h, const int32_t *tokens_d, int32_t B, int32_t T);
 int llm_prefill_at(llm_t *h, int32_t start_pos, const int32_t *tokens, int32_t B, int32_t T);
 int llm_prefill_at_d(llm_t *h, int32_t start_pos, const int32_t *tokens_d, int32_t B, int32_t T);
 
+/* Varlen prefill (ragged prompts; nano-vllm notes, prefill with packed
+ * sequences and cumulative lengths): row b has lens[b] tokens (1 <= lens[b]
+ * <= max_seq_len, lens on the host), packed row after row in tokens
+ * (sum(lens) entries).  Each row runs at positions 0..lens[b]-1 with its own
+ * causal mask; writes KV [0, lens[b]) and token columns of row b, and leaves
+ * the logits of each row's last prompt position.  The handle then holds rows
+ * at different positions ("rows mode"): llm_sample writes column
+ * row_last[b] + 1 of row b, llm_decode_rows advances every row, and the
+ * uniform-position calls (llm_decode, llm_set_tokens, llm_prefill_at with an
+ * offset) return LLM_ESTATE until the next llm_prefill.  Host tokens are
+ * copied before the call returns. */
+int llm_prefill_varlen(llm_t *h, const int32_t *tokens, const int32_t *lens, int32_t B);
+int llm_prefill_varlen_d(llm_t *h, const int32_t *tokens_d, const int32_t *lens, int32_t B);
+
+/* One decode step in rows mode: row b runs the token in its column
+ * row_last[b] + 1 at that position (nano-vllm notes: decode with per-sequence
+ * context lengths) and leaves its logits.  Every row's next column must be
+ * written (llm_sample or llm_set_tokens_rows, else LLM_ESTATE) and below
+ * max_seq_len (else LLM_EINVAL).  Captured as a HIP graph per batch size. */
+int llm_decode_rows(llm_t *h);
+
+/* Rows mode: write tokens[b] into column row_last[b] + 1 of the rows mask
+ * selects (all when mask is NULL); host pointers. */
+int llm_set_tokens_rows(llm_t *h, const int32_t *tokens, const uint8_t *mask);
+
 /* One decode step (seqlen 1, no mask: the course notes on generate,
  * section 3): runs tok[:, prev_pos] at position prev_pos against cached keys
  * 0..prev_pos, writes the KV cache at prev_pos, leaves logits of position

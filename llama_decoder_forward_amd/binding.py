@@ -59,6 +59,10 @@ EXPORTS = {
     "llm_set_tokens": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
     "llm_set_tokens_d": (C.c_int, [_vp, C.c_int32, _vp, _vp]),
     "llm_prefill_at": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32, C.c_int32]),
+    "llm_prefill_varlen": (C.c_int, [_vp, _vp, _vp, C.c_int32]),
+    "llm_prefill_varlen_d": (C.c_int, [_vp, _vp, _vp, C.c_int32]),
+    "llm_decode_rows": (C.c_int, [_vp]),
+    "llm_set_tokens_rows": (C.c_int, [_vp, _vp, _vp]),
     "llm_prefill_at_d": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32, C.c_int32]),
     "llm_profile_decode": (C.c_int, [_vp, C.c_int32, C.c_int32, _vp]),
     "llm_profile_prefill": (C.c_int, [_vp, _vp, C.c_int32, C.c_int32, C.c_int32, _vp]),
@@ -156,6 +160,30 @@ class Handle:
     def prefill_at_d(self, start_pos: int, tokens_ptr: int, B: int, T: int):
         self._ck(_lib.llm_prefill_at_d(self.ptr, start_pos, C.c_void_p(tokens_ptr), B, T))
         self.B = B
+
+    def prefill_varlen(self, rows):
+        """rows: a list of 1-D token arrays of different lengths."""
+        lens = np.ascontiguousarray([len(r) for r in rows], dtype=np.int32)
+        packed = np.ascontiguousarray(np.concatenate([np.asarray(r, np.int32) for r in rows]))
+        self._ck(_lib.llm_prefill_varlen(self.ptr, packed.ctypes.data_as(C.c_void_p),
+                                         lens.ctypes.data_as(C.c_void_p), len(rows)))
+        self.B = len(rows)
+
+    def prefill_varlen_d(self, tokens_ptr: int, lens):
+        ln = np.ascontiguousarray(lens, dtype=np.int32)
+        self._ck(_lib.llm_prefill_varlen_d(self.ptr, C.c_void_p(tokens_ptr), ln.ctypes.data_as(C.c_void_p),
+                                           len(ln)))
+        self.B = len(ln)
+
+    def decode_rows(self):
+        self._ck(_lib.llm_decode_rows(self.ptr))
+
+    def set_tokens_rows(self, tokens, mask=None):
+        t, p = _arr(tokens, np.int32)
+        mp = None
+        if mask is not None:
+            m, mp = _arr(mask, np.uint8)
+        self._ck(_lib.llm_set_tokens_rows(self.ptr, p, mp))
 
     def decode(self, prev_pos: int):
         self._ck(_lib.llm_decode(self.ptr, prev_pos))

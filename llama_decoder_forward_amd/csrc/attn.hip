@@ -41,14 +41,15 @@ constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp(m_old 
 template <int NW, bool PF>
 __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
     const half_t *__restrict__ q, const half_t *__restrict__ kc, const half_t *__restrict__ vc,
-    int H, int Hkv, int S, const int *pos_dev, int pos_imm, half_t *__restrict__ out, int out_lay)
+    int H, int Hkv, int S, const int *pos_dev, int pos_imm, const int *pos_rows, half_t *__restrict__ out,
+    int out_lay)
 {
     constexpr int hd = 128;
     __shared__ floatx4 so[NW / 2][8][64];
     __shared__ float sm[NW / 2][16], sl[NW / 2][16];
     const int bk = blockIdx.x, b = bk / Hkv, kvh = bk % Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int L = (pos_dev ? *pos_dev : pos_imm) + 1;
+    const int L = (pos_rows ? pos_rows[b] : (pos_dev ? *pos_dev : pos_imm)) + 1;
     const int n_rep = H / Hkv;
     const int r = lane & 15, g = lane >> 4;
     const bool qv = r < n_rep;
@@ -206,14 +207,24 @@ constexpr int PF_Q = 128, PF_K = 64;
 
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restrict__ q,
                                                            const half_t *__restrict__ kc,
-                                                           const half_t *__restrict__ vc, int T, int p0,
-                                                           int H, int Hkv, int S,
+                                                           const half_t *__restrict__ vc, int Tu, int p0u,
+                                                           int H, int Hkv, int S, const int *cu,
                                                            half_t *__restrict__ out, int out_lay)
 {
     const int hd = 128;
     __shared__ half8 kl[PF_K * hd / 8];  // 4 sub-tiles x 4 d-steps x 64 lanes
     __shared__ half8 vl[PF_K * hd / 8];  // 8 d-tiles x 2 key-steps x 64 lanes
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    // uniform rows: T = Tu tokens at p0u..; varlen: row b's T tokens are the
+    // packed rows cu[b].. at positions 0..
+    int T = Tu, p0 = p0u;
+    int64_t rbase = (int64_t)b * Tu;
+    if (cu) {
+        rbase = cu[b];
+        T = cu[b + 1] - cu[b];
+        p0 = 0;
+    }
+    if ((int)blockIdx.y * PF_Q >= T) return;  // a query tile past this row's end (whole work-group)
     const int kvh = h / (H / Hkv);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
@@ -226,7 +237,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
 #pragma unroll
     for (int c = 0; c < 2; c++) {
         const int t = wq0 + 16 * c + r;
-        const half_t *qrow = q + (((int64_t)b * T + (t < T ? t : 0)) * H + h) * hd;
+        const half_t *qrow = q + ((rbase + (t < T ? t : 0)) * H + h) * hd;
 #pragma unroll
         for (int s = 0; s < 4; s++)
             qb[c][s] = t < T ? *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g) : z;
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
         const int t = wq0 + 16 * c + r;
         if (t >= T) continue;
         const float inv = 1.0f / lrun[c];
-        half_t *orow = out + (((int64_t)b * T + t) * H + h) * hd;
+        half_t *orow = out + ((rbase + t) * H + h) * hd;
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) {
             half4 o;
@@ -356,7 +367,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
             for (int i = 0; i < 4; i++) o[i] = (half_t)(acc[c][dt][i] * inv);
             const int col = 16 * dt + 4 * g;  // 4 consecutive columns inside one 8-column group
             if (out_lay)
-                *reinterpret_cast<half4 *>(out + act_offset(b * T + t, (int64_t)h * hd + col, (int64_t)H * hd, 0, out_lay)) = o;
+                *reinterpret_cast<half4 *>(out + act_offset((int)(rbase + t), (int64_t)h * hd + col, (int64_t)H * hd, 0, out_lay)) = o;
             else
                 *reinterpret_cast<half4 *>(orow + col) = o;
         }
@@ -367,14 +378,24 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
 // fp32 models (small): one work-group per (b, h, query), scores in LDS.
 // ---------------------------------------------------------------------------
 __global__ void attn_f32_kernel(const float *q, const float *kc, const float *vc, int T, int H,
-                                int Hkv, int hd, int S, const int *pos_dev, int pos_imm, float *out)
+                                int Hkv, int hd, int S, const int *pos_dev, int pos_imm, const int *pos_rows,
+                                const int *cu, float *out)
 {
     extern __shared__ float sh[];  // L scores
     const int bh = blockIdx.x, b = bh / H, h = bh % H, t = blockIdx.y;
     const int kvh = h / (H / Hkv);
-    const int pos = (pos_dev ? *pos_dev : pos_imm) + t;
+    // query row and position: uniform rows, per-row decode positions, or
+    // varlen rows packed at cu[b].. (positions 0..)
+    int64_t row = (int64_t)b * T + t;
+    int pos = (pos_dev ? *pos_dev : pos_imm) + t;
+    if (pos_rows) pos = pos_rows[b];
+    if (cu) {
+        if (t >= cu[b + 1] - cu[b]) return;  // whole work-group
+        row = cu[b] + t;
+        pos = t;
+    }
     const int L = pos + 1;
-    const float *qr = q + (((int64_t)b * T + t) * H + h) * hd;
+    const float *qr = q + (row * H + h) * hd;
     const float *K = kc + ((int64_t)b * Hkv + kvh) * S * hd;
     const float *V = vc + ((int64_t)b * Hkv + kvh) * hd * S;
     const float scale = 1.0f / sqrtf((float)hd);
@@ -391,7 +412,7 @@ __global__ void attn_f32_kernel(const float *q, const float *kc, const float *vc
     for (int d = threadIdx.x; d < hd; d += blockDim.x) {
         float o = 0.f;
         for (int j = 0; j < L; j++) o = fmaf(expf(sh[j] - mx) / sum, V[(int64_t)d * S + j], o);
-        out[(((int64_t)b * T + t) * H + h) * hd + d] = o;
+        out[(row * H + h) * hd + d] = o;
     }
 }
 
@@ -423,13 +444,13 @@ hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s)
     half_t *o = (half_t *)a.out;
     if (pairs >= 512)
         hipLaunchKernelGGL((attn_decode_kernel<2, true>), dim3(pairs), dim3(128), 0, s, q, kc, vc, a.H, a.Hkv, a.S,
-                           a.pos_dev, a.pos_imm, o, a.out_lay);
+                           a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
     else if (pairs >= 128)
         hipLaunchKernelGGL((attn_decode_kernel<4, false>), dim3(pairs), dim3(256), 0, s, q, kc, vc, a.H, a.Hkv, a.S,
-                           a.pos_dev, a.pos_imm, o, a.out_lay);
+                           a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
     else
         hipLaunchKernelGGL((attn_decode_kernel<8, false>), dim3(pairs), dim3(512), 0, s, q, kc, vc, a.H, a.Hkv, a.S,
-                           a.pos_dev, a.pos_imm, o, a.out_lay);
+                           a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
     return hipGetLastError();
 }
 
@@ -438,7 +459,7 @@ hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s)
     if (a.out_lay != ACT_ROWS && a.out_lay != ACT_TILED) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.B * a.H, (a.T + PF_Q - 1) / PF_Q), dim3(256), 0,
                        s, (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache,
-                       a.T, a.pos_imm, a.H, a.Hkv, a.S, (half_t *)a.out, a.out_lay);
+                       a.T, a.pos_imm, a.H, a.Hkv, a.S, a.cu, (half_t *)a.out, a.out_lay);
     return hipGetLastError();
 }
 
@@ -447,7 +468,7 @@ hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s)
     size_t sh = sizeof(float) * (size_t)a.S;
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.B * a.H, a.T), dim3(64), sh, s, (const float *)a.q,
                        (const float *)a.kcache, (const float *)a.vcache, a.T, a.H, a.Hkv, a.hd,
-                       a.S, a.pos_dev, a.pos_imm, (float *)a.out);
+                       a.S, a.pos_dev, a.pos_imm, a.pos_rows, a.cu, (float *)a.out);
     return hipGetLastError();
 }
 

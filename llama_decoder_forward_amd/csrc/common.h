@@ -65,6 +65,26 @@ __host__ __device__ inline int64_t act_offset(int m, int64_t k, int64_t K, int64
     return (int64_t)m * ld + k;
 }
 
+// Where activation row m of a forward pass sits (batch row b, position pos):
+//  - packed rows of different lengths (varlen prefill): rowmap[m] = {b, pos};
+//  - per-row decode positions (T == 1): b = m, pos = pos_rows[m];
+//  - otherwise b = m / T and pos = base + m % T, base = *pos_dev or pos_imm.
+__device__ __forceinline__ void locate_row(int m, int T, const int *pos_dev, int pos_imm, const int *pos_rows,
+                                           const int2 *rowmap, int &b, int &pos)
+{
+    if (rowmap) {
+        const int2 r = rowmap[m];
+        b = r.x;
+        pos = r.y;
+    } else if (pos_rows) {
+        b = m;
+        pos = pos_rows[m];
+    } else {
+        b = m / T;
+        pos = (pos_dev ? *pos_dev : pos_imm) + m % T;
+    }
+}
+
 // Packed matrices of one layer, in stored row order.
 enum Mat { MAT_QKV = 0, MAT_O = 1, MAT_W13 = 2, MAT_W2 = 3, MAT_HEAD = 4, MAT_EMB = 5 };
 
@@ -89,6 +109,8 @@ struct Epilogue {
     const int *pos_dev;   // device position of token 0 (decode) or NULL
     int pos_imm;          // position of token 0 when pos_dev is NULL
     int T;                // tokens per batch row (m = b*T + t)
+    const int *pos_rows;  // per-row decode positions, or NULL (locate_row)
+    const int2 *rowmap;   // packed varlen rows {b, pos}, or NULL (locate_row)
     int H, Hkv, hd, S;
     int out_lay;          // EP_SWIGLU: layout of g (ACT_ROWS with ldo, 1/2 fragment-major, ACT_TILED)
 };
@@ -123,8 +145,12 @@ hipError_t launch_read_weights(const void *src, int dtype, int mat, int64_t N, i
                                int which, int H, int Hkv, int hd, int F, int64_t first,
                                int64_t count, void *out, hipStream_t s);
 
-hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int B, int T,
-                        const int *pos_dev, int pos0, int D, int dtype, void *x, hipStream_t s);
+// M rows: row m embeds tok[b][pos] with (b, pos) from locate_row.
+hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int M, int T,
+                        const int *pos_dev, int pos0, const int *pos_rows, const int2 *rowmap, int D,
+                        int dtype, void *x, hipStream_t s);
+// out[i] = x[idx[i]] for n rows of D elements (es bytes each)
+hipError_t launch_gather_rows(const void *x, const int *idx, int n, int D, int es, void *out, hipStream_t s);
 // y_lay: layout of y (fp16 only for non-row-major layouts).
 hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int D, float eps,
                           int dtype, void *y, hipStream_t s, int y_lay = ACT_ROWS);
@@ -141,6 +167,9 @@ struct AttnArgs {
     const int *pos_dev;    // decode: device position, else NULL
     int pos_imm;
     int out_lay;           // layout of out as [B*T][H*hd] rows (fp16)
+    const int *pos_rows;   // decode with per-row positions (T == 1), or NULL
+    const int *cu;         // varlen prefill: row b's queries are packed rows cu[b]..cu[b+1]-1
+                           // at positions 0..; T is then the longest row; or NULL
 };
 hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s);
@@ -148,19 +177,29 @@ hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_kv_write(const void *k, const void *v, int B, int T, int pos0, int Hkv, int hd,
                            int S, int dtype, void *kcache, void *vcache, hipStream_t s);
 
+// Samplers write token column write_col of every row, or with col_rows
+// column col_rows[b] + 1 of row b (none when that reaches tok_ld).
 hipError_t launch_argmax(const float *logits, int B, int V, int32_t *tok, int64_t tok_ld,
-                         int write_col, int32_t *out, hipStream_t s);
+                         int write_col, const int *col_rows, int32_t *out, hipStream_t s);
 hipError_t launch_softmax_temp(const float *logits, int B, int V, float temperature,
                                float *probs, hipStream_t s);
 hipError_t launch_top_p(const float *probs, int B, int V, float top_p, const float *uniforms,
-                        int32_t *tok, int64_t tok_ld, int write_col, int32_t *out,
+                        int32_t *tok, int64_t tok_ld, int write_col, const int *col_rows, int32_t *out,
                         hipStream_t s);
 // Temperature softmax (from_logits) and top-p in one launch for V <= 32768,
 // else the two-launch path through probs_scratch[B][V].
 hipError_t launch_sample_top_p(const float *src, bool from_logits, float temperature, int B, int V, float top_p,
-                               const float *uniforms, int32_t *tok, int64_t tok_ld, int write_col, int32_t *out,
-                               float *probs_scratch, hipStream_t s);
+                               const float *uniforms, int32_t *tok, int64_t tok_ld, int write_col,
+                               const int *col_rows, int32_t *out, float *probs_scratch, hipStream_t s);
 hipError_t launch_set_int(int *dst, int v, hipStream_t s);
+// dst[i] += 1 for i < n
+hipError_t launch_inc_ints(int *dst, int n, hipStream_t s);
+// tok[b][col_rows[b] + 1] = vals[b] for the rows mask selects (all when NULL)
+hipError_t launch_set_tokens_rows(int32_t *tok, int64_t tok_ld, int B, const int *col_rows, const int32_t *vals,
+                                  const uint8_t *mask, hipStream_t s);
+// packed varlen tokens vals[m] -> tok[b][pos] with rowmap[m] = {b, pos}
+hipError_t launch_scatter_tokens(int32_t *tok, int64_t tok_ld, int M, const int2 *rowmap, const int32_t *vals,
+                                 hipStream_t s);
 hipError_t launch_set_tokens(int32_t *tok, int64_t tok_ld, int B, int col, const int32_t *vals,
                              const uint8_t *mask, hipStream_t s);
 

@@ -61,8 +61,8 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
     case EP_QKV: {
         if (!valid) break;
         const int hd = ep.hd, qrows = ep.H * hd, krows = ep.Hkv * hd;
-        const int pos = (ep.pos_dev ? *ep.pos_dev : ep.pos_imm) + m % ep.T;
-        const int b = m / ep.T;
+        int b, pos;
+        locate_row(m, ep.T, ep.pos_dev, ep.pos_imm, ep.pos_rows, ep.rowmap, b, pos);
         if (n < qrows + krows) {
             const int d0 = n % hd;  // multiple of 4: pairs (d0, d0+1), (d0+2, d0+3)
             const float *cs = ep.rope + ((int64_t)pos * (hd / 2) + d0 / 2) * 2;
@@ -559,7 +559,8 @@ __global__ void linear_f32_kernel(const float *W, const float *X, int64_t ldx, i
         const int n = 2 * unit;
         if (n >= N) return;
         const int hd = ep.hd, qrows = ep.H * hd, krows = ep.Hkv * hd;
-        const int pos = (ep.pos_dev ? *ep.pos_dev : ep.pos_imm) + m % ep.T, b = m / ep.T;
+        int b, pos;
+        locate_row(m, ep.T, ep.pos_dev, ep.pos_imm, ep.pos_rows, ep.rowmap, b, pos);
         float a = dot_row_f32(W + (int64_t)n * K, x, K);
         float bb = dot_row_f32(W + (int64_t)(n + 1) * K, x, K);
         if (n < qrows + krows) {

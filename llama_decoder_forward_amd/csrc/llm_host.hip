@@ -92,18 +92,29 @@ struct llm {
     int32_t *outtok = nullptr, *stage_i32 = nullptr;
     uint8_t *stage_mask = nullptr;
     int *pos_dev = nullptr;
+    int *pos_rows = nullptr;  // [maxB] per-row last written position (rows mode)
+    int *cu = nullptr;        // [maxB + 1] varlen row starts, then [maxB] last packed rows
     // activations, sized for ws_rows rows
     char *ws = nullptr;
     int64_t ws_rows = 0;
     char *x = nullptr, *xn = nullptr, *q = nullptr, *o = nullptr, *g = nullptr;
-    // state
+    int2 *rowmap = nullptr;   // varlen prefill: {b, pos} per packed row
+    int32_t *vtok = nullptr;  // varlen prefill: packed tokens
+    // state.  Uniform mode: every row at last_pos.  Rows mode (after a varlen
+    // prefill): row b at row_last[b], its next token column written when
+    // row_next[b] is set.
     bool prefilled = false, logits_valid = false, poisoned = false;
     int cur_B = 0, last_pos = -1;
     std::vector<uint8_t> col_written;
+    bool rows_mode = false;
+    std::vector<int> row_last;
+    std::vector<uint8_t> row_next;
     std::string err;
-    // decode graph
+    // decode graphs (uniform positions / per-row positions)
     hipGraphExec_t gexec = nullptr;
     int graph_B = -1;
+    hipGraphExec_t gexec_rows = nullptr;
+    int graph_rows_B = -1;
     bool use_graph = true;
 };
 
@@ -161,19 +172,27 @@ int ensure_ws(llm_t *h, int64_t rows)
         h->ws_rows = 0;
     }
     void *p = nullptr;
-    HIPM(h, hipMalloc(&p, 2 * bx + 2 * bq + bg));
+    const int64_t br = align256(rows * (int64_t)sizeof(int2)), bt = align256(rows * 4);
+    HIPM(h, hipMalloc(&p, 2 * bx + 2 * bq + bg + br + bt));
     h->ws = (char *)p;
     h->x = h->ws;
     h->xn = h->x + bx;
     h->q = h->xn + bx;
     h->o = h->q + bq;
     h->g = h->o + bq;
+    h->rowmap = (int2 *)(h->g + bg);
+    h->vtok = (int32_t *)((char *)h->rowmap + br);
     h->ws_rows = rows;
-    // the captured decode graph holds the old addresses
+    // the captured decode graphs hold the old addresses
     if (h->gexec) {
         (void)hipGraphExecDestroy(h->gexec);
         h->gexec = nullptr;
         h->graph_B = -1;
+    }
+    if (h->gexec_rows) {
+        (void)hipGraphExecDestroy(h->gexec_rows);
+        h->gexec_rows = nullptr;
+        h->graph_rows_B = -1;
     }
     return LLM_OK;
 }
@@ -232,6 +251,34 @@ hipError_t run_linear(llm_t *h, int layer, int mat, const void *X, int64_t ldx, 
 // writing xn and the product on xn.
 bool fuse_norm(const llm_t *h, int M) { return h->d.dtype == LLM_F16 && skinny_can_normalise(M, h->d.D); }
 
+// One forward pass: B batch rows, M activation rows.
+//  - uniform prefill: T tokens per row at pos0.. (M = B*T);
+//  - decode (T = 1): position from pos_dev (all rows) or pos_rows (per row);
+//  - varlen prefill: rows of different lengths packed (M = their sum),
+//    rowmap gives {b, pos} per packed row, cu the row starts, last_rows the
+//    packed index of each row's last token, Tmax the longest row.
+struct Pass {
+    int B = 0, T = 1, M = 0;
+    const int *pos_dev = nullptr;
+    int pos0 = 0;
+    const int *pos_rows = nullptr;
+    const int2 *rowmap = nullptr;
+    const int *cu = nullptr, *last_rows = nullptr;
+    int Tmax = 0;
+    bool decode() const { return pos_dev || pos_rows; }
+};
+
+Pass uniform_pass(int B, int T, const int *pos_dev, int pos0 = 0)
+{
+    Pass p;
+    p.B = B;
+    p.T = T;
+    p.M = B * T;
+    p.pos_dev = pos_dev;
+    p.pos0 = pos0;
+    return p;
+}
+
 // Layout of the activations a forward pass hands to its layer products
 // (normalised rows, attention output, SwiGLU output): decode steps of 3..32
 // fp16 rows use the fragment-major layout (row halves of 16), fp16 prefills
@@ -239,11 +286,11 @@ bool fuse_norm(const llm_t *h, int M) { return h->d.dtype == LLM_F16 && skinny_c
 // Row-major always for the output head, whose M is the batch.
 constexpr int kTiledMinRows = 1024;  // the 256 x 256 product takes M >= 1024
 
-int act_layout(const llm_t *h, int B, int T, const int *pos_dev)
+int act_layout(const llm_t *h, const Pass &ps)
 {
     if (h->d.dtype != LLM_F16) return ACT_ROWS;
-    if (pos_dev && T == 1) return B > 2 && B <= 32 ? (B + 15) / 16 : ACT_ROWS;
-    if (!pos_dev && (int64_t)B * T >= kTiledMinRows) return ACT_TILED;
+    if (ps.decode()) return ps.B > 2 && ps.B <= 32 ? (ps.B + 15) / 16 : ACT_ROWS;
+    if (ps.M >= kTiledMinRows) return ACT_TILED;
     return ACT_ROWS;
 }
 
@@ -299,21 +346,35 @@ hipError_t prof_end(Prof *pf, hipStream_t s)
 // (SwiGLU), or the output head on the last position of each row (fp32
 // logits).  With `fused` the RMSNorm in front of wq|wk|wv, w1|w3 and the
 // head runs inside the product on x; otherwise the product reads xn.
-hipError_t product(llm_t *h, int l, int mat, int B, int T, const int *pos_dev, bool fused, int pos0 = 0)
+// The row-major input of the output head: the last position of each row
+// (uniform rows: every T-th row of x; varlen: gathered into q by forward).
+const char *head_rows(llm_t *h, const Pass &ps, int64_t *ld)
+{
+    if (ps.rowmap) {
+        *ld = h->d.D;
+        return h->q;
+    }
+    *ld = (int64_t)ps.T * h->d.D;
+    return h->x + (int64_t)(ps.T - 1) * h->d.D * h->d.es;
+}
+
+hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused)
 {
     const Dims &d = h->d;
-    const int M = B * T;
+    const int M = ps.M;
     const int64_t qd = (int64_t)d.H * d.hd;
-    const int lay = act_layout(h, B, T, pos_dev);
+    const int lay = act_layout(h, ps);
     switch (mat) {
     case MAT_QKV: {
         Epilogue eq = make_ep(EP_QKV, h->q, qd);
         eq.kcache = layer_kc(h, l);
         eq.vcache = layer_vc(h, l);
         eq.rope = h->rope;
-        eq.pos_dev = pos_dev;
-        eq.pos_imm = pos0;
-        eq.T = T;
+        eq.pos_dev = ps.pos_dev;
+        eq.pos_imm = ps.pos0;
+        eq.pos_rows = ps.pos_rows;
+        eq.rowmap = ps.rowmap;
+        eq.T = ps.T;
         eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = d.S;
         const char *nw = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
         return fused ? run_linear(h, l, MAT_QKV, h->x, d.D, M, eq, nw)
@@ -330,22 +391,22 @@ hipError_t product(llm_t *h, int l, int mat, int B, int T, const int *pos_dev, b
     case MAT_W2: return run_linear(h, l, MAT_W2, h->g, d.F, M, make_ep(EP_RESID, h->x, d.D), nullptr, lay);
     default: {
         const char *nw = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
-        const char *xlast = h->x + (int64_t)(T - 1) * d.D * d.es;
+        int64_t ld = 0;
+        const char *xl = head_rows(h, ps, &ld);
         Epilogue el = make_ep(EP_LOGITS, h->logits, d.V);
-        return fused ? run_linear(h, 0, MAT_HEAD, xlast, (int64_t)T * d.D, B, el, nw)
-                     : run_linear(h, 0, MAT_HEAD, h->xn, d.D, B, el, nullptr, head_layout(lay));
+        return fused ? run_linear(h, 0, MAT_HEAD, xl, ld, ps.B, el, nw)
+                     : run_linear(h, 0, MAT_HEAD, h->xn, d.D, ps.B, el, nullptr, head_layout(lay));
     }
     }
 }
 
-// The forward pass over B rows of T tokens (walkthrough sections 2, 3.5-3.8)
-// at positions pos0..pos0+T-1.  Decode (pos_dev != NULL, T == 1) reads its
-// position from device memory so that the launch sequence can be captured
-// once and replayed.
-hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullptr, int pos0 = 0)
+// The forward pass (walkthrough sections 2, 3.5-3.8) described by ps.
+// Decode positions come from device memory so that the launch sequence can
+// be captured once and replayed.
+hipError_t forward(llm_t *h, const Pass &ps, Prof *pf = nullptr)
 {
     const Dims &d = h->d;
-    const int M = B * T;
+    const int M = ps.M, B = ps.B;
     hipStream_t s = h->stream;
     hipError_t e;
 #define TRY_RAW(x)                    \
@@ -359,39 +420,44 @@ hipError_t forward(llm_t *h, int B, int T, const int *pos_dev, Prof *pf = nullpt
         TRY_RAW(x);                        \
         TRY_RAW(prof_end(pf, s));          \
     } while (0)
-    TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, B, T, pos_dev, pos0, d.D, d.dtype, h->x, s));
+    TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, M, ps.T, ps.pos_dev, ps.pos0, ps.pos_rows, ps.rowmap, d.D,
+                                d.dtype, h->x, s));
     const bool fused = fuse_norm(h, M);
-    const int lay = act_layout(h, B, T, pos_dev);
+    const int lay = act_layout(h, ps);
     for (int l = 0; l < d.NL; l++) {
         const char *nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
         const char *nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
         // attention_norm -> wq|wk|wv with RoPE and the KV-cache write
         if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay));
-        TRYC(PC_QKV, product(h, l, MAT_QKV, B, T, pos_dev, fused, pos0));
+        TRYC(PC_QKV, product(h, l, MAT_QKV, ps, fused));
         // attention over the cache
         AttnArgs aa{};
         aa.q = h->q; aa.kcache = layer_kc(h, l); aa.vcache = layer_vc(h, l); aa.out = h->o;
-        aa.B = B; aa.T = T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
-        aa.pos_dev = pos_dev; aa.pos_imm = pos0;
+        aa.B = B; aa.T = ps.rowmap ? ps.Tmax : ps.T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
+        aa.pos_dev = ps.pos_dev; aa.pos_imm = ps.pos0;
+        aa.pos_rows = ps.pos_rows;
+        aa.cu = ps.cu;
         aa.out_lay = lay;
         if (d.dtype == LLM_F32) TRYC(PC_ATTN, launch_attn_f32(aa, s));
-        else if (pos_dev) TRYC(PC_ATTN, launch_attn_decode_f16(aa, s));
+        else if (ps.decode()) TRYC(PC_ATTN, launch_attn_decode_f16(aa, s));
         else TRYC(PC_ATTN, launch_attn_prefill_f16(aa, s));
         // wo + residual
-        TRYC(PC_O, product(h, l, MAT_O, B, T, pos_dev, fused));
+        TRYC(PC_O, product(h, l, MAT_O, ps, fused));
         // ffn_norm -> w1|w3 with SwiGLU -> w2 + residual
         if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_ffn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay));
-        TRYC(PC_W13, product(h, l, MAT_W13, B, T, pos_dev, fused));
-        TRYC(PC_W2, product(h, l, MAT_W2, B, T, pos_dev, fused));
+        TRYC(PC_W13, product(h, l, MAT_W13, ps, fused));
+        TRYC(PC_W2, product(h, l, MAT_W2, ps, fused));
     }
     // final norm on the last position of each row, output head, fp32 logits
+    if (ps.rowmap) TRYC(PC_HEAD, launch_gather_rows(h->x, ps.last_rows, B, d.D, d.es, h->q, s));
     const bool fused_head = fuse_norm(h, B);
     if (!fused_head) {
         const char *nw_final = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
-        const char *xlast = h->x + (int64_t)(T - 1) * d.D * d.es;
-        TRYC(PC_NORM, launch_rmsnorm(xlast, (int64_t)T * d.D, nw_final, B, d.D, h->p.norm_eps, d.dtype, h->xn, s, head_layout(lay)));
+        int64_t ld = 0;
+        const char *xl = head_rows(h, ps, &ld);
+        TRYC(PC_NORM, launch_rmsnorm(xl, ld, nw_final, B, d.D, h->p.norm_eps, d.dtype, h->xn, s, head_layout(lay)));
     }
-    TRYC(PC_HEAD, product(h, 0, MAT_HEAD, B, T, pos_dev, fused_head));
+    TRYC(PC_HEAD, product(h, 0, MAT_HEAD, ps, fused_head));
 #undef TRYC
 #undef TRY_RAW
     return hipSuccess;
@@ -489,12 +555,14 @@ int create_impl(llm_t *h, uint64_t seed)
     h->logits = (float *)p;
     HIPM(h, hipMalloc(&p, (int64_t)d.maxB * d.V * sizeof(float)));
     h->probs = (float *)p;
-    HIPM(h, hipMalloc(&p, 256 + (int64_t)d.maxB * (sizeof(float) + 2 * sizeof(int32_t) + 1)));
+    HIPM(h, hipMalloc(&p, 256 + (int64_t)d.maxB * (sizeof(float) + 5 * sizeof(int32_t) + 1) + 16));
     h->pos_dev = (int *)p;
     h->uni = (float *)((char *)p + 64);
     h->outtok = (int32_t *)(h->uni + d.maxB);
     h->stage_i32 = h->outtok + d.maxB;
-    h->stage_mask = (uint8_t *)(h->stage_i32 + d.maxB);
+    h->pos_rows = h->stage_i32 + d.maxB;
+    h->cu = h->pos_rows + d.maxB;  // maxB + 1 starts, then maxB last rows
+    h->stage_mask = (uint8_t *)(h->cu + 2 * d.maxB + 1);
     int rc = ensure_ws(h, d.maxB);
     if (rc) return rc;
     rc = build_weights(h, seed);
@@ -506,6 +574,7 @@ int create_impl(llm_t *h, uint64_t seed)
 void release(llm_t *h)
 {
     if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
+    if (h->gexec_rows) (void)hipGraphExecDestroy(h->gexec_rows);
     void *bufs[] = {h->wts, h->emb, h->norm_w, h->kv, h->rope, h->tok, h->logits, h->probs,
                     h->pos_dev, h->ws};
     for (void *b : bufs)
@@ -531,12 +600,13 @@ int prefill_common(llm_t *h, int B, int T, int start = 0)
     if (!h->dry) {
         int rc = ensure_ws(h, (int64_t)B * T);
         if (rc) return rc;
-        hipError_t e = forward(h, B, T, nullptr, nullptr, start);
+        hipError_t e = forward(h, uniform_pass(B, T, nullptr, start));
         rc = after_forward(h, e);
         if (rc) return rc;
     }
     h->prefilled = true;
     h->logits_valid = true;
+    h->rows_mode = false;
     h->cur_B = B;
     h->last_pos = start + T - 1;
     if (start == 0) std::fill(h->col_written.begin(), h->col_written.end(), 0);
@@ -551,6 +621,7 @@ int check_prefill_args(llm_t *h, int B, int T, int start = 0)
     if (T < 1 || (int64_t)start + T > h->d.S) return fail(h, LLM_EINVAL, "need 1 <= T and start_pos + T <= max_seq_len");
     if (start > 0) {
         if (!h->prefilled) return fail(h, LLM_ESTATE, "prefill at an offset needs the cache prefix of an earlier prefill");
+        if (h->rows_mode) return fail(h, LLM_ESTATE, "prefill at an offset needs rows at one position (not after a varlen prefill)");
         if (B != h->cur_B) return fail(h, LLM_ESTATE, "prefill at an offset must keep the batch of the cache prefix");
         if (start > h->last_pos + 1) return fail(h, LLM_ESTATE, "start_pos skips positions whose KV is not written");
     }
@@ -567,19 +638,91 @@ int sample_common(llm_t *h, float temperature, float top_p, const float *uniform
         if (!(top_p > 0.f && top_p <= 1.f)) return fail(h, LLM_EINVAL, "top_p must be in (0, 1]");
         if (!have_u) return fail(h, LLM_EINVAL, "uniforms are required when temperature > 0");
     }
+    // uniform rows write column last_pos + 1; rows mode column row_last[b] + 1
     const int col = h->last_pos + 1 < d.S ? h->last_pos + 1 : -1;
+    const int *col_rows = h->rows_mode ? h->pos_rows : nullptr;
     if (!h->dry) {
         hipError_t e;
         if (temperature <= 0.f) {
-            e = launch_argmax(h->logits, h->cur_B, d.V, h->tok, d.S, col, out_d, h->stream);
+            e = launch_argmax(h->logits, h->cur_B, d.V, h->tok, d.S, col, col_rows, out_d, h->stream);
         } else {
             e = launch_sample_top_p(h->logits, true, temperature, h->cur_B, d.V, top_p, uniforms_d, h->tok, d.S,
-                                    col, out_d, h->probs, h->stream);
+                                    col, col_rows, out_d, h->probs, h->stream);
         }
         int rc = after_forward(h, e);
         if (rc) return rc;
     }
-    if (col >= 0) h->col_written[col] = 1;
+    if (h->rows_mode) {
+        for (int b = 0; b < h->cur_B; b++)
+            if (h->row_last[b] + 1 < d.S) h->row_next[b] = 1;
+    } else if (col >= 0) {
+        h->col_written[col] = 1;
+    }
+    return LLM_OK;
+}
+
+// Varlen prefill: validate lengths, build the packed-row map on the host.
+int prep_varlen(llm_t *h, const int32_t *lens, int B, std::vector<int2> &rowmap, std::vector<int> &cu_last,
+                int *Mout, int *Tmax)
+{
+    if (B < 1 || B > h->d.maxB) return fail(h, LLM_EINVAL, "B must be in [1, max_batch_size]");
+    if (!lens) return fail(h, LLM_EINVAL, "lens is NULL");
+    int64_t M = 0;
+    int tmax = 0;
+    for (int b = 0; b < B; b++) {
+        if (lens[b] < 1 || lens[b] > h->d.S) return fail(h, LLM_EINVAL, "every length must be in [1, max_seq_len]");
+        M += lens[b];
+        tmax = std::max(tmax, (int)lens[b]);
+    }
+    rowmap.resize(M);
+    cu_last.assign(2 * B + 1, 0);  // B + 1 starts, then B last rows
+    int64_t m = 0;
+    for (int b = 0; b < B; b++) {
+        cu_last[b] = (int)m;
+        for (int t = 0; t < lens[b]; t++, m++) rowmap[m] = make_int2(b, t);
+        cu_last[B + 1 + b] = (int)m - 1;
+    }
+    cu_last[B] = (int)m;
+    *Mout = (int)M;
+    *Tmax = tmax;
+    return LLM_OK;
+}
+
+// The forward of a varlen prefill whose packed tokens are in h->vtok.
+int varlen_common(llm_t *h, const int32_t *lens, int B, const std::vector<int2> &rowmap,
+                  const std::vector<int> &cu_last, int M, int Tmax)
+{
+    if (!h->dry) {
+        int rc = ensure_ws(h, M);  // (callers run it before staging tokens as well)
+        if (rc) return rc;
+        HIPC(h, hipMemcpyAsync(h->rowmap, rowmap.data(), (size_t)M * sizeof(int2), hipMemcpyHostToDevice, h->stream));
+        HIPC(h, hipMemcpyAsync(h->cu, cu_last.data(), cu_last.size() * sizeof(int), hipMemcpyHostToDevice, h->stream));
+        std::vector<int> last(B);
+        for (int b = 0; b < B; b++) last[b] = lens[b] - 1;
+        HIPC(h, hipMemcpyAsync(h->pos_rows, last.data(), (size_t)B * sizeof(int), hipMemcpyHostToDevice, h->stream));
+        HIPC(h, launch_scatter_tokens(h->tok, h->d.S, M, h->rowmap, h->vtok, h->stream));
+        Pass ps;
+        ps.B = B;
+        ps.M = M;
+        ps.T = 1;
+        ps.rowmap = h->rowmap;
+        ps.cu = h->cu;
+        ps.last_rows = h->cu + B + 1;
+        ps.Tmax = Tmax;
+        rc = after_forward(h, forward(h, ps));
+        if (rc) return rc;
+        HIPC(h, hipStreamSynchronize(h->stream));  // host copies of rowmap / lengths go out of scope
+    }
+    h->prefilled = true;
+    h->logits_valid = true;
+    h->rows_mode = true;
+    h->cur_B = B;
+    h->last_pos = -1;
+    std::fill(h->col_written.begin(), h->col_written.end(), 0);
+    for (int b = 0; b < h->d.maxB; b++) {
+        h->row_last[b] = b < B ? lens[b] - 1 : -1;
+        h->row_next[b] = 0;
+    }
     return LLM_OK;
 }
 
@@ -604,7 +747,7 @@ int profiled_forward(llm_t *h, int B, int T, int prev_pos, int reps, float *ms_o
             e = launch_set_int(h->pos_dev, prev_pos, h->stream);
             pos = h->pos_dev;
         }
-        if (e == hipSuccess) e = forward(h, B, T, pos, &pf);
+        if (e == hipSuccess) e = forward(h, uniform_pass(B, T, pos), &pf);
         if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
         for (size_t i = 0; e == hipSuccess && i + 1 < pf.used; i += 2) {
             float ms = 0.f;
@@ -653,6 +796,8 @@ static llm_t *new_handle(const llm_params *p, const Dims &d)
     h->p = *p;
     h->d = d;
     h->col_written.assign(d.S, 0);
+    h->row_last.assign(d.maxB, -1);
+    h->row_next.assign(d.maxB, 0);
     const char *ng = std::getenv("LLM_NO_GRAPH");
     h->use_graph = !(ng && ng[0] == '1');
     return h;
@@ -772,11 +917,117 @@ int llm_prefill_at_d(llm_t *h, int32_t start_pos, const int32_t *tokens_d, int32
     return prefill_common(h, B, T, start_pos);
 }
 
+int llm_prefill_varlen(llm_t *h, const int32_t *tokens, const int32_t *lens, int32_t B)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    std::vector<int2> rowmap;
+    std::vector<int> cu_last;
+    int M = 0, Tmax = 0;
+    if ((rc = prep_varlen(h, lens, B, rowmap, cu_last, &M, &Tmax))) return rc;
+    if (!tokens) return fail(h, LLM_EINVAL, "tokens is NULL");
+    if (!tokens_ok(tokens, M, h->d.V)) return fail(h, LLM_EINVAL, "token id out of [0, vocab)");
+    if (!h->dry) {
+        if ((rc = ensure_ws(h, M))) return rc;
+        HIPC(h, hipMemcpyAsync(h->vtok, tokens, (size_t)M * 4, hipMemcpyHostToDevice, h->stream));
+    }
+    return varlen_common(h, lens, B, rowmap, cu_last, M, Tmax);
+}
+
+int llm_prefill_varlen_d(llm_t *h, const int32_t *tokens_d, const int32_t *lens, int32_t B)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    std::vector<int2> rowmap;
+    std::vector<int> cu_last;
+    int M = 0, Tmax = 0;
+    if ((rc = prep_varlen(h, lens, B, rowmap, cu_last, &M, &Tmax))) return rc;
+    if (!tokens_d) return fail(h, LLM_EINVAL, "tokens is NULL");
+    if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    if ((rc = ensure_ws(h, M))) return rc;
+    HIPC(h, hipMemcpyAsync(h->vtok, tokens_d, (size_t)M * 4, hipMemcpyDeviceToDevice, h->stream));
+    return varlen_common(h, lens, B, rowmap, cu_last, M, Tmax);
+}
+
+int llm_decode_rows(llm_t *h)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!h->prefilled || !h->rows_mode) return fail(h, LLM_ESTATE, "per-row decode needs a varlen prefill first");
+    const int B = h->cur_B;
+    for (int b = 0; b < B; b++) {
+        if (h->row_last[b] + 1 >= h->d.S) return fail(h, LLM_EINVAL, "a row has reached max_seq_len");
+        if (!h->row_next[b]) return fail(h, LLM_ESTATE, "a row's next token column has not been written");
+    }
+    if (!h->dry) {
+        // each row moves to its next position, then the step runs at pos_rows[b]
+        HIPC(h, launch_inc_ints(h->pos_rows, B, h->stream));
+        Pass ps;
+        ps.B = B;
+        ps.M = B;
+        ps.T = 1;
+        ps.pos_rows = h->pos_rows;
+        if (h->use_graph) {
+            if (!h->gexec_rows || h->graph_rows_B != B) {
+                if (h->gexec_rows) {
+                    (void)hipGraphExecDestroy(h->gexec_rows);
+                    h->gexec_rows = nullptr;
+                }
+                hipGraph_t graph = nullptr;
+                HIPC(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeRelaxed));
+                hipError_t fe = forward(h, ps);
+                hipError_t ce = hipStreamEndCapture(h->stream, &graph);
+                if (fe != hipSuccess) return fail(h, LLM_EDEVICE, std::string("capture: ") + hipGetErrorString(fe));
+                if (ce != hipSuccess) return fail(h, LLM_EDEVICE, std::string("end capture: ") + hipGetErrorString(ce));
+                hipError_t ie = hipGraphInstantiate(&h->gexec_rows, graph, nullptr, nullptr, 0);
+                (void)hipGraphDestroy(graph);
+                if (ie != hipSuccess) return fail(h, LLM_EDEVICE, std::string("instantiate: ") + hipGetErrorString(ie));
+                h->graph_rows_B = B;
+            }
+            HIPC(h, hipGraphLaunch(h->gexec_rows, h->stream));
+        } else {
+            rc = after_forward(h, forward(h, ps));
+            if (rc) return rc;
+        }
+    }
+    for (int b = 0; b < B; b++) {
+        h->row_last[b]++;
+        h->row_next[b] = 0;
+    }
+    h->logits_valid = true;
+    return LLM_OK;
+}
+
+int llm_set_tokens_rows(llm_t *h, const int32_t *tokens, const uint8_t *mask)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!h->prefilled || !h->rows_mode) return fail(h, LLM_ESTATE, "per-row tokens need a varlen prefill first");
+    if (!tokens) return fail(h, LLM_EINVAL, "tokens is NULL");
+    const int B = h->cur_B;
+    for (int b = 0; b < B; b++) {
+        const bool use = !mask || mask[b];
+        if (use && (tokens[b] < 0 || tokens[b] >= h->d.V)) return fail(h, LLM_EINVAL, "token id out of [0, vocab)");
+        if (use && h->row_last[b] + 1 >= h->d.S) return fail(h, LLM_EINVAL, "a row has no column left");
+    }
+    if (!h->dry) {
+        HIPC(h, hipMemcpyAsync(h->stage_i32, tokens, (size_t)B * 4, hipMemcpyHostToDevice, h->stream));
+        if (mask) HIPC(h, hipMemcpyAsync(h->stage_mask, mask, (size_t)B, hipMemcpyHostToDevice, h->stream));
+        HIPC(h, launch_set_tokens_rows(h->tok, h->d.S, B, h->pos_rows, h->stage_i32, mask ? h->stage_mask : nullptr,
+                                       h->stream));
+        HIPC(h, hipStreamSynchronize(h->stream));
+    }
+    for (int b = 0; b < B; b++)
+        if (!mask || mask[b]) h->row_next[b] = 1;
+    return LLM_OK;
+}
+
 int llm_decode(llm_t *h, int32_t prev_pos)
 {
     int rc = guard(h);
     if (rc) return rc;
     if (!h->prefilled) return fail(h, LLM_ESTATE, "decode before prefill");
+    if (h->rows_mode) return fail(h, LLM_ESTATE, "rows are at different positions: use llm_decode_rows");
     if (prev_pos < 1 || prev_pos >= h->d.S) return fail(h, LLM_EINVAL, "prev_pos must be in [1, max_seq_len)");
     if (prev_pos > h->last_pos + 1) return fail(h, LLM_ESTATE, "prev_pos skips positions whose KV is not written");
     if (!h->col_written[prev_pos]) return fail(h, LLM_ESTATE, "token column prev_pos has not been written");
@@ -791,7 +1042,7 @@ int llm_decode(llm_t *h, int32_t prev_pos)
                 }
                 hipGraph_t graph = nullptr;
                 HIPC(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeRelaxed));
-                hipError_t fe = forward(h, B, 1, h->pos_dev);
+                hipError_t fe = forward(h, uniform_pass(B, 1, h->pos_dev));
                 hipError_t ce = hipStreamEndCapture(h->stream, &graph);
                 if (fe != hipSuccess) return fail(h, LLM_EDEVICE, std::string("capture: ") + hipGetErrorString(fe));
                 if (ce != hipSuccess) return fail(h, LLM_EDEVICE, std::string("end capture: ") + hipGetErrorString(ce));
@@ -802,7 +1053,7 @@ int llm_decode(llm_t *h, int32_t prev_pos)
             }
             HIPC(h, hipGraphLaunch(h->gexec, h->stream));
         } else {
-            rc = after_forward(h, forward(h, B, 1, h->pos_dev));
+            rc = after_forward(h, forward(h, uniform_pass(B, 1, h->pos_dev)));
             if (rc) return rc;
         }
     }
@@ -845,6 +1096,7 @@ int llm_set_tokens(llm_t *h, int32_t pos, const int32_t *tokens, const uint8_t *
     int rc = guard(h);
     if (rc) return rc;
     if (!h->prefilled) return fail(h, LLM_ESTATE, "set_tokens before prefill");
+    if (h->rows_mode) return fail(h, LLM_ESTATE, "rows are at different positions: use llm_set_tokens_rows");
     if (pos < 0 || pos >= h->d.S) return fail(h, LLM_EINVAL, "pos must be in [0, max_seq_len)");
     if (!tokens) return fail(h, LLM_EINVAL, "tokens is NULL");
     const int B = h->cur_B;
@@ -869,6 +1121,7 @@ int llm_set_tokens_d(llm_t *h, int32_t pos, const int32_t *tokens_d, const uint8
     int rc = guard(h);
     if (rc) return rc;
     if (!h->prefilled) return fail(h, LLM_ESTATE, "set_tokens before prefill");
+    if (h->rows_mode) return fail(h, LLM_ESTATE, "rows are at different positions: use llm_set_tokens_rows");
     if (pos < 0 || pos >= h->d.S) return fail(h, LLM_EINVAL, "pos must be in [0, max_seq_len)");
     if (!tokens_d) return fail(h, LLM_EINVAL, "tokens is NULL");
     if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
@@ -884,6 +1137,7 @@ int llm_profile_decode(llm_t *h, int32_t prev_pos, int32_t reps, float *ms_out)
     if (!ms_out || reps < 1) return fail(h, LLM_EINVAL, "bad arguments");
     if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
     if (!h->prefilled) return fail(h, LLM_ESTATE, "decode before prefill");
+    if (h->rows_mode) return fail(h, LLM_ESTATE, "rows are at different positions");
     if (prev_pos < 1 || prev_pos >= h->d.S) return fail(h, LLM_EINVAL, "prev_pos must be in [1, max_seq_len)");
     if (prev_pos > h->last_pos + 1) return fail(h, LLM_ESTATE, "prev_pos skips positions whose KV is not written");
     if (!h->col_written[prev_pos]) return fail(h, LLM_ESTATE, "token column prev_pos has not been written");
@@ -927,12 +1181,12 @@ hipError_t projection_pass(llm_t *h, int kind, int reps, bool fused, int *launch
         if (kind < 5) {
             const int per_rep = kinds[kind] == MAT_HEAD ? 1 : NL;
             for (int l = 0; l < per_rep && e == hipSuccess; l++, ++*launches)
-                e = product(h, l, kinds[kind], B, 1, h->pos_dev, fused);
+                e = product(h, l, kinds[kind], uniform_pass(B, 1, h->pos_dev), fused);
         } else {
             for (int l = 0; l < NL && e == hipSuccess; l++)
                 for (int k = 0; k < 4 && e == hipSuccess; k++, ++*launches)
-                    e = product(h, l, kinds[k], B, 1, h->pos_dev, fused);
-            if (e == hipSuccess) e = product(h, 0, MAT_HEAD, B, 1, h->pos_dev, fused);
+                    e = product(h, l, kinds[k], uniform_pass(B, 1, h->pos_dev), fused);
+            if (e == hipSuccess) e = product(h, 0, MAT_HEAD, uniform_pass(B, 1, h->pos_dev), fused);
             ++*launches;
         }
     }
@@ -947,6 +1201,7 @@ int llm_profile_projections(llm_t *h, int32_t reps, float *us_out)
     if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
     if (h->d.dtype != LLM_F16) return fail(h, LLM_EINVAL, "projection timing is for fp16 models");
     if (!h->prefilled) return fail(h, LLM_ESTATE, "projection timing before prefill");
+    if (h->rows_mode) return fail(h, LLM_ESTATE, "rows are at different positions");
     const bool fused = fuse_norm(h, h->cur_B);
     hipEvent_t ev[2] = {nullptr, nullptr};
     hipError_t e = hipEventCreate(&ev[0]);
@@ -1032,8 +1287,8 @@ int llm_sample_probs(llm_t *h, const float *probs, int32_t B, float top_p, const
     if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
     HIPC(h, hipMemcpyAsync(h->probs, probs, (size_t)B * h->d.V * sizeof(float), hipMemcpyHostToDevice, h->stream));
     HIPC(h, hipMemcpyAsync(h->uni, uniforms, (size_t)B * sizeof(float), hipMemcpyHostToDevice, h->stream));
-    HIPC(h, launch_sample_top_p(h->probs, false, 1.f, B, h->d.V, top_p, h->uni, h->tok, h->d.S, -1, h->outtok,
-                                nullptr, h->stream));
+    HIPC(h, launch_sample_top_p(h->probs, false, 1.f, B, h->d.V, top_p, h->uni, h->tok, h->d.S, -1, nullptr,
+                                h->outtok, nullptr, h->stream));
     HIPC(h, hipMemcpyAsync(out, h->outtok, (size_t)B * sizeof(int32_t), hipMemcpyDeviceToHost, h->stream));
     HIPC(h, hipStreamSynchronize(h->stream));
     h->logits_valid = false;  // the probability buffer no longer matches the logits

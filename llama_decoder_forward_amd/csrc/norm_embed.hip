@@ -10,14 +10,23 @@ constexpr int kThreads = 256;
 // tok[b][pos0 + t]; decode (pos_dev != NULL, T == 1): row b reads
 // tok[b][*pos_dev].
 __global__ void embed_kernel(const char *E, const int32_t *tok, int64_t tok_ld, int T,
-                             const int *pos_dev, int pos0, int64_t row_bytes, char *x)
+                             const int *pos_dev, int pos0, const int *pos_rows, const int2 *rowmap,
+                             int64_t row_bytes, char *x)
 {
-    int m = blockIdx.x;
-    int b = m / T, t = m % T;
-    int col = (pos_dev ? *pos_dev : pos0) + t;
+    const int m = blockIdx.x;
+    int b, col;
+    locate_row(m, T, pos_dev, pos0, pos_rows, rowmap, b, col);
     int32_t id = tok[(int64_t)b * tok_ld + col];
     const uint4 *src = reinterpret_cast<const uint4 *>(E + (int64_t)id * row_bytes);
     uint4 *dst = reinterpret_cast<uint4 *>(x + (int64_t)m * row_bytes);
+    for (int64_t i = threadIdx.x; i < row_bytes / 16; i += blockDim.x) dst[i] = src[i];
+}
+
+// Row i of out = row idx[i] of x (the last token of each varlen row).
+__global__ void gather_rows_kernel(const char *x, const int *idx, int64_t row_bytes, char *out)
+{
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + (int64_t)idx[blockIdx.x] * row_bytes);
+    uint4 *dst = reinterpret_cast<uint4 *>(out + (int64_t)blockIdx.x * row_bytes);
     for (int64_t i = threadIdx.x; i < row_bytes / 16; i += blockDim.x) dst[i] = src[i];
 }
 
@@ -93,12 +102,22 @@ __global__ void rmsnorm_f32_kernel(const float *x, int64_t ldx, const float *w, 
 
 }  // namespace
 
-hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int B, int T,
-                        const int *pos_dev, int pos0, int D, int dtype, void *x, hipStream_t s)
+hipError_t launch_embed(const void *E, const int32_t *tok, int64_t tok_ld, int M, int T,
+                        const int *pos_dev, int pos0, const int *pos_rows, const int2 *rowmap, int D,
+                        int dtype, void *x, hipStream_t s)
 {
     int64_t row_bytes = (int64_t)D * (dtype == 1 ? 2 : 4);
-    hipLaunchKernelGGL(embed_kernel, dim3(B * T), dim3(kThreads), 0, s, (const char *)E, tok,
-                       tok_ld, T, pos_dev, pos0, row_bytes, (char *)x);
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(kThreads), 0, s, (const char *)E, tok,
+                       tok_ld, T, pos_dev, pos0, pos_rows, rowmap, row_bytes, (char *)x);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void *x, const int *idx, int n, int D, int es, void *out, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(kThreads), 0, s, (const char *)x, idx,
+                       (int64_t)D * es, (char *)out);
     return hipGetLastError();
 }
 

@@ -29,8 +29,16 @@ __device__ __forceinline__ uint64_t qmass(uint32_t pbits)
 // ---------------------------------------------------------------------------
 // Greedy: argmax, lowest id among equal maxima.
 // ---------------------------------------------------------------------------
+// token column a sampler writes for row b (-1: none)
+__device__ __forceinline__ int sample_col(int b, int write_col, const int *col_rows, int64_t tok_ld)
+{
+    if (!col_rows) return write_col;
+    const int c = col_rows[b] + 1;
+    return c < tok_ld ? c : -1;
+}
+
 __global__ void argmax_kernel(const float *logits, int V, int32_t *tok, int64_t tok_ld,
-                              int write_col, int32_t *out)
+                              int write_col, const int *col_rows, int32_t *out)
 {
     __shared__ float sv[16];
     __shared__ int si[16];
@@ -56,7 +64,8 @@ __global__ void argmax_kernel(const float *logits, int V, int32_t *tok, int64_t 
         for (int k = 1; k < (int)(blockDim.x >> 6); k++)
             if (sv[k] > best || (sv[k] == best && si[k] < bi)) { best = sv[k]; bi = si[k]; }
         if (bi < 0 || bi >= V) bi = 0;  // every logit NaN: keep the id in range
-        if (write_col >= 0) tok[(int64_t)b * tok_ld + write_col] = bi;
+        const int col = sample_col(b, write_col, col_rows, tok_ld);
+        if (col >= 0) tok[(int64_t)b * tok_ld + col] = bi;
         if (out) out[b] = bi;
     }
 }
@@ -167,7 +176,7 @@ __device__ SelectResult radix_select(const uint32_t *keys, int V, uint64_t X, ui
 __global__ __launch_bounds__(kSampThreads) void top_p_kernel(const float *probs, int V, float top_p,
                                                              const float *uniforms, int32_t *tok,
                                                              int64_t tok_ld, int write_col,
-                                                             int32_t *out)
+                                                             const int *col_rows, int32_t *out)
 {
     __shared__ uint32_t hcnt[256];
     __shared__ uint64_t hsum[256];
@@ -223,7 +232,8 @@ __global__ __launch_bounds__(kSampThreads) void top_p_kernel(const float *probs,
     __syncthreads();
     if (threadIdx.x == 0) {
         int id = found >= 0 ? found : 0;
-        if (write_col >= 0) tok[(int64_t)b * tok_ld + write_col] = id;
+        const int col = sample_col(b, write_col, col_rows, tok_ld);
+        if (col >= 0) tok[(int64_t)b * tok_ld + col] = id;
         if (out) out[b] = id;
     }
 }
@@ -335,7 +345,8 @@ __device__ __forceinline__ SelectResult radix_select_lds(const uint32_t *keys, i
 __global__ __launch_bounds__(kSampThreads) void top_p_lds_kernel(const float *src, int from_logits,
                                                                  float temperature, int V, float top_p,
                                                                  const float *uniforms, int32_t *tok,
-                                                                 int64_t tok_ld, int write_col, int32_t *out)
+                                                                 int64_t tok_ld, int write_col,
+                                                                 const int *col_rows, int32_t *out)
 {
     __shared__ TpShared sh;
     extern __shared__ uint32_t keys[];  // V patterns
@@ -427,12 +438,37 @@ __global__ __launch_bounds__(kSampThreads) void top_p_lds_kernel(const float *sr
     __syncthreads();
     if (threadIdx.x == 0) {
         const int id = sh.found >= 0 ? sh.found : 0;
-        if (write_col >= 0) tok[(int64_t)b * tok_ld + write_col] = id;
+        const int col = sample_col(b, write_col, col_rows, tok_ld);
+        if (col >= 0) tok[(int64_t)b * tok_ld + col] = id;
         if (out) out[b] = id;
     }
 }
 
 __global__ void set_int_kernel(int *dst, int v) { *dst = v; }
+
+__global__ void inc_ints_kernel(int *dst, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] += 1;
+}
+
+__global__ void set_tokens_rows_kernel(int32_t *tok, int64_t tok_ld, int B, const int *col_rows,
+                                       const int32_t *vals, const uint8_t *mask)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B || (mask && !mask[b])) return;
+    const int c = col_rows[b] + 1;
+    if (c < tok_ld) tok[(int64_t)b * tok_ld + c] = vals[b];
+}
+
+__global__ void scatter_tokens_kernel(int32_t *tok, int64_t tok_ld, int M, const int2 *rowmap,
+                                      const int32_t *vals)
+{
+    const int m = blockIdx.x * blockDim.x + threadIdx.x;
+    if (m >= M) return;
+    const int2 r = rowmap[m];
+    tok[(int64_t)r.x * tok_ld + r.y] = vals[m];
+}
 
 __global__ void set_tokens_kernel(int32_t *tok, int64_t tok_ld, int B, int col, const int32_t *vals,
                                   const uint8_t *mask)
@@ -446,10 +482,10 @@ __global__ void set_tokens_kernel(int32_t *tok, int64_t tok_ld, int B, int col, 
 }  // namespace
 
 hipError_t launch_argmax(const float *logits, int B, int V, int32_t *tok, int64_t tok_ld,
-                         int write_col, int32_t *out, hipStream_t s)
+                         int write_col, const int *col_rows, int32_t *out, hipStream_t s)
 {
     hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, s, logits, V, tok, tok_ld, write_col,
-                       out);
+                       col_rows, out);
     return hipGetLastError();
 }
 
@@ -462,20 +498,21 @@ hipError_t launch_softmax_temp(const float *logits, int B, int V, float temperat
 }
 
 hipError_t launch_top_p(const float *probs, int B, int V, float top_p, const float *uniforms,
-                        int32_t *tok, int64_t tok_ld, int write_col, int32_t *out, hipStream_t s)
+                        int32_t *tok, int64_t tok_ld, int write_col, const int *col_rows, int32_t *out,
+                        hipStream_t s)
 {
     hipLaunchKernelGGL(top_p_kernel, dim3(B), dim3(kSampThreads), 0, s, probs, V, top_p, uniforms,
-                       tok, tok_ld, write_col, out);
+                       tok, tok_ld, write_col, col_rows, out);
     return hipGetLastError();
 }
 
 hipError_t launch_sample_top_p(const float *src, bool from_logits, float temperature, int B, int V, float top_p,
-                               const float *uniforms, int32_t *tok, int64_t tok_ld, int write_col, int32_t *out,
-                               float *probs_scratch, hipStream_t s)
+                               const float *uniforms, int32_t *tok, int64_t tok_ld, int write_col,
+                               const int *col_rows, int32_t *out, float *probs_scratch, hipStream_t s)
 {
     if (V <= TP_MAXV && V % 4 == 0) {
         hipLaunchKernelGGL(top_p_lds_kernel, dim3(B), dim3(kSampThreads), (size_t)V * 4, s, src, (int)from_logits,
-                           temperature, V, top_p, uniforms, tok, tok_ld, write_col, out);
+                           temperature, V, top_p, uniforms, tok, tok_ld, write_col, col_rows, out);
         return hipGetLastError();
     }
     const float *probs = src;
@@ -484,12 +521,35 @@ hipError_t launch_sample_top_p(const float *src, bool from_logits, float tempera
         if (e != hipSuccess) return e;
         probs = probs_scratch;
     }
-    return launch_top_p(probs, B, V, top_p, uniforms, tok, tok_ld, write_col, out, s);
+    return launch_top_p(probs, B, V, top_p, uniforms, tok, tok_ld, write_col, col_rows, out, s);
 }
 
 hipError_t launch_set_int(int *dst, int v, hipStream_t s)
 {
     hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, s, dst, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_inc_ints(int *dst, int n, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(inc_ints_kernel, dim3((n + 63) / 64), dim3(64), 0, s, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_tokens_rows(int32_t *tok, int64_t tok_ld, int B, const int *col_rows, const int32_t *vals,
+                                  const uint8_t *mask, hipStream_t s)
+{
+    hipLaunchKernelGGL(set_tokens_rows_kernel, dim3((B + 63) / 64), dim3(64), 0, s, tok, tok_ld, B, col_rows, vals,
+                       mask);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_tokens(int32_t *tok, int64_t tok_ld, int M, const int2 *rowmap, const int32_t *vals,
+                                 hipStream_t s)
+{
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(scatter_tokens_kernel, dim3((M + 255) / 256), dim3(256), 0, s, tok, tok_ld, M, rowmap, vals);
     return hipGetLastError();
 }
 

@@ -132,6 +132,49 @@ def test_dry_handle_prefill_at():
     h.destroy()
 
 
+def test_dry_handle_varlen_rows():
+    """Varlen prefill puts the rows at their own positions: per-row decode and
+    tokens work, the uniform-position calls are refused until a plain
+    prefill."""
+    w = configs.TINY
+    h = b.llm_create_dry(b.params_for(w, max_batch_size=2))
+    S = w.max_seq_len
+
+    def code(fn, *a):
+        try:
+            fn(*a)
+            return b.LLM_OK
+        except b.LlmError as e:
+            return e.code
+
+    r = lambda n: np.zeros(n, np.int32)
+    assert code(h.decode_rows) == b.LLM_ESTATE                       # no varlen prefill yet
+    assert code(h.prefill_varlen, [r(3), r(0)]) == b.LLM_EINVAL       # empty row
+    assert code(h.prefill_varlen, [r(3), r(S + 1)]) == b.LLM_EINVAL   # longer than the cache
+    assert code(h.prefill_varlen, [r(1)] * 3) == b.LLM_EINVAL         # B > max_batch_size
+    assert code(h.prefill_varlen, [r(3), np.full(2, w.vocab_size, np.int32)]) == b.LLM_EINVAL
+    assert code(h.prefill_varlen, [r(3), r(8)]) == b.LLM_OK
+    assert code(h.decode_rows) == b.LLM_ESTATE                        # next columns not written
+    assert code(h.decode, 8) == b.LLM_ESTATE                          # uniform calls refused
+    assert code(h.set_tokens, 8, np.array([1, 2])) == b.LLM_ESTATE
+    assert code(h.prefill_at, 3, np.zeros((2, 2), np.int32)) == b.LLM_ESTATE
+    assert code(h.set_tokens_rows, np.array([1, 2]), np.array([1, 0])) == b.LLM_OK
+    assert code(h.decode_rows) == b.LLM_ESTATE                        # row 1 still unwritten
+    assert code(h.sample, 0.0, 1.0, None, False) == b.LLM_OK          # writes both next columns
+    assert code(h.decode_rows) == b.LLM_OK                            # rows now at 3 and 8
+    assert code(h.set_tokens_rows, np.array([1, w.vocab_size])) == b.LLM_EINVAL
+    for _ in range(S - 9):                                            # row 1 reaches S - 1
+        assert code(h.sample, 0.0, 1.0, None, False) == b.LLM_OK
+        assert code(h.decode_rows) == b.LLM_OK
+    assert code(h.sample, 0.0, 1.0, None, False) == b.LLM_OK          # row 1's token has no column
+    assert code(h.decode_rows) == b.LLM_EINVAL
+    assert code(h.prefill, np.zeros((2, 4), np.int32)) == b.LLM_OK     # back to uniform rows
+    assert code(h.sample, 0.0, 1.0, None, False) == b.LLM_OK
+    assert code(h.decode, 4) == b.LLM_OK
+    assert code(h.decode_rows) == b.LLM_ESTATE
+    h.destroy()
+
+
 def test_dry_handle_last_slot():
     """With prompt 8 and 24 steps the last decode runs at position S-1 = 31
     and its sampled token has no column left (it is returned, not stored)."""

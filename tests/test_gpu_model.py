@@ -209,6 +209,49 @@ def test_prefill_at_offset(B, case):
     h.destroy()
 
 
+@pytest.mark.parametrize("case", ["fp32", "fp16", "fp16-tiled", "fp16-wide"])
+def test_varlen_prefill_rows_decode(B, case):
+    """Ragged prompts in one varlen prefill, then per-row decode steps with
+    teacher-forced columns: every row's logits match the oracle's one-row
+    forward over that row's tokens, and the token buffer holds each row's
+    prompt and forced tokens."""
+    if case == "fp32":
+        kw = dict(n_layers=2, dim=64, n_heads=4, n_kv_heads=2, vocab_size=256, multiple_of=32,
+                  ffn_dim_multiplier=0.0, max_batch_size=2, max_seq_len=32, dtype=0)
+        lens, steps = [3, 8], 6
+    elif case == "fp16":
+        kw = small_kw()
+        lens, steps = [5, 17, 40], 5
+    elif case == "fp16-tiled":  # 1100 packed rows: weight-tile activation layout
+        kw = small_kw(max_seq_len=768, max_batch_size=2)
+        lens, steps = [700, 400], 3
+    else:  # 20 rows: fragment-major decode steps with two row halves
+        kw = small_kw(max_batch_size=20)
+        lens, steps = list(synth.prompt_lengths(49, 20, 1, 40)), 3
+    Bn = len(lens)
+    N = max(lens) + steps
+    toks = synth.tokens(50, Bn, N, kw["vocab_size"])
+    say("varlen", case, lens[:4])
+    h = B.llm_create(B.make_params(**kw), 98)
+    h.prefill_varlen([toks[b, :lens[b]] for b in range(Bn)])
+    got = [h.get_logits()]
+    for k in range(steps):
+        h.set_tokens_rows([toks[b, lens[b] + k] for b in range(Bn)])
+        h.decode_rows()
+        got.append(h.get_logits())
+    got = np.stack(got, 1)                                   # [B][steps+1][V]
+    buf = h.get_tokens(N)
+    for b in range(Bn):
+        n = lens[b] + steps
+        assert np.array_equal(buf[b, :n], toks[b, :n])
+        want = oracle.forward_stream(ocfg(kw), 98, toks[b:b + 1, :n], lens[b] - 1)[0]
+        if case == "fp32":
+            assert np.abs(got[b] - want).max() <= 1e-3
+        else:
+            check_logits(got[b:b + 1], want[None])
+    h.destroy()
+
+
 def test_small_fp16_sampled_and_deterministic(B):
     kw = small_kw()
     T0, steps = 9, 10
