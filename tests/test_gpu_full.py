@@ -223,6 +223,7 @@ def test_70b_shape_short_prompt_end_to_end(B):
     check_logits(got, want)
 
 
+@pytest.mark.timeout(900)
 def test_70b_full_depth_vs_oracle(B):
     """All 80 layers of the 70B model, one row, a 4-token prompt and 2 forced
     decode steps.  At this depth the fp16 rounding points amplify any change
@@ -237,8 +238,11 @@ def test_70b_full_depth_vs_oracle(B):
     h = B.llm_create(B.make_params(**kw), w.weight_seed)
     got = forced(h, toks, 4, 2)
     h.destroy()
-    say("70B full depth: oracle fp32 and fp64")
+    # Each oracle pass regenerates all 69e9 weights on the host: one to
+    # three minutes each, depending on the host's cores.
+    say("70B full depth: oracle fp32")
     o32 = oracle.forward_stream(oracle.Cfg(**kw), w.weight_seed, toks, 3)
+    say("70B full depth: oracle fp64 accumulation")
     o64 = oracle.forward_stream(oracle.Cfg(**kw), w.weight_seed, toks, 3, acc64=True)
     spread = np.abs(o32 - o64).max()
     cos_spread = cosine(o32.reshape(-1, o32.shape[-1]), o64.reshape(-1, o64.shape[-1])).min()
