@@ -104,6 +104,62 @@ const char *llm_last_error(const llm_t *h);
  * handle unless one was passed to llm_create); NULL for a dry handle. */
 void *llm_get_stream(llm_t *h);
 
+/* ---- paged KV cache ------------------------------------------------------
+ * The block-pool cache of the nano-vllm notes (model runner,
+ * allocate_kv_cache; block tables and slot mapping of prepare_prefill /
+ * prepare_decode) in place of the static cache.  The pool holds num_blocks
+ * blocks; a block holds block_size consecutive positions of one batch row,
+ * K and V of every KV head of every layer.  Row b's positions
+ * [i*block_size, (i+1)*block_size) live in the block at entry i of its block
+ * table (width ceil(max_seq_len / block_size)).  Results are identical to a
+ * static-cache handle of the same parameters, bit for bit.
+ *
+ * Blocks are handed out on demand: a pass that writes positions [.., end) of
+ * row b first gives every empty table entry below ceil(end / block_size) the
+ * lowest-numbered free block.  A row keeps its blocks until its table is
+ * replaced (llm_kv_set_block_table) or a prefill from position 0 of B rows
+ * returns the blocks of rows >= B to the pool.  A pass that needs more free
+ * blocks than the pool has fails with LLM_ENOMEM, and a pass that reads
+ * cached positions whose table entry is empty fails with LLM_ESTATE, both
+ * before anything changes.  Every other call behaves as on a static handle. */
+typedef struct {
+    int32_t block_size;            /* positions per block: a power of two in [32, 65536] */
+    int32_t num_blocks;            /* pool size, at most max_batch_size * table width; 0: from
+                                      the memory budget */
+    float gpu_memory_utilization;  /* num_blocks == 0: the pool takes
+                                      total * gpu_memory_utilization - (memory in use once
+                                      weights, buffers and the workspace of the largest pass
+                                      are allocated), in (0, 1] */
+} llm_paging;
+
+/* Bytes of one block: 2 * n_layers * block_size * n_kv_heads * head_dim *
+ * element size (the nano-vllm notes' block_bytes), or < 0. */
+int64_t llm_kv_block_bytes(const llm_params *p, int32_t block_size);
+
+/* llm_create with a paged cache; the pool is zeroed.  Errors as llm_create,
+ * LLM_EINVAL for paging values out of range, LLM_ENOMEM when the budget
+ * leaves no room for one block. */
+int llm_create_paged(const llm_params *p, const llm_paging *pg, uint64_t seed, void *hip_stream,
+                     llm_t **out);
+/* llm_create_dry with a paged cache (num_blocks must be > 0): the block
+ * bookkeeping runs as on a real handle. */
+int llm_create_paged_dry(const llm_params *p, const llm_paging *pg, llm_t **out);
+
+/* Pool size, free blocks and block-table width; 0 for a static handle. */
+int32_t llm_kv_num_blocks(const llm_t *h);
+int32_t llm_kv_free_blocks(const llm_t *h);
+int32_t llm_kv_table_width(const llm_t *h);
+
+/* Copy the first n entries of row's block table (-1 for empty) into out. */
+int llm_kv_block_table(llm_t *h, int32_t row, int32_t *out, int32_t n);
+
+/* Replace row's block table by blocks[0..n) (the rest empty), n <= table
+ * width.  The ids must be distinct, in [0, num_blocks) and free or already
+ * held by this row; the row's other blocks return to the pool.  A block's
+ * contents are what was last written to it: moving cached positions to
+ * other blocks makes the row read those.  n == 0 releases the row. */
+int llm_kv_set_block_table(llm_t *h, int32_t row, const int32_t *blocks, int32_t n);
+
 /* ---- the forward pass --------------------------------------------------- */
 
 /* Prefill (Transformer.forward(tokens, 0), walkthrough sections 2 and 3.8):

@@ -39,8 +39,14 @@ class llm_params(C.Structure):
                 ("max_seq_len", C.c_int32), ("dtype", C.c_int32)]
 
 
+class llm_paging(C.Structure):
+    _fields_ = [("block_size", C.c_int32), ("num_blocks", C.c_int32),
+                ("gpu_memory_utilization", C.c_float)]
+
+
 _vp = C.c_void_p
 _P = C.POINTER(llm_params)
+_PG = C.POINTER(llm_paging)
 EXPORTS = {
     "llm_ffn_hidden": (C.c_int64, [_P]),
     "llm_kv_cache_bytes": (C.c_int64, [_P]),
@@ -77,6 +83,14 @@ EXPORTS = {
     "llm_op_linear": (C.c_int, [_vp, C.c_int32, C.c_int32, _vp, C.c_int32, _vp]),
     "llm_op_kv_write": (C.c_int, [_vp, C.c_int32, _vp, _vp, C.c_int32, C.c_int32, C.c_int32]),
     "llm_op_attention": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32, C.c_int32, C.c_int32, _vp]),
+    "llm_kv_block_bytes": (C.c_int64, [_P, C.c_int32]),
+    "llm_create_paged": (C.c_int, [_P, _PG, C.c_uint64, _vp, C.POINTER(_vp)]),
+    "llm_create_paged_dry": (C.c_int, [_P, _PG, C.POINTER(_vp)]),
+    "llm_kv_num_blocks": (C.c_int32, [_vp]),
+    "llm_kv_free_blocks": (C.c_int32, [_vp]),
+    "llm_kv_table_width": (C.c_int32, [_vp]),
+    "llm_kv_block_table": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32]),
+    "llm_kv_set_block_table": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32]),
 }
 for _name, (_res, _args) in EXPORTS.items():
     _f = getattr(_lib, _name)
@@ -117,6 +131,10 @@ def llm_weight_bytes(p: llm_params) -> int:
 
 def llm_check_params(p: llm_params) -> int:
     return _lib.llm_check_params(C.byref(p))
+
+
+def llm_kv_block_bytes(p: llm_params, block_size: int) -> int:
+    return _lib.llm_kv_block_bytes(C.byref(p), block_size)
 
 
 class Handle:
@@ -277,6 +295,25 @@ class Handle:
     def op_attention(self, layer: int, q_ptr: int, B: int, T: int, pos0: int, out_ptr: int):
         self._ck(_lib.llm_op_attention(self.ptr, layer, C.c_void_p(q_ptr), B, T, pos0, C.c_void_p(out_ptr)))
 
+    def kv_num_blocks(self) -> int:
+        return _lib.llm_kv_num_blocks(self.ptr)
+
+    def kv_free_blocks(self) -> int:
+        return _lib.llm_kv_free_blocks(self.ptr)
+
+    def kv_table_width(self) -> int:
+        return _lib.llm_kv_table_width(self.ptr)
+
+    def kv_block_table(self, row: int) -> np.ndarray:
+        n = self.kv_table_width()
+        out = np.empty(n, np.int32)
+        self._ck(_lib.llm_kv_block_table(self.ptr, row, out.ctypes.data_as(C.c_void_p), n))
+        return out
+
+    def kv_set_block_table(self, row: int, blocks):
+        b, bp = _arr(blocks, np.int32)
+        self._ck(_lib.llm_kv_set_block_table(self.ptr, row, bp if b.size else None, b.size))
+
     def destroy(self):
         if self.ptr:
             _lib.llm_destroy(self.ptr)
@@ -308,6 +345,27 @@ def llm_create_dry(params: llm_params) -> Handle:
     rc = _lib.llm_create_dry(C.byref(params), C.byref(out))
     if rc != LLM_OK:
         raise LlmError(rc, "llm_create_dry failed")
+    return Handle(out, params)
+
+
+def make_paging(block_size: int, num_blocks: int = 0, gpu_memory_utilization: float = 0.9) -> llm_paging:
+    return llm_paging(block_size, num_blocks, gpu_memory_utilization)
+
+
+def llm_create_paged(params: llm_params, paging: llm_paging, seed: int, hip_stream: int | None = None) -> Handle:
+    out = C.c_void_p()
+    rc = _lib.llm_create_paged(C.byref(params), C.byref(paging), seed, C.c_void_p(hip_stream or None),
+                               C.byref(out))
+    if rc != LLM_OK:
+        raise LlmError(rc, "llm_create_paged failed")
+    return Handle(out, params)
+
+
+def llm_create_paged_dry(params: llm_params, paging: llm_paging) -> Handle:
+    out = C.c_void_p()
+    rc = _lib.llm_create_paged_dry(C.byref(params), C.byref(paging), C.byref(out))
+    if rc != LLM_OK:
+        raise LlmError(rc, "llm_create_paged_dry failed")
     return Handle(out, params)
 
 

@@ -4,8 +4,10 @@
 // subtracted, weighted sum of values; query head h reads KV head h / n_rep
 // (repeat_kv, section 3.4).
 //
-// Cache layout (per layer): K[b][kvh][s][d] (key-major), V in blocks of 32
-// keys, d-major inside a block (common.h).  Both kernels compute S^T = K Q^T and O^T = V^T P^T with
+// Cache layout (per layer): streams of positions per (block, KV head), K
+// key-major, V in blocks of 32 keys, d-major inside a block (common.h); a
+// static cache has one stream per (row, KV head), a paged one reaches a
+// row's positions through its block table.  Both kernels compute S^T = K Q^T and O^T = V^T P^T with
 // v_mfma_f32_16x16x32_f16, so the query is the MFMA column (lane % 16) and
 // each lane owns its query's running max / sum with no cross-lane moves.
 //
@@ -36,13 +38,16 @@ constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp(m_old 
 // The NW waves are merged in LDS in halving rounds (fixed order), and the
 // normalised output written.  Few (row, KV head) pairs take 8 waves (the
 // work-group count, not the bandwidth, is the limit there); many pairs
-// take 2 or 4 so that more of them fit the CUs at once.
+// take 2 or 4 so that more of them fit the CUs at once.  PAGED: each 32-key
+// step lies in one block of the row's table (blocks hold a multiple of 32
+// positions); the block id of a wave's next step is read before the current
+// step computes.
 // ---------------------------------------------------------------------------
-template <int NW, bool PF>
+template <int NW, bool PF, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
     const half_t *__restrict__ q, const half_t *__restrict__ kc, const half_t *__restrict__ vc,
-    int H, int Hkv, int S, const int *pos_dev, int pos_imm, const int *pos_rows, half_t *__restrict__ out,
-    int out_lay)
+    int H, int Hkv, int S, KvPages pg, const int *pos_dev, int pos_imm, const int *pos_rows,
+    half_t *__restrict__ out, int out_lay)
 {
     constexpr int hd = 128;
     __shared__ floatx4 so[NW / 2][8][64];
@@ -63,8 +68,15 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
 #pragma unroll
     for (int s = 0; s < 4; s++) qb[s] = qv ? *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g) : z;
 
-    const half_t *K = kc + ((int64_t)b * Hkv + kvh) * S * hd;
-    const half_t *V = vc + ((int64_t)b * Hkv + kvh) * S * hd;  // S/32 blocks of 32 x hd
+    // element offset of the first key of 32-key step st in both K and V
+    auto step_base = [&](int st) -> int64_t {
+        const int k0 = 32 * st;
+        if (PAGED) {
+            const int64_t blk = pg.tab[(int64_t)b * pg.ld + (k0 >> pg.shift)];
+            return (((blk * Hkv + kvh) << pg.shift) + (k0 & ((1 << pg.shift) - 1))) * hd;
+        }
+        return (((int64_t)b * Hkv + kvh) * S + k0) * hd;
+    };
 
     floatx4 acc[8];
 #pragma unroll
@@ -72,19 +84,19 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
     float mrun = kNegBig, lrun = 0.f;
 
     // all K and V operands of a step are loaded before any of its arithmetic
-    auto load = [&](int st, half8 (&kf)[2][4], half8 (&vf)[8]) {
+    auto load = [&](int st, int64_t base, half8 (&kf)[2][4], half8 (&vf)[8]) {
         const int k0 = 32 * st;
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-            const int key = k0 + perm_key(t, r);
-            const bool ok = key < L;
-            const half_t *krow = K + (int64_t)(ok ? key : 0) * hd + 8 * g;
+            const int kp = perm_key(t, r);
+            const bool ok = k0 + kp < L;
+            const half_t *krow = kc + base + (ok ? kp : 0) * hd + 8 * g;
 #pragma unroll
             for (int s = 0; s < 4; s++) kf[t][s] = ok ? *reinterpret_cast<const half8 *>(krow + 32 * s) : z;
         }
         const int kk = k0 + 8 * g;
         const bool vok = kk + 8 <= L;
-        const half_t *vblk = V + (int64_t)st * (32 * hd) + 8 * g;
+        const half_t *vblk = vc + base + 8 * g;
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) {
             const half_t *vrow = vblk + (16 * dt + r) * 32;
@@ -138,12 +150,13 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
     };
     half8 kf[2][4], vf[8];
     int st = wave;
-    if (st < nsteps) load(st, kf, vf);
+    if (st < nsteps) load(st, step_base(st), kf, vf);
     for (; st < nsteps; st += NW) {
         const int nx = st + NW;
+        const int64_t nbase = nx < nsteps ? step_base(nx) : 0;
         if (PF) {
             half8 kn[2][4], vn[8];
-            if (nx < nsteps) load(nx, kn, vn);
+            if (nx < nsteps) load(nx, nbase, kn, vn);
             compute(st, kf, vf);
 #pragma unroll
             for (int t = 0; t < 2; t++)
@@ -153,7 +166,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
             for (int dt = 0; dt < 8; dt++) vf[dt] = vn[dt];
         } else {
             compute(st, kf, vf);
-            if (nx < nsteps) load(nx, kf, vf);
+            if (nx < nsteps) load(nx, nbase, kf, vf);
         }
     }
 
@@ -201,14 +214,16 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
 // softmax.  Grid (B*H, ceil(T/128)); 4 waves x 32 queries (two MFMA column
 // groups).  64-key tiles of K (in permuted operand order) and V^T are staged
 // in LDS with register prefetch of the next tile.  Tiles entirely above a
-// wave's last query are skipped; the diagonal tile is masked.
+// wave's last query are skipped; the diagonal tile is masked.  Each 32-key
+// half of a tile lies in one cache stream (blocks of a paged cache hold a
+// multiple of 32 positions), located once per tile.
 // ---------------------------------------------------------------------------
 constexpr int PF_Q = 128, PF_K = 64;
 
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restrict__ q,
                                                            const half_t *__restrict__ kc,
                                                            const half_t *__restrict__ vc, int Tu, int p0u,
-                                                           int H, int Hkv, int S, const int *cu,
+                                                           int H, int Hkv, int S, KvPages pg, const int *cu,
                                                            half_t *__restrict__ out, int out_lay)
 {
     const int hd = 128;
@@ -243,8 +258,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
             qb[c][s] = t < T ? *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g) : z;
     }
 
-    const half_t *K = kc + ((int64_t)b * Hkv + kvh) * S * hd;
-    const half_t *V = vc + ((int64_t)b * Hkv + kvh) * S * hd;  // S/32 blocks of 32 x hd
+    // element offset of key k0 (a multiple of 32) in both K and V
+    auto key_base = [&](int k0) -> int64_t {
+        int off;
+        const int64_t st = kv_stream(pg, b, kvh, k0, Hkv, off);
+        return k_offset(st, off, 0, S, hd);
+    };
 
     floatx4 acc[2][8];
 #pragma unroll
@@ -262,14 +281,18 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
     half8 rk[4], rv[4];
     auto load_tile = [&](int kt) {
         const int base = kt * PF_K;
+        // base < Lk for every tile walked; the second half only when in range
+        const int64_t hb0 = key_base(base);
+        const int64_t hb1 = base + 32 < Lk ? key_base(base + 32) : hb0;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int c = tid + 256 * j;
             const int key = c >> 4, dch = c & 15;  // K: 64 keys x 16 chunks of 8 d
-            rk[j] = base + key < Lk ? *reinterpret_cast<const half8 *>(K + (int64_t)(base + key) * hd + dch * 8) : z;
+            const int64_t kb = key < 32 ? hb0 : hb1;
+            rk[j] = base + key < Lk ? *reinterpret_cast<const half8 *>(kc + kb + (key & 31) * hd + dch * 8) : z;
             const int d = c >> 3, kch = c & 7;     // V^T: 128 d x 8 chunks of 8 keys
             const int key0 = base + kch * 8;
-            const half_t *vp = V + (int64_t)(key0 >> 5) * (32 * hd) + d * 32 + (key0 & 31);
+            const half_t *vp = vc + (kch < 4 ? hb0 : hb1) + d * 32 + (kch & 3) * 8;
             rv[j] = key0 + 8 <= Lk ? *reinterpret_cast<const half8 *>(vp) : z;
             if (key0 < Lk && key0 + 8 > Lk) {
                 half8 t8;
@@ -378,8 +401,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
 // fp32 models (small): one work-group per (b, h, query), scores in LDS.
 // ---------------------------------------------------------------------------
 __global__ void attn_f32_kernel(const float *q, const float *kc, const float *vc, int T, int H,
-                                int Hkv, int hd, int S, const int *pos_dev, int pos_imm, const int *pos_rows,
-                                const int *cu, float *out)
+                                int Hkv, int hd, int Sb, KvPages pg, const int *pos_dev, int pos_imm,
+                                const int *pos_rows, const int *cu, float *out)
 {
     extern __shared__ float sh[];  // L scores
     const int bh = blockIdx.x, b = bh / H, h = bh % H, t = blockIdx.y;
@@ -396,12 +419,13 @@ __global__ void attn_f32_kernel(const float *q, const float *kc, const float *vc
     }
     const int L = pos + 1;
     const float *qr = q + (row * H + h) * hd;
-    const float *K = kc + ((int64_t)b * Hkv + kvh) * S * hd;
-    const float *V = vc + ((int64_t)b * Hkv + kvh) * hd * S;
     const float scale = 1.0f / sqrtf((float)hd);
     for (int j = threadIdx.x; j < L; j += blockDim.x) {
+        int off;
+        const int64_t st = kv_stream(pg, b, kvh, j, Hkv, off);
+        const float *kr = kc + k_offset(st, off, 0, Sb, hd);
         float s = 0.f;
-        for (int d = 0; d < hd; d++) s = fmaf(qr[d], K[(int64_t)j * hd + d], s);
+        for (int d = 0; d < hd; d++) s = fmaf(qr[d], kr[d], s);
         sh[j] = s * scale;
     }
     __syncthreads();
@@ -411,14 +435,18 @@ __global__ void attn_f32_kernel(const float *q, const float *kc, const float *vc
     for (int j = 0; j < L; j++) sum += expf(sh[j] - mx);
     for (int d = threadIdx.x; d < hd; d += blockDim.x) {
         float o = 0.f;
-        for (int j = 0; j < L; j++) o = fmaf(expf(sh[j] - mx) / sum, V[(int64_t)d * S + j], o);
+        for (int j = 0; j < L; j++) {
+            int off;
+            const int64_t st = kv_stream(pg, b, kvh, j, Hkv, off);
+            o = fmaf(expf(sh[j] - mx) / sum, vc[v32_offset(st, off, d, Sb, hd)], o);
+        }
         out[(row * H + h) * hd + d] = o;
     }
 }
 
 template <typename Tv>
-__global__ void kv_write_kernel(const Tv *k, const Tv *v, int T, int pos0, int Hkv, int hd, int S,
-                                Tv *kc, Tv *vc)
+__global__ void kv_write_kernel(const Tv *k, const Tv *v, int T, int pos0, int Hkv, int hd, int Sb,
+                                KvPages pg, Tv *kc, Tv *vc)
 {
     // one thread per element of k[B][T][Hkv][hd]
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -427,31 +455,39 @@ __global__ void kv_write_kernel(const Tv *k, const Tv *v, int T, int pos0, int H
     if (i >= per_row) return;
     const int d = (int)(i % hd), kvh = (int)((i / hd) % Hkv), t = (int)(i / ((int64_t)hd * Hkv));
     const int pos = pos0 + t;
-    kc[(((int64_t)b * Hkv + kvh) * S + pos) * hd + d] = k[(int64_t)b * per_row + i];
+    int off;
+    const int64_t st = kv_stream(pg, b, kvh, pos, Hkv, off);
+    kc[k_offset(st, off, d, Sb, hd)] = k[(int64_t)b * per_row + i];
     if (sizeof(Tv) == 2)
-        vc[vblk_offset(b, kvh, d, pos, Hkv, S, hd)] = v[(int64_t)b * per_row + i];
+        vc[v16_offset(st, off, d, Sb, hd)] = v[(int64_t)b * per_row + i];
     else
-        vc[(((int64_t)b * Hkv + kvh) * hd + d) * S + pos] = v[(int64_t)b * per_row + i];
+        vc[v32_offset(st, off, d, Sb, hd)] = v[(int64_t)b * per_row + i];
 }
 
 }  // namespace
 
-hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s)
+template <bool PAGED>
+hipError_t launch_decode(const AttnArgs &a, hipStream_t s)
 {
-    if (a.out_lay && (a.out_lay > 2 || a.B > 16 * a.out_lay || a.T != 1)) return hipErrorInvalidValue;
     const int pairs = a.B * a.Hkv;
     const half_t *q = (const half_t *)a.q, *kc = (const half_t *)a.kcache, *vc = (const half_t *)a.vcache;
     half_t *o = (half_t *)a.out;
     if (pairs >= 512)
-        hipLaunchKernelGGL((attn_decode_kernel<2, true>), dim3(pairs), dim3(128), 0, s, q, kc, vc, a.H, a.Hkv, a.S,
-                           a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
+        hipLaunchKernelGGL((attn_decode_kernel<2, true, PAGED>), dim3(pairs), dim3(128), 0, s, q, kc, vc, a.H, a.Hkv,
+                           a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
     else if (pairs >= 128)
-        hipLaunchKernelGGL((attn_decode_kernel<4, false>), dim3(pairs), dim3(256), 0, s, q, kc, vc, a.H, a.Hkv, a.S,
-                           a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
+        hipLaunchKernelGGL((attn_decode_kernel<4, false, PAGED>), dim3(pairs), dim3(256), 0, s, q, kc, vc, a.H, a.Hkv,
+                           a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
     else
-        hipLaunchKernelGGL((attn_decode_kernel<8, false>), dim3(pairs), dim3(512), 0, s, q, kc, vc, a.H, a.Hkv, a.S,
-                           a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
+        hipLaunchKernelGGL((attn_decode_kernel<8, false, PAGED>), dim3(pairs), dim3(512), 0, s, q, kc, vc, a.H, a.Hkv,
+                           a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
     return hipGetLastError();
+}
+
+hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s)
+{
+    if (a.out_lay && (a.out_lay > 2 || a.B > 16 * a.out_lay || a.T != 1)) return hipErrorInvalidValue;
+    return a.pg.tab ? launch_decode<true>(a, s) : launch_decode<false>(a, s);
 }
 
 hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s)
@@ -459,7 +495,7 @@ hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s)
     if (a.out_lay != ACT_ROWS && a.out_lay != ACT_TILED) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.B * a.H, (a.T + PF_Q - 1) / PF_Q), dim3(256), 0,
                        s, (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache,
-                       a.T, a.pos_imm, a.H, a.Hkv, a.S, a.cu, (half_t *)a.out, a.out_lay);
+                       a.T, a.pos_imm, a.H, a.Hkv, a.Sb, a.pg, a.cu, (half_t *)a.out, a.out_lay);
     return hipGetLastError();
 }
 
@@ -468,20 +504,20 @@ hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s)
     size_t sh = sizeof(float) * (size_t)a.S;
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.B * a.H, a.T), dim3(64), sh, s, (const float *)a.q,
                        (const float *)a.kcache, (const float *)a.vcache, a.T, a.H, a.Hkv, a.hd,
-                       a.S, a.pos_dev, a.pos_imm, a.pos_rows, a.cu, (float *)a.out);
+                       a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, a.cu, (float *)a.out);
     return hipGetLastError();
 }
 
 hipError_t launch_kv_write(const void *k, const void *v, int B, int T, int pos0, int Hkv, int hd,
-                           int S, int dtype, void *kcache, void *vcache, hipStream_t s)
+                           int Sb, const KvPages &pg, int dtype, void *kcache, void *vcache, hipStream_t s)
 {
     int64_t per_row = (int64_t)T * Hkv * hd;
     dim3 grid((unsigned)((per_row + 255) / 256), B);
     if (dtype == 1)
         hipLaunchKernelGGL(kv_write_kernel<half_t>, grid, dim3(256), 0, s, (const half_t *)k,
-                           (const half_t *)v, T, pos0, Hkv, hd, S, (half_t *)kcache, (half_t *)vcache);
+                           (const half_t *)v, T, pos0, Hkv, hd, Sb, pg, (half_t *)kcache, (half_t *)vcache);
     else
         hipLaunchKernelGGL(kv_write_kernel<float>, grid, dim3(256), 0, s, (const float *)k,
-                           (const float *)v, T, pos0, Hkv, hd, S, (float *)kcache, (float *)vcache);
+                           (const float *)v, T, pos0, Hkv, hd, Sb, pg, (float *)kcache, (float *)vcache);
     return hipGetLastError();
 }

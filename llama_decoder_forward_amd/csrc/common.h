@@ -28,15 +28,48 @@ __host__ __device__ inline int64_t tiled_offset(int64_t n, int64_t k, int64_t K)
     return (nt * (K >> 5) + kt) * 512 + lane * 8 + (k & 7);
 }
 
-// KV cache (per layer), fp16 models:
-//   K[b][kvh][s][d]            key-major: a key's 128 values are contiguous;
-//   V[b][kvh][s/32][d][s%32]   blocks of 32 keys, d-major inside a block, so a
-//                              32-key step reads one contiguous 8 KiB block and
-//                              a lane's 8 consecutive keys of one d are 16 bytes.
-// fp32 models use K[b][kvh][s][d] and V[b][kvh][d][s].
-__host__ __device__ inline int64_t vblk_offset(int64_t b, int kvh, int d, int pos, int Hkv, int S, int hd)
+// KV cache (per layer).  The cache is a set of "streams" of Sb positions,
+// one per (block, KV head), stream index blk * Hkv + kvh:
+//  - static cache: block b is batch row b and Sb = max_seq_len;
+//  - paged cache (nano-vllm notes, allocate_kv_cache): a pool of blocks of
+//    Sb = bs positions (a power of two >= 32); position p of row b lives in
+//    block tab[b * ld + p / bs] at offset p % bs.
+// Inside a stream, fp16 models use
+//   K[s][d]            key-major: a key's 128 values are contiguous;
+//   V[s/32][d][s%32]   blocks of 32 keys, d-major inside a block, so a
+//                      32-key step reads one contiguous 8 KiB block and
+//                      a lane's 8 consecutive keys of one d are 16 bytes;
+// fp32 models use K[s][d] and V[d][s].
+struct KvPages {
+    const int *tab;  // [rows][ld] block ids, or NULL for the static cache
+    int ld;          // entries per row
+    int shift;       // log2 of the block size
+};
+
+// Stream of position pos of (row b, KV head kvh) and the offset in it.
+__device__ __forceinline__ int64_t kv_stream(const KvPages &pg, int b, int kvh, int pos, int Hkv, int &off)
 {
-    return ((b * Hkv + kvh) * (int64_t)(S / 32) + pos / 32) * (int64_t)(hd * 32) + d * 32 + (pos & 31);
+    if (pg.tab) {
+        off = pos & ((1 << pg.shift) - 1);
+        return (int64_t)pg.tab[(int64_t)b * pg.ld + (pos >> pg.shift)] * Hkv + kvh;
+    }
+    off = pos;
+    return (int64_t)b * Hkv + kvh;
+}
+
+// Element offsets of (position at offset off of stream st, d) for streams of
+// Sb positions.
+__host__ __device__ inline int64_t k_offset(int64_t st, int off, int d, int Sb, int hd)
+{
+    return (st * Sb + off) * hd + d;
+}
+__host__ __device__ inline int64_t v16_offset(int64_t st, int off, int d, int Sb, int hd)
+{
+    return (st * Sb + (off & ~31)) * hd + d * 32 + (off & 31);
+}
+__host__ __device__ inline int64_t v32_offset(int64_t st, int off, int d, int Sb, int hd)
+{
+    return (st * hd + d) * Sb + off;
 }
 
 // Decode activations of 2 < M <= 32 rows, "fragment-major": the B operand of
@@ -111,7 +144,8 @@ struct Epilogue {
     int T;                // tokens per batch row (m = b*T + t)
     const int *pos_rows;  // per-row decode positions, or NULL (locate_row)
     const int2 *rowmap;   // packed varlen rows {b, pos}, or NULL (locate_row)
-    int H, Hkv, hd, S;
+    int H, Hkv, hd, S;    // S: positions per cache stream (max_seq_len, or the block size when paged)
+    KvPages pg;           // block tables of a paged cache (pg.tab NULL: static cache)
     int out_lay;          // EP_SWIGLU: layout of g (ACT_ROWS with ldo, 1/2 fragment-major, ACT_TILED)
 };
 
@@ -170,12 +204,14 @@ struct AttnArgs {
     const int *pos_rows;   // decode with per-row positions (T == 1), or NULL
     const int *cu;         // varlen prefill: row b's queries are packed rows cu[b]..cu[b+1]-1
                            // at positions 0..; T is then the longest row; or NULL
+    int Sb;                // positions per cache stream (S, or the block size when paged)
+    KvPages pg;            // block tables of a paged cache (pg.tab NULL: static cache)
 };
 hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_kv_write(const void *k, const void *v, int B, int T, int pos0, int Hkv, int hd,
-                           int S, int dtype, void *kcache, void *vcache, hipStream_t s);
+                           int Sb, const KvPages &pg, int dtype, void *kcache, void *vcache, hipStream_t s);
 
 // Samplers write token column write_col of every row, or with col_rows
 // column col_rows[b] + 1 of row b (none when that reaches tok_ld).

@@ -79,12 +79,15 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
                 *reinterpret_cast<half4 *>((half_t *)ep.out + (int64_t)m * ep.ldo + n) = o;
             } else {
                 const int kvh = (n - qrows) / hd;
-                half_t *kc = (half_t *)ep.kcache + (((int64_t)b * ep.Hkv + kvh) * ep.S + pos) * hd + d0;
-                *reinterpret_cast<half4 *>(kc) = o;
+                int off;
+                const int64_t st = kv_stream(ep.pg, b, kvh, pos, ep.Hkv, off);
+                *reinterpret_cast<half4 *>((half_t *)ep.kcache + k_offset(st, off, d0, ep.S, hd)) = o;
             }
         } else {
             const int r = n - qrows - krows, kvh = r / hd, d0 = r % hd;
-            half_t *vc = (half_t *)ep.vcache + vblk_offset(b, kvh, d0, pos, ep.Hkv, ep.S, hd);
+            int off;
+            const int64_t st = kv_stream(ep.pg, b, kvh, pos, ep.Hkv, off);
+            half_t *vc = (half_t *)ep.vcache + v16_offset(st, off, d0, ep.S, hd);
             for (int i = 0; i < 4; i++) vc[i * 32] = (half_t)acc[i];
         }
         break;
@@ -572,13 +575,17 @@ __global__ void linear_f32_kernel(const float *W, const float *X, int64_t ldx, i
                 out[(int64_t)m * ep.ldo + n] = re;
                 out[(int64_t)m * ep.ldo + n + 1] = im;
             } else {
-                float *kc = (float *)ep.kcache + (((int64_t)b * ep.Hkv + (n - qrows) / hd) * ep.S + pos) * hd + d0;
+                int off;
+                const int64_t st = kv_stream(ep.pg, b, (n - qrows) / hd, pos, ep.Hkv, off);
+                float *kc = (float *)ep.kcache + k_offset(st, off, d0, ep.S, hd);
                 kc[0] = re;
                 kc[1] = im;
             }
         } else {
             const int r = n - qrows - krows, kvh = r / hd, d0 = r % hd;
-            float *vc = (float *)ep.vcache + (((int64_t)b * ep.Hkv + kvh) * hd + d0) * ep.S + pos;
+            int off;
+            const int64_t st = kv_stream(ep.pg, b, kvh, pos, ep.Hkv, off);
+            float *vc = (float *)ep.vcache + v32_offset(st, off, d0, ep.S, hd);
             vc[0] = a;
             vc[ep.S] = bb;
         }

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <set>
 #include <string>
 #include <vector>
 
@@ -86,6 +87,17 @@ struct llm {
     // cache and buffers
     char *kv = nullptr;
     int64_t kv_layer_bytes = 0;  // K part then V part
+    // paged cache (bs > 0): a pool of kv_blocks blocks of bs positions; row b's
+    // positions [bs*i, bs*i + bs) live in block btab[b * bt_ld + i] (-1: none)
+    int bs = 0, bshift = 0, kv_blocks = 0, bt_ld = 0;
+    std::vector<int> btab;     // host copy, the authority
+    std::vector<int> owner;    // [kv_blocks] row holding the block, or -1
+    std::set<int> free_ids;    // unheld blocks; allocation takes the lowest
+    int *btab_d = nullptr;     // device copy, refreshed before a forward pass
+    int *btab_stage = nullptr; // pinned staging buffer of that refresh
+    hipEvent_t btab_ev = nullptr;  // the last refresh's read of the staging buffer
+    bool btab_dirty = false;
+    float kv_util = 0.f;       // memory budget of a pool sized at creation
     float *rope = nullptr;
     int32_t *tok = nullptr;
     float *logits = nullptr, *probs = nullptr, *uni = nullptr;
@@ -196,6 +208,150 @@ int ensure_ws(llm_t *h, int64_t rows)
     }
     return LLM_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Paged KV cache (nano-vllm notes, allocate_kv_cache and the block tables).
+// ---------------------------------------------------------------------------
+// Bytes of one block: K and V of bs positions of every KV head of every layer.
+int64_t block_bytes(const Dims &d, int bs) { return 2 * (int64_t)d.NL * bs * d.Hkv * d.hd * d.es; }
+
+std::string check_paging(const Dims &d, const llm_paging *pg, bool dry)
+{
+    if (!pg) return "paging is NULL";
+    const int bs = pg->block_size;
+    if (bs < 32 || bs > (1 << 16) || (bs & (bs - 1))) return "block_size must be a power of two in [32, 65536]";
+    const int64_t cap = (int64_t)d.maxB * ((d.S + bs - 1) / bs);
+    if (pg->num_blocks < 0 || pg->num_blocks > cap)
+        return "num_blocks must be in [0, max_batch_size * ceil(max_seq_len / block_size)]";
+    if (pg->num_blocks == 0) {
+        if (dry) return "a dry handle needs num_blocks > 0";
+        if (!(pg->gpu_memory_utilization > 0.f && pg->gpu_memory_utilization <= 1.f))
+            return "gpu_memory_utilization must be in (0, 1]";
+    }
+    return "";
+}
+
+// Host bookkeeping of a pool of n blocks, every block free.
+void init_pages(llm_t *h, int n)
+{
+    h->kv_blocks = n;
+    h->btab.assign((size_t)h->d.maxB * h->bt_ld, -1);
+    h->owner.assign(n, -1);
+    h->free_ids.clear();
+    for (int i = 0; i < n; i++) h->free_ids.insert(h->free_ids.end(), i);
+    h->btab_dirty = true;
+}
+
+// The pool: num_blocks blocks, or with num_blocks == 0 as many as the
+// budget allows: total * utilisation - memory in use once everything else,
+// including the activation workspace of the largest pass, is allocated
+// (the transient peak of a forward pass is reserved before measuring).
+// More blocks than every row at max_seq_len could hold are never taken.
+int alloc_pool(llm_t *h)
+{
+    const Dims &d = h->d;
+    const int64_t per_block = block_bytes(d, h->bs), cap = (int64_t)d.maxB * h->bt_ld;
+    int64_t n = h->kv_blocks;
+    if (n == 0) {
+        int rc = ensure_ws(h, (int64_t)d.maxB * d.S);
+        if (rc) return rc;
+        size_t fr = 0, tot = 0;
+        HIPC(h, hipMemGetInfo(&fr, &tot));
+        const double budget = (double)tot * h->kv_util - (double)(tot - fr);
+        n = budget > 0 ? (int64_t)(budget / (double)per_block) : 0;
+        if (n < 1) return fail(h, LLM_ENOMEM, "the memory budget leaves no room for one KV block");
+        n = std::min(n, cap);
+    }
+    void *p = nullptr;
+    h->kv_layer_bytes = per_block / d.NL * n;
+    HIPM(h, hipMalloc(&p, h->kv_layer_bytes * d.NL));
+    h->kv = (char *)p;
+    HIPC(h, launch_zero_bytes(h->kv, h->kv_layer_bytes * d.NL, h->stream));
+    init_pages(h, (int)n);  // sizes the host tables
+    const size_t tb = h->btab.size() * sizeof(int);
+    HIPM(h, hipMalloc(&p, tb));
+    h->btab_d = (int *)p;
+    HIPM(h, hipHostMalloc(&p, tb, hipHostMallocDefault));
+    h->btab_stage = (int *)p;
+    HIPC(h, hipEventCreateWithFlags(&h->btab_ev, hipEventDisableTiming));
+    return LLM_OK;
+}
+
+// Give every row b < B blocks for positions [0, end[b]) after checking that
+// the positions [0, read_end[b]) it reads are held; with release_rest the
+// blocks of rows >= B are returned to the pool first (a prefill from position
+// 0 ends those rows).  All or nothing: on error no table changes.
+int kv_reserve(llm_t *h, int B, const std::vector<int> &read_end, const std::vector<int> &end, bool release_rest)
+{
+    if (!h->bs) return LLM_OK;
+    const int ld = h->bt_ld;
+    int64_t avail = (int64_t)h->free_ids.size(), need = 0;
+    if (release_rest)
+        for (size_t i = (size_t)B * ld; i < h->btab.size(); i++) avail += h->btab[i] >= 0;
+    for (int b = 0; b < B; b++) {
+        const int nr = (read_end[b] + h->bs - 1) >> h->bshift, ne = (end[b] + h->bs - 1) >> h->bshift;
+        for (int i = 0; i < nr; i++)
+            if (h->btab[(size_t)b * ld + i] < 0)
+                return fail(h, LLM_ESTATE, "row " + std::to_string(b) + " holds no block for cached positions it reads");
+        for (int i = nr; i < ne; i++) need += h->btab[(size_t)b * ld + i] < 0;
+    }
+    if (need > avail)
+        return fail(h, LLM_ENOMEM, "KV block pool exhausted: " + std::to_string(need) + " blocks needed, " +
+                                       std::to_string(avail) + " free");
+    if (release_rest)
+        for (size_t i = (size_t)B * ld; i < h->btab.size(); i++)
+            if (h->btab[i] >= 0) {
+                h->owner[h->btab[i]] = -1;
+                h->free_ids.insert(h->btab[i]);
+                h->btab[i] = -1;
+                h->btab_dirty = true;
+            }
+    for (int b = 0; b < B; b++) {
+        const int ne = (end[b] + h->bs - 1) >> h->bshift;
+        for (int i = 0; i < ne; i++) {
+            int &e = h->btab[(size_t)b * ld + i];
+            if (e >= 0) continue;
+            e = *h->free_ids.begin();
+            h->free_ids.erase(h->free_ids.begin());
+            h->owner[e] = b;
+            h->btab_dirty = true;
+        }
+    }
+    return LLM_OK;
+}
+
+// Same positions for every row b < B.
+int kv_reserve_uniform(llm_t *h, int B, int read_end, int end, bool release_rest)
+{
+    return kv_reserve(h, B, std::vector<int>(B, read_end), std::vector<int>(B, end), release_rest);
+}
+
+// Bring the device block tables up to date (outside any graph capture).
+int kv_upload(llm_t *h)
+{
+    if (!h->bs || h->dry || !h->btab_dirty) return LLM_OK;
+    HIPC(h, hipEventSynchronize(h->btab_ev));  // the previous copy has read the staging buffer
+    const size_t tb = h->btab.size() * sizeof(int);
+    memcpy(h->btab_stage, h->btab.data(), tb);
+    HIPC(h, hipMemcpyAsync(h->btab_d, h->btab_stage, tb, hipMemcpyHostToDevice, h->stream));
+    HIPC(h, hipEventRecord(h->btab_ev, h->stream));
+    h->btab_dirty = false;
+    return LLM_OK;
+}
+
+KvPages kv_pages(const llm_t *h)
+{
+    KvPages pg{};
+    if (h->bs) {
+        pg.tab = h->btab_d;
+        pg.ld = h->bt_ld;
+        pg.shift = h->bshift;
+    }
+    return pg;
+}
+
+// Positions per cache stream: the block size of a paged cache, else max_seq_len.
+int stream_len(const llm_t *h) { return h->bs ? h->bs : h->d.S; }
 
 int64_t mat_rows(const Dims &d, int mat)
 {
@@ -375,7 +531,8 @@ hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused)
         eq.pos_rows = ps.pos_rows;
         eq.rowmap = ps.rowmap;
         eq.T = ps.T;
-        eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = d.S;
+        eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = stream_len(h);
+        eq.pg = kv_pages(h);
         const char *nw = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
         return fused ? run_linear(h, l, MAT_QKV, h->x, d.D, M, eq, nw)
                      : run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq, nullptr, lay);
@@ -434,6 +591,8 @@ hipError_t forward(llm_t *h, const Pass &ps, Prof *pf = nullptr)
         AttnArgs aa{};
         aa.q = h->q; aa.kcache = layer_kc(h, l); aa.vcache = layer_vc(h, l); aa.out = h->o;
         aa.B = B; aa.T = ps.rowmap ? ps.Tmax : ps.T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
+        aa.Sb = stream_len(h);
+        aa.pg = kv_pages(h);
         aa.pos_dev = ps.pos_dev; aa.pos_imm = ps.pos0;
         aa.pos_rows = ps.pos_rows;
         aa.cu = ps.cu;
@@ -536,11 +695,14 @@ int create_impl(llm_t *h, uint64_t seed)
     h->emb = (char *)p;
     HIPM(h, hipMalloc(&p, align256((int64_t)(2 * d.NL + 1) * d.D * d.es)));
     h->norm_w = (char *)p;
-    // static KV cache (walkthrough section 3.1), zeroed
-    h->kv_layer_bytes = 2 * (int64_t)d.maxB * d.Hkv * d.S * d.hd * d.es;
-    HIPM(h, hipMalloc(&p, h->kv_layer_bytes * d.NL));
-    h->kv = (char *)p;
-    HIPC(h, launch_zero_bytes(h->kv, h->kv_layer_bytes * d.NL, h->stream));
+    // static KV cache (walkthrough section 3.1), zeroed; a paged pool is
+    // allocated last, from what the rest leaves
+    if (!h->bs) {
+        h->kv_layer_bytes = 2 * (int64_t)d.maxB * d.Hkv * d.S * d.hd * d.es;
+        HIPM(h, hipMalloc(&p, h->kv_layer_bytes * d.NL));
+        h->kv = (char *)p;
+        HIPC(h, launch_zero_bytes(h->kv, h->kv_layer_bytes * d.NL, h->stream));
+    }
     // RoPE table
     std::vector<float> rt;
     rope_table_host(d.hd, d.S, h->p.rope_theta, rt);
@@ -567,6 +729,7 @@ int create_impl(llm_t *h, uint64_t seed)
     if (rc) return rc;
     rc = build_weights(h, seed);
     if (rc) return rc;
+    if (h->bs && (rc = alloc_pool(h))) return rc;
     HIPC(h, hipStreamSynchronize(h->stream));
     return LLM_OK;
 }
@@ -576,9 +739,11 @@ void release(llm_t *h)
     if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
     if (h->gexec_rows) (void)hipGraphExecDestroy(h->gexec_rows);
     void *bufs[] = {h->wts, h->emb, h->norm_w, h->kv, h->rope, h->tok, h->logits, h->probs,
-                    h->pos_dev, h->ws};
+                    h->pos_dev, h->ws, h->btab_d};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
+    if (h->btab_stage) (void)hipHostFree(h->btab_stage);
+    if (h->btab_ev) (void)hipEventDestroy(h->btab_ev);
     if (h->own_stream && h->stream) (void)hipStreamDestroy(h->stream);
 }
 
@@ -600,6 +765,7 @@ int prefill_common(llm_t *h, int B, int T, int start = 0)
     if (!h->dry) {
         int rc = ensure_ws(h, (int64_t)B * T);
         if (rc) return rc;
+        if ((rc = kv_upload(h))) return rc;
         hipError_t e = forward(h, uniform_pass(B, T, nullptr, start));
         rc = after_forward(h, e);
         if (rc) return rc;
@@ -695,6 +861,7 @@ int varlen_common(llm_t *h, const int32_t *lens, int B, const std::vector<int2> 
     if (!h->dry) {
         int rc = ensure_ws(h, M);  // (callers run it before staging tokens as well)
         if (rc) return rc;
+        if ((rc = kv_upload(h))) return rc;
         HIPC(h, hipMemcpyAsync(h->rowmap, rowmap.data(), (size_t)M * sizeof(int2), hipMemcpyHostToDevice, h->stream));
         HIPC(h, hipMemcpyAsync(h->cu, cu_last.data(), cu_last.size() * sizeof(int), hipMemcpyHostToDevice, h->stream));
         std::vector<int> last(B);
@@ -737,6 +904,8 @@ int varlen_common(llm_t *h, const int32_t *lens, int B, const std::vector<int2> 
 // tokens at positions 0..T-1, else a decode step at prev_pos.
 int profiled_forward(llm_t *h, int B, int T, int prev_pos, int reps, float *ms_out)
 {
+    int rc = kv_upload(h);
+    if (rc) return rc;
     Prof pf;
     double acc[PC_N] = {0};
     hipError_t e = hipSuccess;
@@ -803,31 +972,49 @@ static llm_t *new_handle(const llm_params *p, const Dims &d)
     return h;
 }
 
-int llm_create_dry(const llm_params *p, llm_t **out)
+// Set up the paged-cache fields of a new handle (sizes only).
+static void set_paging(llm_t *h, const llm_paging *pg)
+{
+    h->bs = pg->block_size;
+    h->bshift = 0;
+    while ((1 << h->bshift) < h->bs) h->bshift++;
+    h->bt_ld = (h->d.S + h->bs - 1) / h->bs;
+    h->kv_blocks = pg->num_blocks;
+    h->kv_util = pg->gpu_memory_utilization;
+}
+
+static int create_dry(const llm_params *p, const llm_paging *pg, llm_t **out)
 {
     if (!out) return LLM_EINVAL;
     *out = nullptr;
     Dims d;
     if (!check(p, &d).empty()) return LLM_EINVAL;
+    if (pg && !check_paging(d, pg, true).empty()) return LLM_EINVAL;
     llm_t *h = new_handle(p, d);
     if (!h) return LLM_ENOMEM;
     h->dry = true;
+    if (pg) {
+        set_paging(h, pg);
+        init_pages(h, pg->num_blocks);
+    }
     *out = h;
     return LLM_OK;
 }
 
-int llm_create(const llm_params *p, uint64_t seed, void *hip_stream, llm_t **out)
+static int create(const llm_params *p, const llm_paging *pg, uint64_t seed, void *hip_stream, llm_t **out)
 {
     if (!out) return LLM_EINVAL;
     *out = nullptr;
     Dims d;
     std::string why = check(p, &d);
+    if (why.empty() && pg) why = check_paging(d, pg, false);
     if (!why.empty()) {
         fprintf(stderr, "llm_create: %s\n", why.c_str());
         return LLM_EINVAL;
     }
     llm_t *h = new_handle(p, d);
     if (!h) return LLM_ENOMEM;
+    if (pg) set_paging(h, pg);
     if (hip_stream) {
         h->stream = (hipStream_t)hip_stream;
     } else {
@@ -846,6 +1033,85 @@ int llm_create(const llm_params *p, uint64_t seed, void *hip_stream, llm_t **out
         return rc;
     }
     *out = h;
+    return LLM_OK;
+}
+
+int llm_create_dry(const llm_params *p, llm_t **out) { return create_dry(p, nullptr, out); }
+
+int llm_create(const llm_params *p, uint64_t seed, void *hip_stream, llm_t **out)
+{
+    return create(p, nullptr, seed, hip_stream, out);
+}
+
+int64_t llm_kv_block_bytes(const llm_params *p, int32_t block_size)
+{
+    Dims d;
+    if (!check(p, &d).empty() || block_size < 1) return -1;
+    return block_bytes(d, block_size);
+}
+
+int llm_create_paged(const llm_params *p, const llm_paging *pg, uint64_t seed, void *hip_stream, llm_t **out)
+{
+    if (!pg) {
+        if (out) *out = nullptr;
+        return LLM_EINVAL;
+    }
+    return create(p, pg, seed, hip_stream, out);
+}
+
+int llm_create_paged_dry(const llm_params *p, const llm_paging *pg, llm_t **out)
+{
+    if (!pg) {
+        if (out) *out = nullptr;
+        return LLM_EINVAL;
+    }
+    return create_dry(p, pg, out);
+}
+
+int32_t llm_kv_num_blocks(const llm_t *h) { return h && h->bs ? h->kv_blocks : 0; }
+
+int32_t llm_kv_free_blocks(const llm_t *h) { return h && h->bs ? (int32_t)h->free_ids.size() : 0; }
+
+int32_t llm_kv_table_width(const llm_t *h) { return h && h->bs ? h->bt_ld : 0; }
+
+int llm_kv_block_table(llm_t *h, int32_t row, int32_t *out, int32_t n)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!h->bs) return fail(h, LLM_EINVAL, "not a paged handle");
+    if (row < 0 || row >= h->d.maxB) return fail(h, LLM_EINVAL, "row must be in [0, max_batch_size)");
+    if (!out || n < 0 || n > h->bt_ld) return fail(h, LLM_EINVAL, "n must be in [0, table width]");
+    memcpy(out, h->btab.data() + (size_t)row * h->bt_ld, (size_t)n * sizeof(int32_t));
+    return LLM_OK;
+}
+
+int llm_kv_set_block_table(llm_t *h, int32_t row, const int32_t *blocks, int32_t n)
+{
+    int rc = guard(h);
+    if (rc) return rc;
+    if (!h->bs) return fail(h, LLM_EINVAL, "not a paged handle");
+    if (row < 0 || row >= h->d.maxB) return fail(h, LLM_EINVAL, "row must be in [0, max_batch_size)");
+    if (n < 0 || n > h->bt_ld || (n > 0 && !blocks)) return fail(h, LLM_EINVAL, "n must be in [0, table width]");
+    std::set<int> seen;
+    for (int i = 0; i < n; i++) {
+        const int id = blocks[i];
+        if (id < 0 || id >= h->kv_blocks) return fail(h, LLM_EINVAL, "block id out of [0, num_blocks)");
+        if (!seen.insert(id).second) return fail(h, LLM_EINVAL, "a block id appears twice");
+        if (h->owner[id] >= 0 && h->owner[id] != row) return fail(h, LLM_EINVAL, "a block is held by another row");
+    }
+    int *t = h->btab.data() + (size_t)row * h->bt_ld;
+    for (int i = 0; i < h->bt_ld; i++)
+        if (t[i] >= 0) {
+            h->owner[t[i]] = -1;
+            h->free_ids.insert(t[i]);
+            t[i] = -1;
+        }
+    for (int i = 0; i < n; i++) {
+        t[i] = blocks[i];
+        h->owner[t[i]] = row;
+        h->free_ids.erase(t[i]);
+    }
+    h->btab_dirty = true;
     return LLM_OK;
 }
 
@@ -870,6 +1136,7 @@ int llm_prefill(llm_t *h, const int32_t *tokens, int32_t B, int32_t T)
     if ((rc = check_prefill_args(h, B, T))) return rc;
     if (!tokens) return fail(h, LLM_EINVAL, "tokens is NULL");
     if (!tokens_ok(tokens, (int64_t)B * T, h->d.V)) return fail(h, LLM_EINVAL, "token id out of [0, vocab)");
+    if ((rc = kv_reserve_uniform(h, B, 0, T, true))) return rc;
     if (!h->dry) {
         HIPC(h, hipMemcpy2DAsync(h->tok, (size_t)h->d.S * 4, tokens, (size_t)T * 4, (size_t)T * 4, B,
                                  hipMemcpyHostToDevice, h->stream));
@@ -885,6 +1152,7 @@ int llm_prefill_d(llm_t *h, const int32_t *tokens_d, int32_t B, int32_t T)
     if ((rc = check_prefill_args(h, B, T))) return rc;
     if (!tokens_d) return fail(h, LLM_EINVAL, "tokens is NULL");
     if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    if ((rc = kv_reserve_uniform(h, B, 0, T, true))) return rc;
     HIPC(h, hipMemcpy2DAsync(h->tok, (size_t)h->d.S * 4, tokens_d, (size_t)T * 4, (size_t)T * 4, B,
                              hipMemcpyDeviceToDevice, h->stream));
     return prefill_common(h, B, T);
@@ -897,6 +1165,7 @@ int llm_prefill_at(llm_t *h, int32_t start_pos, const int32_t *tokens, int32_t B
     if ((rc = check_prefill_args(h, B, T, start_pos))) return rc;
     if (!tokens) return fail(h, LLM_EINVAL, "tokens is NULL");
     if (!tokens_ok(tokens, (int64_t)B * T, h->d.V)) return fail(h, LLM_EINVAL, "token id out of [0, vocab)");
+    if ((rc = kv_reserve_uniform(h, B, start_pos, start_pos + T, start_pos == 0))) return rc;
     if (!h->dry) {
         HIPC(h, hipMemcpy2DAsync(h->tok + start_pos, (size_t)h->d.S * 4, tokens, (size_t)T * 4, (size_t)T * 4, B,
                                  hipMemcpyHostToDevice, h->stream));
@@ -912,6 +1181,7 @@ int llm_prefill_at_d(llm_t *h, int32_t start_pos, const int32_t *tokens_d, int32
     if ((rc = check_prefill_args(h, B, T, start_pos))) return rc;
     if (!tokens_d) return fail(h, LLM_EINVAL, "tokens is NULL");
     if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    if ((rc = kv_reserve_uniform(h, B, start_pos, start_pos + T, start_pos == 0))) return rc;
     HIPC(h, hipMemcpy2DAsync(h->tok + start_pos, (size_t)h->d.S * 4, tokens_d, (size_t)T * 4, (size_t)T * 4, B,
                              hipMemcpyDeviceToDevice, h->stream));
     return prefill_common(h, B, T, start_pos);
@@ -927,6 +1197,7 @@ int llm_prefill_varlen(llm_t *h, const int32_t *tokens, const int32_t *lens, int
     if ((rc = prep_varlen(h, lens, B, rowmap, cu_last, &M, &Tmax))) return rc;
     if (!tokens) return fail(h, LLM_EINVAL, "tokens is NULL");
     if (!tokens_ok(tokens, M, h->d.V)) return fail(h, LLM_EINVAL, "token id out of [0, vocab)");
+    if ((rc = kv_reserve(h, B, std::vector<int>(B, 0), std::vector<int>(lens, lens + B), true))) return rc;
     if (!h->dry) {
         if ((rc = ensure_ws(h, M))) return rc;
         HIPC(h, hipMemcpyAsync(h->vtok, tokens, (size_t)M * 4, hipMemcpyHostToDevice, h->stream));
@@ -944,6 +1215,7 @@ int llm_prefill_varlen_d(llm_t *h, const int32_t *tokens_d, const int32_t *lens,
     if ((rc = prep_varlen(h, lens, B, rowmap, cu_last, &M, &Tmax))) return rc;
     if (!tokens_d) return fail(h, LLM_EINVAL, "tokens is NULL");
     if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    if ((rc = kv_reserve(h, B, std::vector<int>(B, 0), std::vector<int>(lens, lens + B), true))) return rc;
     if ((rc = ensure_ws(h, M))) return rc;
     HIPC(h, hipMemcpyAsync(h->vtok, tokens_d, (size_t)M * 4, hipMemcpyDeviceToDevice, h->stream));
     return varlen_common(h, lens, B, rowmap, cu_last, M, Tmax);
@@ -959,7 +1231,16 @@ int llm_decode_rows(llm_t *h)
         if (h->row_last[b] + 1 >= h->d.S) return fail(h, LLM_EINVAL, "a row has reached max_seq_len");
         if (!h->row_next[b]) return fail(h, LLM_ESTATE, "a row's next token column has not been written");
     }
+    {
+        std::vector<int> rd(B), en(B);
+        for (int b = 0; b < B; b++) {
+            rd[b] = h->row_last[b] + 1;
+            en[b] = h->row_last[b] + 2;
+        }
+        if ((rc = kv_reserve(h, B, rd, en, false))) return rc;
+    }
     if (!h->dry) {
+        if ((rc = kv_upload(h))) return rc;
         // each row moves to its next position, then the step runs at pos_rows[b]
         HIPC(h, launch_inc_ints(h->pos_rows, B, h->stream));
         Pass ps;
@@ -1031,7 +1312,9 @@ int llm_decode(llm_t *h, int32_t prev_pos)
     if (prev_pos < 1 || prev_pos >= h->d.S) return fail(h, LLM_EINVAL, "prev_pos must be in [1, max_seq_len)");
     if (prev_pos > h->last_pos + 1) return fail(h, LLM_ESTATE, "prev_pos skips positions whose KV is not written");
     if (!h->col_written[prev_pos]) return fail(h, LLM_ESTATE, "token column prev_pos has not been written");
+    if ((rc = kv_reserve_uniform(h, h->cur_B, prev_pos, prev_pos + 1, false))) return rc;
     if (!h->dry) {
+        if ((rc = kv_upload(h))) return rc;
         HIPC(h, launch_set_int(h->pos_dev, prev_pos, h->stream));
         const int B = h->cur_B;
         if (h->use_graph) {
@@ -1141,6 +1424,7 @@ int llm_profile_decode(llm_t *h, int32_t prev_pos, int32_t reps, float *ms_out)
     if (prev_pos < 1 || prev_pos >= h->d.S) return fail(h, LLM_EINVAL, "prev_pos must be in [1, max_seq_len)");
     if (prev_pos > h->last_pos + 1) return fail(h, LLM_ESTATE, "prev_pos skips positions whose KV is not written");
     if (!h->col_written[prev_pos]) return fail(h, LLM_ESTATE, "token column prev_pos has not been written");
+    if ((rc = kv_reserve_uniform(h, h->cur_B, prev_pos, prev_pos + 1, false))) return rc;
     rc = profiled_forward(h, h->cur_B, 1, prev_pos, reps, ms_out);
     if (rc) return rc;
     h->last_pos = prev_pos;
@@ -1155,6 +1439,7 @@ int llm_profile_prefill(llm_t *h, const int32_t *tokens_d, int32_t B, int32_t T,
     if ((rc = check_prefill_args(h, B, T))) return rc;
     if (!tokens_d || !ms_out || reps < 1) return fail(h, LLM_EINVAL, "bad arguments");
     if (h->dry) return fail(h, LLM_ESTATE, "dry handle has no device memory");
+    if ((rc = kv_reserve_uniform(h, B, 0, T, true))) return rc;
     HIPC(h, hipMemcpy2DAsync(h->tok, (size_t)h->d.S * 4, tokens_d, (size_t)T * 4, (size_t)T * 4, B,
                              hipMemcpyDeviceToDevice, h->stream));
     if ((rc = ensure_ws(h, (int64_t)B * T))) return rc;
@@ -1202,6 +1487,8 @@ int llm_profile_projections(llm_t *h, int32_t reps, float *us_out)
     if (h->d.dtype != LLM_F16) return fail(h, LLM_EINVAL, "projection timing is for fp16 models");
     if (!h->prefilled) return fail(h, LLM_ESTATE, "projection timing before prefill");
     if (h->rows_mode) return fail(h, LLM_ESTATE, "rows are at different positions");
+    if ((rc = kv_reserve_uniform(h, h->cur_B, h->last_pos + 1, h->last_pos + 1, false))) return rc;
+    if ((rc = kv_upload(h))) return rc;
     const bool fused = fuse_norm(h, h->cur_B);
     hipEvent_t ev[2] = {nullptr, nullptr};
     hipError_t e = hipEventCreate(&ev[0]);
@@ -1379,8 +1666,10 @@ int llm_op_kv_write(llm_t *h, int32_t layer, const void *k_d, const void *v_d, i
     const Dims &d = h->d;
     if (!k_d || !v_d || layer < 0 || layer >= d.NL || B < 1 || B > d.maxB || T < 1 || pos0 < 0 || pos0 + T > d.S)
         return fail(h, LLM_EINVAL, "bad arguments");
-    return op_end(h, launch_kv_write(k_d, v_d, B, T, pos0, d.Hkv, d.hd, d.S, d.dtype, layer_kc(h, layer),
-                                     layer_vc(h, layer), h->stream));
+    if ((rc = kv_reserve_uniform(h, B, 0, pos0 + T, false))) return rc;
+    if ((rc = kv_upload(h))) return rc;
+    return op_end(h, launch_kv_write(k_d, v_d, B, T, pos0, d.Hkv, d.hd, stream_len(h), kv_pages(h), d.dtype,
+                                     layer_kc(h, layer), layer_vc(h, layer), h->stream));
 }
 
 int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_t T, int32_t pos0, void *out_d)
@@ -1390,9 +1679,13 @@ int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_
     const Dims &d = h->d;
     if (!q_d || !out_d || layer < 0 || layer >= d.NL || B < 1 || B > d.maxB || T < 1 || pos0 < 0 || pos0 + T > d.S)
         return fail(h, LLM_EINVAL, "bad arguments");
+    if ((rc = kv_reserve_uniform(h, B, pos0 + T, pos0 + T, false))) return rc;
+    if ((rc = kv_upload(h))) return rc;
     AttnArgs aa{};
     aa.q = q_d; aa.kcache = layer_kc(h, layer); aa.vcache = layer_vc(h, layer); aa.out = out_d;
     aa.B = B; aa.T = T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
+    aa.Sb = stream_len(h);
+    aa.pg = kv_pages(h);
     aa.pos_dev = nullptr; aa.pos_imm = pos0;
     hipError_t e;
     if (d.dtype == LLM_F32) e = launch_attn_f32(aa, h->stream);

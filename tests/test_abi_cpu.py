@@ -189,3 +189,82 @@ def test_dry_handle_last_slot():
     with pytest.raises(b.LlmError):
         h.decode(w.max_seq_len)
     h.destroy()
+
+
+def _code(fn, *a):
+    try:
+        fn(*a)
+        return b.LLM_OK
+    except b.LlmError as e:
+        return e.code
+
+
+def test_paging_parameters():
+    """Block size, pool size and budget checks; block bytes follow
+    2 * layers * block * kv_heads * head_dim * element size."""
+    w = configs.TINY
+    p = b.params_for(w, max_batch_size=3, max_seq_len=256)
+    hd = w.dim // w.n_heads
+    assert b.llm_kv_block_bytes(p, 32) == 2 * w.n_layers * 32 * w.n_kv_heads * hd * 4
+    for bs, n in [(16, 4), (48, 4), (131072, 4), (32, -1), (32, 3 * 8 + 1), (32, 0)]:
+        with pytest.raises(b.LlmError) as e:
+            b.llm_create_paged_dry(p, b.make_paging(bs, n))
+        assert e.value.code == b.LLM_EINVAL, (bs, n)
+    h = b.llm_create_paged_dry(p, b.make_paging(64, 3 * 4))   # the largest pool: every row at 256
+    assert (h.kv_num_blocks(), h.kv_free_blocks(), h.kv_table_width()) == (12, 12, 4)
+    h.destroy()
+    s = b.llm_create_dry(p)
+    assert (s.kv_num_blocks(), s.kv_table_width()) == (0, 0)
+    assert _code(s.kv_set_block_table, 0, [0]) == b.LLM_EINVAL       # not a paged handle
+    s.destroy()
+
+
+def test_paged_block_bookkeeping():
+    """Blocks are handed out lowest id first as passes reach new positions,
+    kept by their row, returned by a prefill from position 0 (rows >= B) or
+    an explicit table; an exhausted pool and uncovered cached positions are
+    refused before anything changes."""
+    w = configs.TINY
+    p = b.params_for(w, max_batch_size=3, max_seq_len=256)
+    h = b.llm_create_paged_dry(p, b.make_paging(32, 10))
+    tab = lambda r: [int(x) for x in h.kv_block_table(r) if x >= 0]
+    zeros = lambda B, T: np.zeros((B, T), np.int32)
+    assert _code(h.prefill, zeros(3, 40)) == b.LLM_OK                 # 2 blocks per row
+    assert [tab(r) for r in range(3)] == [[0, 1], [2, 3], [4, 5]]
+    for pos in range(40, 64):
+        assert _code(h.set_tokens, pos, np.ones(3, np.int32)) == b.LLM_OK
+        assert _code(h.decode, pos) == b.LLM_OK
+    assert h.kv_free_blocks() == 4
+    assert _code(h.set_tokens, 64, np.ones(3, np.int32)) == b.LLM_OK
+    assert _code(h.decode, 64) == b.LLM_OK                            # a third block each
+    assert [tab(r) for r in range(3)] == [[0, 1, 6], [2, 3, 7], [4, 5, 8]]
+    for pos in range(65, 96):
+        assert _code(h.set_tokens, pos, np.ones(3, np.int32)) == b.LLM_OK
+        assert _code(h.decode, pos) == b.LLM_OK
+    assert _code(h.set_tokens, 96, np.ones(3, np.int32)) == b.LLM_OK
+    assert _code(h.decode, 96) == b.LLM_ENOMEM                        # 3 needed, 1 free
+    assert h.kv_free_blocks() == 1 and tab(0) == [0, 1, 6]             # nothing changed
+    assert _code(h.decode, 95) == b.LLM_OK                            # recomputing a position is fine
+    h.kv_set_block_table(2, [])                                       # release row 2
+    assert h.kv_free_blocks() == 4
+    assert _code(h.decode, 96) == b.LLM_ESTATE                        # row 2's cache is gone
+    # validation of explicit tables
+    assert _code(h.kv_set_block_table, 2, [9, 9]) == b.LLM_EINVAL     # twice
+    assert _code(h.kv_set_block_table, 2, [10]) == b.LLM_EINVAL       # out of the pool
+    assert _code(h.kv_set_block_table, 2, [0]) == b.LLM_EINVAL        # row 0 holds it
+    assert _code(h.kv_set_block_table, 2, list(range(4, 9)) + [9] * 4) == b.LLM_EINVAL  # wider than the table
+    assert _code(h.kv_set_block_table, 3, [9]) == b.LLM_EINVAL        # no such row
+    h.kv_set_block_table(2, [9, 5])
+    assert tab(2) == [9, 5] and h.kv_free_blocks() == 2
+    h.kv_set_block_table(0, [6, 1, 0])                                # a row may reorder its own blocks
+    assert tab(0) == [6, 1, 0]
+    # a prefill from 0 of two rows releases row 2 and extends rows 0 and 1
+    assert _code(h.prefill, zeros(2, 100)) == b.LLM_OK
+    assert [tab(r) for r in range(3)] == [[6, 1, 0, 4], [2, 3, 7, 5], []]
+    assert h.kv_free_blocks() == 2
+    assert _code(h.prefill_at, 100, zeros(2, 100)) == b.LLM_ENOMEM    # 3 more each, 2 free
+    assert _code(h.prefill_at, 100, zeros(2, 28)) == b.LLM_OK         # stays in block 3
+    # varlen: rows keep their blocks, rows past B are released first
+    assert _code(h.prefill_varlen, [np.zeros(200, np.int32)]) == b.LLM_OK
+    assert tab(0) == [6, 1, 0, 4, 2, 3, 5] and tab(1) == [] and h.kv_free_blocks() == 3
+    h.destroy()
