@@ -108,6 +108,9 @@ def main():
                     choices=sorted(k for k, v in configs.WORKLOADS.items() if v.dtype == configs.F16))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-reps", type=int, default=5)
+    ap.add_argument("--kv-block", type=int, default=0,
+                    help="run with a paged KV cache of blocks of this many positions (a pool with room "
+                         "for every row at max_seq_len) instead of the static cache")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device to device three times (a known-size kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -154,7 +157,11 @@ def main():
     temp, top_p = w.temperature, w.top_p
 
     t_create = time.perf_counter()
-    h = Bd.llm_create(Bd.params_for(w), w.weight_seed)
+    if args.kv_block:
+        nblk = B * -(-w.max_seq_len // args.kv_block)
+        h = Bd.llm_create_paged(Bd.params_for(w), Bd.make_paging(args.kv_block, nblk), w.weight_seed)
+    else:
+        h = Bd.llm_create(Bd.params_for(w), w.weight_seed)
     t_create = time.perf_counter() - t_create
     stream = torch.cuda.ExternalStream(h.stream())
 
@@ -253,7 +260,8 @@ def main():
         "config": {"workload": w.name, "batch": B, "prompt": T0 if not ragged else f"ragged {w.prompt_range}, prefill {T0}",
                    "decode_steps": steps, "temperature": temp, "top_p": top_p,
                    "layers": w.n_layers, "dim": w.dim, "heads": f"{w.n_heads}/{w.n_kv_heads}",
-                   "ffn": w.ffn_hidden(), "vocab": w.vocab_size, "max_seq_len": S},
+                   "ffn": w.ffn_hidden(), "vocab": w.vocab_size, "max_seq_len": S,
+                   "kv_cache": f"paged, blocks of {args.kv_block}" if args.kv_block else "static"},
         "roofline": {"bound": "hbm",
                      "kernel": "gemm_skinny_kernel (decode weight products: wq|wk|wv, wo, w1|w3, w2, head)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

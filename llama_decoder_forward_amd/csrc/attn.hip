@@ -53,7 +53,9 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
     __shared__ floatx4 so[NW / 2][8][64];
     __shared__ float sm[NW / 2][16], sl[NW / 2][16];
     const int bk = blockIdx.x, b = bk / Hkv, kvh = bk % Hkv;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index is uniform across the wave: in a scalar register, so the
+    // step loop and its block lookups branch on scalars
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int L = (pos_rows ? pos_rows[b] : (pos_dev ? *pos_dev : pos_imm)) + 1;
     const int n_rep = H / Hkv;
     const int r = lane & 15, g = lane >> 4;
@@ -68,11 +70,25 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
 #pragma unroll
     for (int s = 0; s < 4; s++) qb[s] = qv ? *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g) : z;
 
+    // PAGED: lane j holds entries j and 64 + j of the row's block table (the
+    // entries its L positions use), so a step finds its block with a lane
+    // read instead of a memory load; entries from 128 on are loaded
+    int tv0 = 0, tv1 = 0;
+    if (PAGED) {
+        const int *trow = pg.tab + (int64_t)b * pg.ld;
+        const int nent = ((L - 1) >> pg.shift) + 1;
+        tv0 = lane < nent ? trow[lane] : 0;
+        tv1 = 64 + lane < nent ? trow[64 + lane] : 0;
+    }
     // element offset of the first key of 32-key step st in both K and V
     auto step_base = [&](int st) -> int64_t {
         const int k0 = 32 * st;
         if (PAGED) {
-            const int64_t blk = pg.tab[(int64_t)b * pg.ld + (k0 >> pg.shift)];
+            const int e = k0 >> pg.shift;
+            int64_t blk;
+            if (e < 64) blk = __builtin_amdgcn_readlane(tv0, e);
+            else if (e < 128) blk = __builtin_amdgcn_readlane(tv1, e - 64);
+            else blk = pg.tab[(int64_t)b * pg.ld + e];
             return (((blk * Hkv + kvh) << pg.shift) + (k0 & ((1 << pg.shift) - 1))) * hd;
         }
         return (((int64_t)b * Hkv + kvh) * S + k0) * hd;
