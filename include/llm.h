@@ -4,7 +4,8 @@
  * The library runs the decoder-only forward pass described in the
  * walkthrough "Meta Llama 源码深度剖析与生产应用教程" (section 2 data flow,
  * sections 3.2-3.8 for the layer) with the reference's static per-layer KV
- * cache (section 3.1), as a full-prompt causal prefill followed by one-token
+ * cache (section 3.1) or a paged block pool (nano-vllm notes, see "paged KV
+ * cache" below), as a full-prompt causal prefill followed by one-token
  * decode steps (section 4.2, and the course notes on generate, section 1),
  * and ends in last-position logits with greedy, temperature and top-p
  * sampling (section 4.3).  Every step runs in hand-written HIP kernels on one
