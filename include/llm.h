@@ -91,7 +91,13 @@ int llm_check_params(const llm_params *p);
  * are 1.  The KV cache is zeroed.  `hip_stream` is a hipStream_t to order all
  * work on, or NULL for a stream owned by the handle.
  * Errors: LLM_EINVAL (parameters), LLM_ENOMEM, LLM_EDEVICE.  On error *out is
- * NULL. */
+ * NULL.
+ * Environment read at creation: LLM_NO_GRAPH=1 runs decode steps eagerly
+ * instead of replaying a captured graph; LLM_FUSED_LAYER=1 runs every layer
+ * of a one-row fp16 decode step as one persistent launch (grid barriers
+ * between its phases; bit-identical results).  A grid barrier that does not
+ * settle raises a device flag instead of hanging; llm_get_logits and
+ * llm_sync then return LLM_EDEVICE. */
 int llm_create(const llm_params *p, uint64_t seed, void *hip_stream, llm_t **out);
 
 /* A handle that validates arguments and tracks state exactly like a real
@@ -307,7 +313,8 @@ int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_
  * milliseconds per step of each kernel class to ms_out[9]: 0 embedding,
  * 1 RMSNorm, 2 wq|wk|wv product (with RoPE and the KV write), 3 attention,
  * 4 wo product, 5 w1|w3 product (with SwiGLU), 6 w2 product, 7 output head,
- * 8 first-to-last event.  Same preconditions and effects as llm_decode;
+ * 8 first-to-last event (with LLM_FUSED_LAYER=1 and one row, class 2 holds
+ * the whole fused layer).  Same preconditions and effects as llm_decode;
  * synchronises. */
 int llm_profile_decode(llm_t *h, int32_t prev_pos, int32_t reps, float *ms_out);
 

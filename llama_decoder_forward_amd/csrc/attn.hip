@@ -16,6 +16,7 @@
 // 8g..8g+7 of the step, which is exactly the B-operand k-group of P^T, and
 // the matching A operand V^T[d][8g..8g+7] is one contiguous 16-byte load.
 #include "common.h"
+#include "attn_decode.h"
 
 namespace {
 
@@ -24,8 +25,6 @@ __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Key (0..31 within a step) held in row r of sub-tile t.
-__device__ __forceinline__ int perm_key(int t, int r) { return 8 * (r >> 2) + 4 * t + (r & 3); }
 
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp(m_old - m_new) is never NaN
 
@@ -49,178 +48,11 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
     int H, int Hkv, int S, KvPages pg, const int *pos_dev, int pos_imm, const int *pos_rows,
     half_t *__restrict__ out, int out_lay)
 {
-    constexpr int hd = 128;
     __shared__ floatx4 so[NW / 2][8][64];
     __shared__ float sm[NW / 2][16], sl[NW / 2][16];
     const int bk = blockIdx.x, b = bk / Hkv, kvh = bk % Hkv;
-    // the wave index is uniform across the wave: in a scalar register, so the
-    // step loop and its block lookups branch on scalars
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int L = (pos_rows ? pos_rows[b] : (pos_dev ? *pos_dev : pos_imm)) + 1;
-    const int n_rep = H / Hkv;
-    const int r = lane & 15, g = lane >> 4;
-    const bool qv = r < n_rep;
-    const int h = kvh * n_rep + r;
-    const float scale = 1.0f / sqrtf((float)hd);
-    const int nsteps = (L + 31) / 32;
-    const half8 z = {};
-
-    half8 qb[4];
-    const half_t *qrow = q + ((int64_t)b * H + (qv ? h : 0)) * hd;
-#pragma unroll
-    for (int s = 0; s < 4; s++) qb[s] = qv ? *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g) : z;
-
-    // PAGED: lane j holds entries j and 64 + j of the row's block table (the
-    // entries its L positions use), so a step finds its block with a lane
-    // read instead of a memory load; entries from 128 on are loaded
-    int tv0 = 0, tv1 = 0;
-    if (PAGED) {
-        const int *trow = pg.tab + (int64_t)b * pg.ld;
-        const int nent = ((L - 1) >> pg.shift) + 1;
-        tv0 = lane < nent ? trow[lane] : 0;
-        tv1 = 64 + lane < nent ? trow[64 + lane] : 0;
-    }
-    // element offset of the first key of 32-key step st in both K and V
-    auto step_base = [&](int st) -> int64_t {
-        const int k0 = 32 * st;
-        if (PAGED) {
-            const int e = k0 >> pg.shift;
-            int64_t blk;
-            if (e < 64) blk = __builtin_amdgcn_readlane(tv0, e);
-            else if (e < 128) blk = __builtin_amdgcn_readlane(tv1, e - 64);
-            else blk = pg.tab[(int64_t)b * pg.ld + e];
-            return (((blk * Hkv + kvh) << pg.shift) + (k0 & ((1 << pg.shift) - 1))) * hd;
-        }
-        return (((int64_t)b * Hkv + kvh) * S + k0) * hd;
-    };
-
-    floatx4 acc[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; dt++) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float mrun = kNegBig, lrun = 0.f;
-
-    // all K and V operands of a step are loaded before any of its arithmetic
-    auto load = [&](int st, int64_t base, half8 (&kf)[2][4], half8 (&vf)[8]) {
-        const int k0 = 32 * st;
-#pragma unroll
-        for (int t = 0; t < 2; t++) {
-            const int kp = perm_key(t, r);
-            const bool ok = k0 + kp < L;
-            const half_t *krow = kc + base + (ok ? kp : 0) * hd + 8 * g;
-#pragma unroll
-            for (int s = 0; s < 4; s++) kf[t][s] = ok ? *reinterpret_cast<const half8 *>(krow + 32 * s) : z;
-        }
-        const int kk = k0 + 8 * g;
-        const bool vok = kk + 8 <= L;
-        const half_t *vblk = vc + base + 8 * g;
-#pragma unroll
-        for (int dt = 0; dt < 8; dt++) {
-            const half_t *vrow = vblk + (16 * dt + r) * 32;
-            if (vok) {
-                vf[dt] = *reinterpret_cast<const half8 *>(vrow);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; e++) vf[dt][e] = (kk + e < L) ? vrow[e] : (half_t)0.f;
-            }
-        }
-    };
-    auto compute = [&](int st, const half8 (&kf)[2][4], const half8 (&vf)[8]) {
-        const int k0 = 32 * st;
-        floatx4 sc[2];
-#pragma unroll
-        for (int t = 0; t < 2; t++) {
-            floatx4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; s++) a = mfma16(kf[t][s], qb[s], a);
-            sc[t] = a;
-        }
-        float p[8];
-        float mx = kNegBig;
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int key = k0 + 8 * g + 4 * t + i;
-                float v = key < L ? sc[t][i] * scale : -INFINITY;
-                p[4 * t + i] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrun, mx);
-        const float fac = expf(mrun - mnew);
-        float ls = 0.f;
-        half8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            float ev = expf(p[e] - mnew);
-            ls += ev;
-            pb[e] = (half_t)ev;
-        }
-        ls += __shfl_xor(ls, 16);
-        ls += __shfl_xor(ls, 32);
-        lrun = lrun * fac + ls;
-        mrun = mnew;
-#pragma unroll
-        for (int dt = 0; dt < 8; dt++) acc[dt] = mfma16(vf[dt], pb, acc[dt] * fac);
-    };
-    half8 kf[2][4], vf[8];
-    int st = wave;
-    if (st < nsteps) load(st, step_base(st), kf, vf);
-    for (; st < nsteps; st += NW) {
-        const int nx = st + NW;
-        const int64_t nbase = nx < nsteps ? step_base(nx) : 0;
-        if (PF) {
-            half8 kn[2][4], vn[8];
-            if (nx < nsteps) load(nx, nbase, kn, vn);
-            compute(st, kf, vf);
-#pragma unroll
-            for (int t = 0; t < 2; t++)
-#pragma unroll
-                for (int s = 0; s < 4; s++) kf[t][s] = kn[t][s];
-#pragma unroll
-            for (int dt = 0; dt < 8; dt++) vf[dt] = vn[dt];
-        } else {
-            compute(st, kf, vf);
-            if (nx < nsteps) load(nx, nbase, kf, vf);
-        }
-    }
-
-    // merge: in each round the upper half of the live waves hands its state to
-    // the lower half (lane (r, g) holds O^T[16 dt + 4 g + i][head r])
-    for (int half = NW / 2; half >= 1; half >>= 1) {
-        if (wave >= half && wave < 2 * half) {
-#pragma unroll
-            for (int dt = 0; dt < 8; dt++) so[wave - half][dt][lane] = acc[dt];
-            if (g == 0) {
-                sm[wave - half][r] = mrun;
-                sl[wave - half][r] = lrun;
-            }
-        }
-        __syncthreads();
-        if (wave < half) {
-            const float mo = sm[wave][r], lo = sl[wave][r];
-            const float M = fmaxf(mrun, mo);
-            const float fa = expf(mrun - M), fb = expf(mo - M);
-#pragma unroll
-            for (int dt = 0; dt < 8; dt++) acc[dt] = acc[dt] * fa + so[wave][dt][lane] * fb;
-            lrun = lrun * fa + lo * fb;
-            mrun = M;
-        }
-        __syncthreads();
-    }
-    if (wave == 0 && qv) {
-        half_t *orow = out + ((int64_t)b * H + h) * hd;
-        const float inv = 1.0f / lrun;
-#pragma unroll
-        for (int dt = 0; dt < 8; dt++) {
-            half4 hv;
-            for (int i = 0; i < 4; i++) hv[i] = (half_t)(acc[dt][i] * inv);
-            const int c = 16 * dt + 4 * g;  // 4 consecutive columns inside one 8-column group
-            if (out_lay) *reinterpret_cast<half4 *>(out + act_offset(b, (int64_t)h * hd + c, (int64_t)H * hd, 0, out_lay)) = hv;
-            else *reinterpret_cast<half4 *>(orow + c) = hv;
-        }
-    }
+    adec::attn_decode_wg<NW, PF, PAGED, false>(q, kc, vc, H, Hkv, S, pg, b, kvh, L, out, out_lay, so, sm, sl);
 }
 
 // ---------------------------------------------------------------------------

@@ -45,6 +45,9 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
         break;
     }
     case EP_LOGITS: {
+        // the position a captured decode step reads moves to the next step
+        // (every earlier kernel of the step has read it)
+        if (ep.pos_advance && n0 == 0 && m == 0 && lane == 0) *ep.pos_advance += 1;
         if (!valid) break;
         float4 o = make_float4(r16(acc[0]), r16(acc[1]), r16(acc[2]), r16(acc[3]));
         *reinterpret_cast<float4 *>((float *)ep.out + (int64_t)m * ep.ldo + n) = o;
@@ -134,7 +137,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
                                                               const half_t *__restrict__ X,
                                                               int64_t ldx, int M, int N, int K,
                                                               Epilogue ep, const half_t *__restrict__ nw,
-                                                              float eps)
+                                                              float eps, const int32_t *__restrict__ gtok,
+                                                              int64_t gtok_ld, half_t *__restrict__ xres)
 {
     extern __shared__ half8 xs[];  // STAGE: [M][K/8]
     __shared__ floatx4 red[NW][TPB][TWO ? 2 : 1][64];
@@ -156,10 +160,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
 
     if (STAGE) {
         for (int m = 0; m < M; m++) {
+            // gtok: X is the embedding table and row m embeds token
+            // gtok[b][pos] of its (b, pos); work-group 0 also stores the row
+            // into the residual stream xres
+            const half_t *xrow = X + (int64_t)m * ldx;
+            if (gtok) {
+                int b, pos;
+                locate_row(m, ep.T, ep.pos_dev, ep.pos_imm, ep.pos_rows, ep.rowmap, b, pos);
+                xrow = X + (int64_t)gtok[(int64_t)b * gtok_ld + pos] * ldx;
+            }
             float ss = 0.f;
             for (int i = tid; i < K8; i += NW * 64) {
-                half8 v = reinterpret_cast<const half8 *>(X + (int64_t)m * ldx)[i];
+                half8 v = reinterpret_cast<const half8 *>(xrow)[i];
                 xs[m * K8 + i] = v;
+                if (gtok && blockIdx.x == 0) reinterpret_cast<half8 *>(xres + (int64_t)m * K)[i] = v;
                 if (NORM) {
 #pragma unroll
                     for (int e = 0; e < 8; e++) { float f = (float)v[e]; ss += f * f; }
@@ -552,6 +566,7 @@ __global__ void linear_f32_kernel(const float *W, const float *X, int64_t ldx, i
     case EP_STORE:
     case EP_LOGITS:
     case EP_RESID: {
+        if (ep.kind == EP_LOGITS && ep.pos_advance && unit == 0 && m == 0) *ep.pos_advance += 1;
         if (unit >= N) return;
         float a = dot_row_f32(W + (int64_t)unit * K, x, K);
         float *o = out + (int64_t)m * ep.ldo + unit;
@@ -612,25 +627,31 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
     if (a.M <= 0) return hipSuccess;
     const half_t *W = (const half_t *)a.W, *X = (const half_t *)a.X, *nw = (const half_t *)a.norm_w;
     if (nw && !skinny_can_normalise(a.M, a.K)) return hipErrorInvalidValue;
+    if (a.gather_tok && (!nw || a.x_lay != ACT_ROWS)) return hipErrorInvalidValue;  // the staged, normalising form only
     const dim3 blk(512);
     if (a.x_lay == 1 || a.x_lay == 2) {
         // fragment-major activations of a decode step, 2 < M <= 32
         if (nw || a.M > 16 * a.x_lay || a.x_lay > 2) return hipErrorInvalidValue;
         const int tiles = a.N / 16;
-        if (a.x_lay == 1)
+        if (a.x_lay == 1 && tiles < 1024 && tiles % 2 == 0)
+            // up to 16 rows, fewer than 1024 row blocks: two per work-group
+            // (measured on the 13B shapes: wo and w2 12% faster than one)
+            hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 2, false, false, false, true>), dim3(tiles / 2), blk, 0, s,
+                               W, X, 0, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
+        else if (a.x_lay == 1)
             hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, false, false, true>), dim3(tiles), blk, 0, s, W,
-                               X, 0, a.M, a.N, a.K, a.ep, nw, a.eps);
+                               X, 0, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
         else if (tiles >= 640 && tiles < 1024 && tiles % 4 == 0)
             // tall products: four row blocks per work-group share each activation fragment
             hipLaunchKernelGGL((gemm_skinny_kernel<8, 2, 4, true, false, false, true>), dim3(tiles / 4), blk, 0, s,
-                               W, X, 0, a.M, a.N, a.K, a.ep, nw, a.eps);
+                               W, X, 0, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
         else if (tiles >= 320 && tiles % 2 == 0)
             hipLaunchKernelGGL((gemm_skinny_kernel<8, 4, 2, true, false, false, true>), dim3(tiles / 2), blk, 0, s,
-                               W, X, 0, a.M, a.N, a.K, a.ep, nw, a.eps);
+                               W, X, 0, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
         else
             // few row blocks: one per work-group keeps every CU streaming
             hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, true, false, false, true>), dim3(tiles), blk, 0, s, W,
-                               X, 0, a.M, a.N, a.K, a.ep, nw, a.eps);
+                               X, 0, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
         return hipGetLastError();
     }
     if (a.x_lay == ACT_TILED) {
@@ -642,21 +663,21 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
         const size_t lds = (size_t)a.M * a.K * 2;
         if (nw)
             hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, true, true>), dim3(a.N / 16), blk, lds, s, W, X,
-                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
+                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
         else
             hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, true, false>), dim3(a.N / 16), blk, lds, s, W,
-                               X, a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
+                               X, a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
     } else if (a.M <= 16) {
         hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, false, false>), dim3(a.N / 16), blk, 0, s, W, X,
-                           a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
+                           a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
     } else if (a.M <= 32) {
         // two row blocks per work-group reuse each activation fragment twice
         if ((a.N / 16) % 2 == 0)
             hipLaunchKernelGGL((gemm_skinny_kernel<8, 4, 2, true, false, false>), dim3(a.N / 32), blk, 0, s, W, X,
-                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
+                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
         else
             hipLaunchKernelGGL((gemm_skinny_kernel<8, 4, 1, true, false, false>), dim3(a.N / 16), blk, 0, s, W, X,
-                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps);
+                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
     } else if (a.M < 1024) {
         int NB = (a.N + BIG_BN - 1) / BIG_BN, MB = (a.M + BIG_BM - 1) / BIG_BM;
         hipLaunchKernelGGL(gemm_big_kernel, dim3(NB * MB), dim3(256), 0, s, W, X, a.ldx, a.M, a.N, a.K, a.ep);

@@ -104,6 +104,7 @@ struct llm {
     int32_t *outtok = nullptr, *stage_i32 = nullptr;
     uint8_t *stage_mask = nullptr;
     int *pos_dev = nullptr;
+    int dev_pos = -1;         // what *pos_dev holds once the queued work has run (-1: unknown)
     int *pos_rows = nullptr;  // [maxB] per-row last written position (rows mode)
     int *cu = nullptr;        // [maxB + 1] varlen row starts, then [maxB] last packed rows
     // activations, sized for ws_rows rows
@@ -128,6 +129,10 @@ struct llm {
     hipGraphExec_t gexec_rows = nullptr;
     int graph_rows_B = -1;
     bool use_graph = true;
+    // one-row decode steps: each layer in one persistent launch (fp16)
+    bool use_fused = false;
+    int fused_G = 0;           // its work-groups: one per CU
+    unsigned *fbar = nullptr;  // barrier counters, one set of kFusedBarWords per layer, then the error flag
 };
 
 namespace {
@@ -165,6 +170,8 @@ int guard(llm_t *h)
     if (h->poisoned) return LLM_EDEVICE;
     return LLM_OK;
 }
+
+constexpr int kFusedBarWords = 8 * 32;  // eight group counters, one 128-byte line each
 
 char *layer_kc(llm_t *h, int l) { return h->kv + (int64_t)l * h->kv_layer_bytes; }
 char *layer_vc(llm_t *h, int l) { return h->kv + (int64_t)l * h->kv_layer_bytes + h->kv_layer_bytes / 2; }
@@ -386,9 +393,13 @@ const char *mat_ptr(llm_t *h, int layer, int mat)
 }
 
 hipError_t run_linear(llm_t *h, int layer, int mat, const void *X, int64_t ldx, int M,
-                      const Epilogue &ep, const void *norm_w = nullptr, int x_lay = ACT_ROWS)
+                      const Epilogue &ep, const void *norm_w = nullptr, int x_lay = ACT_ROWS,
+                      const int32_t *gather_tok = nullptr)
 {
     GemmArgs a{};
+    a.gather_tok = gather_tok;
+    a.gather_ld = h->d.S;
+    a.gather_out = h->x;
     a.W = mat_ptr(h, layer, mat);
     a.X = X;
     a.ldx = ldx;
@@ -421,6 +432,7 @@ struct Pass {
     const int2 *rowmap = nullptr;
     const int *cu = nullptr, *last_rows = nullptr;
     int Tmax = 0;
+    bool advance = false;  // the head's product moves *pos_dev on by one (captured decode steps)
     bool decode() const { return pos_dev || pos_rows; }
 };
 
@@ -534,6 +546,9 @@ hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused)
         eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = stream_len(h);
         eq.pg = kv_pages(h);
         const char *nw = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
+        // fused, layer 0: the product gathers the embedding rows itself and
+        // stores them into x (no embedding launch)
+        if (fused && l == 0) return run_linear(h, l, MAT_QKV, h->emb, d.D, M, eq, nw, ACT_ROWS, h->tok);
         return fused ? run_linear(h, l, MAT_QKV, h->x, d.D, M, eq, nw)
                      : run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq, nullptr, lay);
     }
@@ -551,6 +566,7 @@ hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused)
         int64_t ld = 0;
         const char *xl = head_rows(h, ps, &ld);
         Epilogue el = make_ep(EP_LOGITS, h->logits, d.V);
+        el.pos_advance = ps.advance ? h->pos_dev : nullptr;
         return fused ? run_linear(h, 0, MAT_HEAD, xl, ld, ps.B, el, nw)
                      : run_linear(h, 0, MAT_HEAD, h->xn, d.D, ps.B, el, nullptr, head_layout(lay));
     }
@@ -577,9 +593,32 @@ hipError_t forward(llm_t *h, const Pass &ps, Prof *pf = nullptr)
         TRY_RAW(x);                        \
         TRY_RAW(prof_end(pf, s));          \
     } while (0)
-    TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, M, ps.T, ps.pos_dev, ps.pos0, ps.pos_rows, ps.rowmap, d.D,
-                                d.dtype, h->x, s));
+    if (h->use_fused && ps.decode() && M == 1) {
+        // one row: every layer in one launch, then the final norm and the head
+        TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, M, ps.T, ps.pos_dev, ps.pos0, ps.pos_rows, ps.rowmap, d.D,
+                                    d.dtype, h->x, s));
+        for (int l = 0; l < d.NL; l++) {
+            FusedLayer f{};
+            f.wqkv = h->wqkv[l]; f.wo = h->wo[l]; f.w13 = h->w13[l]; f.w2 = h->w2[l];
+            f.nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
+            f.nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
+            f.kc = layer_kc(h, l); f.vc = layer_vc(h, l); f.pg = kv_pages(h); f.S = stream_len(h);
+            f.rope = h->rope;
+            f.pos = ps.pos_rows ? ps.pos_rows : ps.pos_dev;
+            f.x = h->x; f.q = h->q; f.o = h->o; f.g = h->g;
+            f.bar = h->fbar + (int64_t)l * kFusedBarWords;
+            f.bar_reset = h->fbar + (int64_t)((l + 1) % d.NL) * kFusedBarWords;
+            f.err = h->fbar + (int64_t)d.NL * kFusedBarWords;
+            f.D = d.D; f.H = d.H; f.Hkv = d.Hkv; f.F = d.F; f.eps = h->p.norm_eps;
+            TRYC(PC_QKV, launch_decode_layer(f, h->fused_G, s));
+        }
+        TRYC(PC_HEAD, product(h, 0, MAT_HEAD, ps, true));
+        return hipSuccess;
+    }
     const bool fused = fuse_norm(h, M);
+    if (!fused)  // else layer 0's wq|wk|wv product gathers the embedding rows
+        TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, M, ps.T, ps.pos_dev, ps.pos0, ps.pos_rows, ps.rowmap, d.D,
+                                    d.dtype, h->x, s));
     const int lay = act_layout(h, ps);
     for (int l = 0; l < d.NL; l++) {
         const char *nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
@@ -730,6 +769,22 @@ int create_impl(llm_t *h, uint64_t seed)
     rc = build_weights(h, seed);
     if (rc) return rc;
     if (h->bs && (rc = alloc_pool(h))) return rc;
+    if (d.dtype == LLM_F16 && d.NL >= 2) {
+        int dev = 0, cus = 0;
+        HIPC(h, hipGetDevice(&dev));
+        HIPC(h, hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+        // opt-in (LLM_FUSED_LAYER=1): bit-identical, but measured slower than
+        // the separate launches on the 7B one-row step (95 vs 89 us a layer)
+        const char *fl = std::getenv("LLM_FUSED_LAYER");
+        if (cus > 0 && fused_layer_fits(d.D, d.H, d.Hkv, d.F, cus) && fl && fl[0] == '1') {
+            const int64_t bytes = ((int64_t)d.NL * kFusedBarWords + 32) * sizeof(unsigned);
+            HIPM(h, hipMalloc(&p, bytes));
+            h->fbar = (unsigned *)p;
+            HIPC(h, launch_zero_bytes(h->fbar, bytes, h->stream));
+            h->fused_G = cus;
+            h->use_fused = true;
+        }
+    }
     HIPC(h, hipStreamSynchronize(h->stream));
     return LLM_OK;
 }
@@ -739,7 +794,7 @@ void release(llm_t *h)
     if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
     if (h->gexec_rows) (void)hipGraphExecDestroy(h->gexec_rows);
     void *bufs[] = {h->wts, h->emb, h->norm_w, h->kv, h->rope, h->tok, h->logits, h->probs,
-                    h->pos_dev, h->ws, h->btab_d};
+                    h->pos_dev, h->ws, h->btab_d, h->fbar};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (h->btab_stage) (void)hipHostFree(h->btab_stage);
@@ -752,6 +807,20 @@ bool tokens_ok(const int32_t *t, int64_t n, int V)
     for (int64_t i = 0; i < n; i++)
         if (t[i] < 0 || t[i] >= V) return false;
     return true;
+}
+
+// The fused decode layer raises a flag when a grid barrier did not settle
+// (its waits are bounded, so the launch still ended).  Checked by the calls
+// that synchronise.
+int check_fused_flag(llm_t *h)
+{
+    if (!h->fbar || h->dry) return LLM_OK;
+    unsigned flag = 0;
+    HIPC(h, hipMemcpyAsync(&flag, h->fbar + (int64_t)h->d.NL * kFusedBarWords, sizeof(flag), hipMemcpyDeviceToHost,
+                           h->stream));
+    HIPC(h, hipStreamSynchronize(h->stream));
+    if (flag) return fail(h, LLM_EDEVICE, "fused decode layer: a grid barrier did not settle (results invalid)");
+    return LLM_OK;
 }
 
 int after_forward(llm_t *h, hipError_t e)
@@ -914,6 +983,7 @@ int profiled_forward(llm_t *h, int B, int T, int prev_pos, int reps, float *ms_o
         const int *pos = nullptr;
         if (prev_pos >= 0) {
             e = launch_set_int(h->pos_dev, prev_pos, h->stream);
+            h->dev_pos = prev_pos;
             pos = h->pos_dev;
         }
         if (e == hipSuccess) e = forward(h, uniform_pass(B, T, pos), &pf);
@@ -1315,8 +1385,15 @@ int llm_decode(llm_t *h, int32_t prev_pos)
     if ((rc = kv_reserve_uniform(h, h->cur_B, prev_pos, prev_pos + 1, false))) return rc;
     if (!h->dry) {
         if ((rc = kv_upload(h))) return rc;
-        HIPC(h, launch_set_int(h->pos_dev, prev_pos, h->stream));
+        // each step moves the device position on by one, so consecutive
+        // steps need no position write
+        if (h->dev_pos != prev_pos) {
+            h->dev_pos = -1;
+            HIPC(h, launch_set_int(h->pos_dev, prev_pos, h->stream));
+        }
         const int B = h->cur_B;
+        Pass ps = uniform_pass(B, 1, h->pos_dev);
+        ps.advance = true;
         if (h->use_graph) {
             if (!h->gexec || h->graph_B != B) {
                 if (h->gexec) {
@@ -1325,7 +1402,7 @@ int llm_decode(llm_t *h, int32_t prev_pos)
                 }
                 hipGraph_t graph = nullptr;
                 HIPC(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeRelaxed));
-                hipError_t fe = forward(h, uniform_pass(B, 1, h->pos_dev));
+                hipError_t fe = forward(h, ps);
                 hipError_t ce = hipStreamEndCapture(h->stream, &graph);
                 if (fe != hipSuccess) return fail(h, LLM_EDEVICE, std::string("capture: ") + hipGetErrorString(fe));
                 if (ce != hipSuccess) return fail(h, LLM_EDEVICE, std::string("end capture: ") + hipGetErrorString(ce));
@@ -1336,9 +1413,10 @@ int llm_decode(llm_t *h, int32_t prev_pos)
             }
             HIPC(h, hipGraphLaunch(h->gexec, h->stream));
         } else {
-            rc = after_forward(h, forward(h, uniform_pass(B, 1, h->pos_dev)));
+            rc = after_forward(h, forward(h, ps));
             if (rc) return rc;
         }
+        h->dev_pos = prev_pos + 1;
     }
     h->last_pos = prev_pos;
     h->logits_valid = true;
@@ -1494,6 +1572,7 @@ int llm_profile_projections(llm_t *h, int32_t reps, float *us_out)
     hipError_t e = hipEventCreate(&ev[0]);
     if (e == hipSuccess) e = hipEventCreate(&ev[1]);
     if (e == hipSuccess) e = launch_set_int(h->pos_dev, h->last_pos, h->stream);
+    h->dev_pos = h->last_pos;
     // each pass is captured once and replayed, as a decode step is, so the
     // host's launch rate does not pace the short products
     for (int k = 0; k < 6 && e == hipSuccess; k++) {
@@ -1537,7 +1616,7 @@ int llm_get_logits(llm_t *h, float *out)
     HIPC(h, hipMemcpyAsync(out, h->logits, (size_t)h->cur_B * h->d.V * sizeof(float), hipMemcpyDeviceToHost,
                            h->stream));
     HIPC(h, hipStreamSynchronize(h->stream));
-    return LLM_OK;
+    return check_fused_flag(h);
 }
 
 int llm_get_logits_d(llm_t *h, float *out_d)
@@ -1587,7 +1666,7 @@ int llm_sync(llm_t *h)
     int rc = guard(h);
     if (rc) return rc;
     if (!h->dry) HIPC(h, hipStreamSynchronize(h->stream));
-    return LLM_OK;
+    return check_fused_flag(h);
 }
 
 int llm_read_weights(llm_t *h, int32_t tensor_id, int64_t first, int64_t count, void *out)

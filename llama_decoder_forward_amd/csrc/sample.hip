@@ -46,9 +46,22 @@ __global__ void argmax_kernel(const float *logits, int V, int32_t *tok, int64_t 
     const float *row = logits + (int64_t)b * V;
     float best = -INFINITY;
     int bi = 0x7fffffff;
-    for (int i = threadIdx.x; i < V; i += blockDim.x) {
-        float v = row[i];
+    auto consider = [&](float v, int i) {
         if (v > best || (v == best && i < bi)) { best = v; bi = i; }
+    };
+    if ((V & 3) == 0) {
+        // 16-byte loads, several in flight per thread
+        const float4 *r4 = reinterpret_cast<const float4 *>(row);
+#pragma unroll 4
+        for (int i = threadIdx.x; i < (V >> 2); i += blockDim.x) {
+            const float4 v = r4[i];
+            consider(v.x, 4 * i);
+            consider(v.y, 4 * i + 1);
+            consider(v.z, 4 * i + 2);
+            consider(v.w, 4 * i + 3);
+        }
+    } else {
+        for (int i = threadIdx.x; i < V; i += blockDim.x) consider(row[i], i);
     }
     for (int o = 32; o > 0; o >>= 1) {
         float ov = __shfl_xor(best, o);

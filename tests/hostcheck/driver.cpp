@@ -85,6 +85,8 @@ int main()
         uniform_run(h, 3, {40, 30}, 20);
         rows_run(h, {5, 70, 130}, 10);
         uniform_run(h, 2, {1}, 100);
+        uniform_run(h, 1, {10}, 60);  // one row: the fused decode layer
+        rows_run(h, {7}, 20);
         llm_destroy(h);
         h = nullptr;
     }

@@ -35,6 +35,8 @@ hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 hipError_t hipEventDestroy(hipEvent_t e) { free(e); return hipSuccess; }
 hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
 hipError_t hipEventElapsedTime(float *ms, hipEvent_t, hipEvent_t) { *ms = 0.f; return hipSuccess; }
+hipError_t hipGetDevice(int *d) { *d = 0; return hipSuccess; }
+hipError_t hipDeviceGetAttribute(int *v, hipDeviceAttribute_t, int) { *v = 256; return hipSuccess; }
 hipError_t hipMemGetInfo(size_t *fr, size_t *tot) { *tot = (size_t)1 << 36; *fr = *tot / 2; return hipSuccess; }
 hipError_t hipMemcpyAsync(void *dst, const void *src, size_t n, hipMemcpyKind, hipStream_t) { memcpy(dst, src, n); return hipSuccess; }
 hipError_t hipMemcpy2DAsync(void *dst, size_t dp, const void *src, size_t sp, size_t w, size_t hgt, hipMemcpyKind, hipStream_t)
@@ -128,3 +130,16 @@ hipError_t launch_inc_ints(int *d, int n, hipStream_t) { for (int i = 0; i < n; 
 hipError_t launch_set_tokens_rows(int32_t *, int64_t, int, const int *, const int32_t *, const uint8_t *, hipStream_t) { return hipSuccess; }
 hipError_t launch_scatter_tokens(int32_t *, int64_t, int, const int2 *, const int32_t *, hipStream_t) { return hipSuccess; }
 hipError_t launch_set_tokens(int32_t *, int64_t, int, int, const int32_t *, const uint8_t *, hipStream_t) { return hipSuccess; }
+
+bool fused_layer_fits(int, int, int Hkv, int, int G) { return Hkv <= G; }
+hipError_t launch_decode_layer(const FusedLayer &f, int, hipStream_t)
+{
+    g_es = 2;
+    CHECK(f.pos, 4);
+    const int pos = *f.pos;
+    for (int p = 0; p <= pos; p++) check_kv(f.kc, f.vc, f.pg, f.S, f.Hkv, 128, 0, p);
+    CHECK(f.bar, 8 * 32 * 4);
+    CHECK(f.bar_reset, 8 * 32 * 4);
+    CHECK(f.err, 4);
+    return hipSuccess;
+}
