@@ -176,53 +176,73 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
         if (kt + 1 < ntiles) load_tile(kt + 1);
         const int kbase = kt * PF_K;
         if (kbase > p0 + wq0 + 31) continue;  // all keys after this wave's queries
+        // S^T for both query column groups: every K fragment is read from LDS
+        // once and used for both
+        floatx4 sc[2][2][2];  // [c][ks][t]
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                half8 kf[4];
+#pragma unroll
+                for (int s = 0; s < 4; s++) kf[s] = kl[((ks * 2 + t) * 4 + s) * 64 + lane];
+#pragma unroll
+                for (int c = 0; c < 2; c++) {
+                    floatx4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; s++) a = mfma16(kf[s], qb[c][s], a);
+                    sc[c][ks][t] = a;
+                }
+            }
+        // online softmax per column group
+        half8 pb[2][2];
+        float fac[2];
 #pragma unroll
         for (int c = 0; c < 2; c++) {
             const int qi = p0 + wq0 + 16 * c + r;  // this lane's query position
             float p[2][8];
             float mx = kNegBig;
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
+            for (int ks = 0; ks < 2; ks++)
 #pragma unroll
-                for (int t = 0; t < 2; t++) {
-                    floatx4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < 4; s++)
-                        a = mfma16(kl[((ks * 2 + t) * 4 + s) * 64 + lane], qb[c][s], a);
+                for (int t = 0; t < 2; t++)
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
                         const int key = kbase + 32 * ks + 8 * g + 4 * t + i;
-                        float v = key <= qi ? a[i] * scale : -INFINITY;
+                        float v = key <= qi ? sc[c][ks][t][i] * scale : -INFINITY;
                         p[ks][4 * t + i] = v;
                         mx = fmaxf(mx, v);
                     }
-                }
-            }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float mnew = fmaxf(mrun[c], mx);
-            const float fac = expf(mrun[c] - mnew);
+            fac[c] = expf(mrun[c] - mnew);
             float ls = 0.f;
-            half8 pb[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ks++)
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
                     float ev = expf(p[ks][e] - mnew);
                     ls += ev;
-                    pb[ks][e] = (half_t)ev;
+                    pb[c][ks][e] = (half_t)ev;
                 }
             ls += __shfl_xor(ls, 16);
             ls += __shfl_xor(ls, 32);
-            lrun[c] = lrun[c] * fac + ls;
+            lrun[c] = lrun[c] * fac[c] + ls;
             mrun[c] = mnew;
+        }
+        // O^T += V^T P^T for both column groups: every V fragment read once
 #pragma unroll
-            for (int dt = 0; dt < 8; dt++) {
-                floatx4 o = acc[c][dt] * fac;
+        for (int dt = 0; dt < 8; dt++) {
+            floatx4 o0 = acc[0][dt] * fac[0], o1 = acc[1][dt] * fac[1];
 #pragma unroll
-                for (int ks = 0; ks < 2; ks++) o = mfma16(vl[(dt * 2 + ks) * 64 + lane], pb[ks], o);
-                acc[c][dt] = o;
+            for (int ks = 0; ks < 2; ks++) {
+                const half8 vf = vl[(dt * 2 + ks) * 64 + lane];
+                o0 = mfma16(vf, pb[0][ks], o0);
+                o1 = mfma16(vf, pb[1][ks], o1);
             }
+            acc[0][dt] = o0;
+            acc[1][dt] = o1;
         }
     }
 #pragma unroll
