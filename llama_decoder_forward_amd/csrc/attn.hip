@@ -68,15 +68,19 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
 // ---------------------------------------------------------------------------
 constexpr int PF_Q = 128, PF_K = 64;
 
-__global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restrict__ q,
+constexpr int PF_LDS = 2 * 2 * PF_K * 128 * 2;  // two stages of a K and a V tile (bytes)
+
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__restrict__ q,
                                                            const half_t *__restrict__ kc,
                                                            const half_t *__restrict__ vc, int Tu, int p0u,
                                                            int H, int Hkv, int S, KvPages pg, const int *cu,
                                                            half_t *__restrict__ out, int out_lay)
 {
     const int hd = 128;
-    __shared__ half8 kl[PF_K * hd / 8];  // 4 sub-tiles x 4 d-steps x 64 lanes
-    __shared__ half8 vl[PF_K * hd / 8];  // 8 d-tiles x 2 key-steps x 64 lanes
+    extern __shared__ half8 smem[];
+    // per stage: K tile as 4 sub-tiles x 4 d-steps x 64 lanes, V^T tile as 8
+    // d-tiles x 2 key-steps x 64 lanes (operand order)
+    half8 *const klds = smem, *const vlds = smem + 2 * PF_K * hd / 8;
     const int bh = blockIdx.x, b = bh / H, h = bh % H;
     // uniform rows: T = Tu tokens at p0u..; varlen: row b's T tokens are the
     // packed rows cu[b].. at positions 0..
@@ -126,54 +130,63 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const half_t *__restr
     const int qlast = min(q0 + PF_Q, T) - 1;
     const int ntiles = (p0 + qlast) / PF_K + 1;
 
-    half8 rk[4], rv[4];
-    auto load_tile = [&](int kt) {
-        const int base = kt * PF_K;
+    // Stage kt of the tile ring: direct global -> LDS copies, each lane
+    // fetching the 16 bytes that belong at its slot of the operand order.
+    // Wave w copies K blocks 4w..4w+3 (block (ks, t, s): lane rr + 16 gg
+    // holds key 32 ks + 8 (rr / 4) + 4 t + rr % 4, d 32 s + 8 gg .. +7) and V
+    // blocks 4w..4w+3 (block (dt, ks): lane d % 16 + 16 gg holds the keys
+    // 32 ks + 8 gg .. +7 of dimension d = 16 dt + d % 16).  Keys past Lk read
+    // cache entries of the same (row, KV head) that the scores mask out.
+    auto issue_tile = [&](int kt) {
+        const int base = kt * PF_K, buf = kt & 1;
         // base < Lk for every tile walked; the second half only when in range
         const int64_t hb0 = key_base(base);
         const int64_t hb1 = base + 32 < Lk ? key_base(base + 32) : hb0;
+        const int rr = lane & 15, gg = lane >> 4;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const int c = tid + 256 * j;
-            const int key = c >> 4, dch = c & 15;  // K: 64 keys x 16 chunks of 8 d
-            const int64_t kb = key < 32 ? hb0 : hb1;
-            rk[j] = base + key < Lk ? *reinterpret_cast<const half8 *>(kc + kb + (key & 31) * hd + dch * 8) : z;
-            const int d = c >> 3, kch = c & 7;     // V^T: 128 d x 8 chunks of 8 keys
-            const int key0 = base + kch * 8;
-            const half_t *vp = vc + (kch < 4 ? hb0 : hb1) + d * 32 + (kch & 3) * 8;
-            rv[j] = key0 + 8 <= Lk ? *reinterpret_cast<const half8 *>(vp) : z;
-            if (key0 < Lk && key0 + 8 > Lk) {
-                half8 t8;
-                for (int e = 0; e < 8; e++) t8[e] = key0 + e < Lk ? vp[e] : (half_t)0.f;
-                rv[j] = t8;
-            }
+            const int blk = 4 * wave + j;
+            const int ks = blk >> 3, t = (blk >> 2) & 1, s = blk & 3;
+            const int kap = 8 * (rr >> 2) + 4 * t + (rr & 3);
+            lds_copy16(kc + (ks ? hb1 : hb0) + kap * hd + (4 * s + gg) * 8, klds + (buf * 16 + blk) * 64);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int blk = 4 * wave + j;
+            const int dt = blk >> 1, ks = blk & 1;
+            lds_copy16(vc + (ks ? hb1 : hb0) + (16 * dt + rr) * 32 + gg * 8, vlds + (buf * 16 + blk) * 64);
         }
     };
-    auto store_tile = [&]() {
+    // V entries past Lk get probability 0, but 0 times a non-finite stale
+    // value would not vanish: after its copies of the tile holding Lk have
+    // landed, each lane zeroes the keys past Lk in its own V slots
+    auto clear_v_tail = [&](int kt) {
+        const int base = kt * PF_K, buf = kt & 1, gg = lane >> 4;
+        if (base + PF_K <= Lk) return;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const int c = tid + 256 * j;
-            {
-                const int key = c >> 4, dch = c & 15;
-                const int ks = key >> 5, kap = key & 31;
-                const int t = (kap >> 2) & 1, rr = 4 * (kap >> 3) + (kap & 3);
-                const int s = dch >> 2, gg = dch & 3;
-                kl[((ks * 2 + t) * 4 + s) * 64 + rr + 16 * gg] = rk[j];
-            }
-            {
-                const int d = c >> 3, kch = c & 7;
-                const int ks = kch >> 2, gg = kch & 3;
-                vl[((d >> 4) * 2 + ks) * 64 + (d & 15) + 16 * gg] = rv[j];
+            const int blk = 4 * wave + j, ks = blk & 1;
+            const int key0 = base + 32 * ks + 8 * gg;
+            if (key0 + 8 > Lk) {
+                half8 &slot = vlds[(buf * 16 + blk) * 64 + lane];
+                half8 v = slot;
+#pragma unroll
+                for (int e = 0; e < 8; e++) v[e] = key0 + e < Lk ? v[e] : (half_t)0.f;
+                slot = v;
             }
         }
     };
 
-    load_tile(0);
+    issue_tile(0);
     for (int kt = 0; kt < ntiles; kt++) {
-        __syncthreads();  // previous tile's readers are done
-        store_tile();
+        // this wave's copies of stage kt have landed (none of stage kt+1 is
+        // issued yet); the barrier makes every wave's visible and ends the
+        // reads of stage kt-1, whose buffer the next copies reuse
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        clear_v_tail(kt);
         __syncthreads();
-        if (kt + 1 < ntiles) load_tile(kt + 1);
+        if (kt + 1 < ntiles) issue_tile(kt + 1);
+        const half8 *kl = klds + (kt & 1) * 1024, *vl = vlds + (kt & 1) * 1024;
         const int kbase = kt * PF_K;
         if (kbase > p0 + wq0 + 31) continue;  // all keys after this wave's queries
         // S^T for both query column groups: every K fragment is read from LDS
@@ -361,7 +374,7 @@ hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s)
 hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s)
 {
     if (a.out_lay != ACT_ROWS && a.out_lay != ACT_TILED) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.B * a.H, (a.T + PF_Q - 1) / PF_Q), dim3(256), 0,
+    hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.B * a.H, (a.T + PF_Q - 1) / PF_Q), dim3(256), PF_LDS,
                        s, (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache,
                        a.T, a.pos_imm, a.H, a.Hkv, a.Sb, a.pg, a.cu, (half_t *)a.out, a.out_lay);
     return hipGetLastError();

@@ -100,6 +100,18 @@ __device__ __forceinline__ void st_coh_half(half_t *p, half_t v)
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One 16-byte global -> LDS copy per lane (LDS address m0 + 16 * lane).  It
+// is issued from inline assembly: with the compiler's own LDS-DMA builtin in
+// the loop, its wait-count model stops trusting the in-order completion of
+// LDS reads and waits for all of them before the first MFMA of a step.  The
+// kernels track these copies themselves with explicit vmcnt waits; m0 is used by
+// nothing else in the kernel.
+__device__ __forceinline__ void lds_copy16(const void *gsrc, const void *ldst)
+{
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(l) : "memory", "m0");
+}
+
 // Decode activations of 2 < M <= 32 rows, "fragment-major": the B operand of
 // v_mfma_f32_16x16x32_f16 for 16 rows and 32 columns is one contiguous
 // 1 KiB block, so a product's activation load is as coalesced as its weight

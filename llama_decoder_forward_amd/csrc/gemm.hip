@@ -384,17 +384,6 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const half_t *__restrict_
 // (ACT_TILED), so its copies are as contiguous as the weights'; otherwise X
 // is row-major with stride ldx.
 // ---------------------------------------------------------------------------
-// One 16-byte global -> LDS copy per lane (LDS address m0 + 16 * lane).  It
-// is issued from inline assembly: with the compiler's own LDS-DMA builtin in
-// the loop, its wait-count model stops trusting the in-order completion of
-// LDS reads and waits for all of them before the first MFMA of a step.  The
-// kernel tracks these copies itself with explicit vmcnt waits; m0 is used by
-// nothing else in the kernel.
-__device__ __forceinline__ void lds_copy16(const void *gsrc, const void *ldst)
-{
-    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(l) : "memory", "m0");
-}
 
 template <int NS>
 __device__ __forceinline__ void wait_vm_in_flight8(bool keep)
