@@ -356,7 +356,7 @@ hipError_t launch_decode(const AttnArgs &a, hipStream_t s)
     if (pairs >= 512)
         hipLaunchKernelGGL((attn_decode_kernel<2, true, PAGED>), dim3(pairs), dim3(128), 0, s, q, kc, vc, a.H, a.Hkv,
                            a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
-    else if (pairs >= 128)
+    else if (pairs >= 300)  // 320 pairs (13B bs8); 256 (70B bs32) do better with eight
         hipLaunchKernelGGL((attn_decode_kernel<4, false, PAGED>), dim3(pairs), dim3(256), 0, s, q, kc, vc, a.H, a.Hkv,
                            a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
     else

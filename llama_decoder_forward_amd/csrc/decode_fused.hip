@@ -23,7 +23,7 @@
 // current position's K/V, the attention output, x, the SwiGLU output) is
 // written and read with device-coherent accesses, which bypass the XCDs'
 // private L2 caches; the barrier counts arrivals with relaxed device-scope
-// atomics (per-XCD-group counters, then one global count).  Every wait is
+// atomics on eight group counters (work-groups by blockIdx % 8).  Every wait is
 // bounded: after kSpinLimit polls the work-group raises the error flag and
 // every later wait returns, so the launch always ends; the host reports the
 // flag.

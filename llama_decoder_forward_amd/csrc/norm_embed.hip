@@ -57,13 +57,21 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64
     half8 *yr = reinterpret_cast<half8 *>(y + (int64_t)row * D);
     const half8 *wr = reinterpret_cast<const half8 *>(w);
     const int nv = D / 8;
-    half8 v[RMS_VEC];
-    float ss = 0.f;
+    half8 v[RMS_VEC], wv[RMS_VEC];
+    // the weight row is loaded with x, so the two loads share one round trip
 #pragma unroll
     for (int j = 0; j < RMS_VEC; j++) {
         const int i = lane + 64 * j;
         if (i < nv) {
             v[j] = xr[i];
+            wv[j] = wr[i];
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < RMS_VEC; j++) {
+        const int i = lane + 64 * j;
+        if (i < nv) {
 #pragma unroll
             for (int e = 0; e < 8; e++) { float f = (float)v[j][e]; ss += f * f; }
         }
@@ -75,11 +83,11 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64
     for (int j = 0; j < RMS_VEC; j++) {
         const int i = lane + 64 * j;
         if (i < nv) {
-            half8 wv = wr[i], o;
+            half8 o;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
                 half_t n = (half_t)((float)v[j][e] * r);
-                o[e] = (half_t)((float)n * (float)wv[e]);
+                o[e] = (half_t)((float)n * (float)wv[j][e]);
             }
             if (y_lay) *reinterpret_cast<half8 *>(y + act_offset(row, 8 * (int64_t)i, D, D, y_lay)) = o;
             else yr[i] = o;

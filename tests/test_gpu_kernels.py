@@ -226,16 +226,16 @@ def test_attention_decode(B, small, L):
 
 
 @pytest.mark.parametrize("Bn,L,S", [(64, 300, 320), (64, 33, 320), (256, 77, 320), (256, 1, 320),
-                                     (64, 700, 1024), (80, 1000, 1024), (80, 3, 1024)])
+                                     (64, 700, 1024), (160, 1000, 1024), (160, 3, 1024)])
 def test_attention_decode_many_pairs(B, Bn, L, S):
-    """Bn * n_kv_heads (row, KV head) pairs: 128 and 160 pairs take the
-    four-wave work-groups, 512 the two-wave ones with the next step
-    prefetched; caches of 320 and 1024 positions, ragged last steps, long
-    contexts and a single key included."""
+    """Bn * n_kv_heads (row, KV head) pairs: 128 pairs take the eight-wave
+    work-groups, 320 the four-wave ones, 512 the two-wave ones with the next
+    step prefetched; caches of 320 and 1024 positions, ragged last steps,
+    long contexts and a single key included."""
     kw = small_f16(max_batch_size=Bn, max_seq_len=S)
     h = B.llm_create(B.make_params(**kw), 78)
     H, Hkv, d = kw["n_heads"], kw["n_kv_heads"], 128
-    assert Bn * Hkv in (128, 160, 512)
+    assert Bn * Hkv in (128, 320, 512)
     rng = np.random.default_rng(15 + L)
     K = randn_f16(rng, (Bn, L, Hkv, d))
     V = randn_f16(rng, (Bn, L, Hkv, d))

@@ -141,11 +141,12 @@ def test_paged_equals_static(B, case):
                 assert np.abs(got[b] - ref).max() <= 1e-3
 
 
-@pytest.mark.parametrize("Bn,L,bs", [(16, 300, 32), (64, 300, 64), (256, 77, 32), (256, 1, 32),
+@pytest.mark.parametrize("Bn,L,bs", [(16, 300, 32), (64, 300, 64), (160, 200, 32), (256, 77, 32), (256, 1, 32),
                                      (64, 33, 128)])
 def test_paged_attention_decode_kernel(B, Bn, L, bs):
-    """32, 128 and 512 (row, KV head) pairs: the eight-, four- and two-wave
-    decode work-groups read scrambled tables; equal to the static cache."""
+    """32 and 128, 320, and 512 (row, KV head) pairs: the eight-, four- and
+    two-wave decode work-groups read scrambled tables; equal to the static
+    cache."""
     kw = small_kw(max_batch_size=Bn, max_seq_len=320)
     H, Hkv, d = kw["n_heads"], kw["n_kv_heads"], 128
     rng = np.random.default_rng(70 + L)
