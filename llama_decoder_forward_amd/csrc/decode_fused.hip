@@ -34,8 +34,8 @@ namespace {
 
 constexpr int FNW = 8;         // waves per work-group
 constexpr int FNT = FNW * 64;  // threads per work-group
-constexpr int FU = 8;          // 1 KiB weight tiles per wave per round
-static_assert(FU == 8, "wait_vm counts rounds of eight loads");
+constexpr int FU = 4;          // 1 KiB weight tiles per wave per round (as the one-row products)
+static_assert(FU == 4, "wait_vm counts rounds of four loads");
 constexpr int FROUND = FNW * FU;  // 32-wide K tiles per round of a 16-row block
 constexpr unsigned kSpinLimit = 1u << 22;
 
@@ -83,15 +83,16 @@ __device__ void grid_sync(unsigned *bar, unsigned *err, unsigned k)
 // with pending = the number of those loads, completes the stores only.
 __device__ __forceinline__ void wait_vm(int pending)
 {
-    if (pending >= 2 * FU) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (pending >= FU) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if (pending >= 2 * FU) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (pending >= FU) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // The work-group's share of one product: row blocks t = wg, wg + G, ... of a
 // tiled matrix of NT blocks and KT 32-wide K tiles, against the staged
 // activation row xs.  Work item j is round j % NR of the work-group's block
-// j / NR; wave w's tiles in round r are K tiles r*FROUND + w*FU + u.
+// j / NR; wave w's tiles in round r are K tiles r*FROUND + w*FU + u.  The
+// weight stream is read with non-temporal loads.
 struct Product {
     const half8 *W;
     int KT, NT, NR, n;  // K tiles, row blocks, rounds per block, this work-group's items
@@ -110,10 +111,10 @@ struct Product {
         const half8 *src = W + (int64_t)t * KT * 64 + lane;
         if (base + FU <= KT) {  // a full round: no per-tile checks
 #pragma unroll
-            for (int u = 0; u < FU; u++) buf[u] = src[(int64_t)(base + u) * 64];
+            for (int u = 0; u < FU; u++) buf[u] = __builtin_nontemporal_load(src + (int64_t)(base + u) * 64);
         } else {  // the ragged last round: tiles past KT re-read the last one (zeroed when used)
 #pragma unroll
-            for (int u = 0; u < FU; u++) buf[u] = src[(int64_t)min(base + u, KT - 1) * 64];
+            for (int u = 0; u < FU; u++) buf[u] = __builtin_nontemporal_load(src + (int64_t)min(base + u, KT - 1) * 64);
         }
     }
 };

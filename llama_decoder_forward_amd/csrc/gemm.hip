@@ -132,7 +132,15 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
 // ---------------------------------------------------------------------------
 constexpr int STAGE_MAX_BYTES = 48 * 1024;
 
-template <int NW, int U, int TPB, bool TWO, bool STAGE, bool NORM, bool XT = false>
+// NT: the weight stream is read with non-temporal loads
+template <bool NT>
+__device__ __forceinline__ half8 ldw1(const half8 *p)
+{
+    if (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+
+template <int NW, int U, int TPB, bool TWO, bool STAGE, bool NORM, bool XT = false, bool PF = false, bool NT = false>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__restrict__ W,
                                                               const half_t *__restrict__ X,
                                                               int64_t ldx, int M, int N, int K,
@@ -156,7 +164,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
 #pragma unroll
     for (int t = 0; t < TPB; t++)
 #pragma unroll
-        for (int u = 0; u < U; u++) w[t][u] = (base + u < KT) ? Wt[((int64_t)t * KT + base + u) * 64] : z;
+        for (int u = 0; u < U; u++)
+            w[t][u] = PF ? ldw1<NT>(Wt + ((int64_t)t * KT + min(base + u, KT - 1)) * 64)
+                         : (base + u < KT) ? ldw1<NT>(Wt + ((int64_t)t * KT + base + u) * 64) : z;
 
     if (STAGE) {
         for (int m = 0; m < M; m++) {
@@ -218,7 +228,69 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
 #pragma unroll
         for (int c = 0; c < (TWO ? 2 : 1); c++) acc[t][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    for (; base < KT; base += NW * U) {
+    if (PF) {
+        // Two weight rounds in flight per wave: each round issues its
+        // activation loads, then the next round's weight tiles, then waits
+        // only for its own operands (loads retire in issue order).  The
+        // rounds of a wave are counted up front and the last one, which
+        // prefetches nothing, is peeled, so the loop body has no branch and
+        // the compiler's wait counts stay exact.
+        constexpr int STEP = NW * U;
+        const int nr = base < KT ? (KT - base + STEP - 1) / STEP : 0;
+        half8 w2[TPB][U];
+        auto ldw = [&](half8 (&d)[TPB][U], int b) {
+#pragma unroll
+            for (int t = 0; t < TPB; t++)
+#pragma unroll
+                for (int u = 0; u < U; u++) d[t][u] = ldw1<NT>(Wt + ((int64_t)t * KT + min(b + u, KT - 1)) * 64);
+        };
+        auto round = [&](half8 (&wc)[TPB][U], half8 (&wn)[TPB][U], int b, bool pre) {
+            half8 b0[U], b1[TWO ? U : 1];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int kt = min(b + u, KT - 1);
+                if (STAGE) b0[u] = xl[kt * 4];
+                else if (XT) b0[u] = xt[(int64_t)kt * MH * 64];
+                else b0[u] = *reinterpret_cast<const half8 *>(x0 + kt * 32);
+                if (TWO) {
+                    if (XT) b1[TWO ? u : 0] = xt[((int64_t)kt * MH + 1) * 64];
+                    else b1[TWO ? u : 0] = *reinterpret_cast<const half8 *>(x1 + kt * 32);
+                }
+            }
+            if (pre) ldw(wn, b + STEP);
+            // keep the scheduler from sinking the prefetch below the MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                // past the end of K (last round) both operands are zero, as
+                // are the rows past M
+                const bool in = b + u < KT;
+                const half8 a0 = (in && h0) ? b0[u] : z;
+                const half8 a1 = (TWO && in && h1) ? b1[TWO ? u : 0] : z;
+#pragma unroll
+                for (int t = 0; t < TPB; t++) {
+                    const half8 wv = in ? wc[t][u] : z;
+                    acc[t][0] = mfma16(wv, a0, acc[t][0]);
+                    if (TWO) acc[t][TWO ? 1 : 0] = mfma16(wv, a1, acc[t][TWO ? 1 : 0]);
+                }
+            }
+        };
+        int i = 0;
+        for (; i + 2 < nr; i += 2) {
+            round(w, w2, base, true);
+            base += STEP;
+            round(w2, w, base, true);
+            base += STEP;
+        }
+        if (nr - i == 2) {
+            round(w, w2, base, true);
+            base += STEP;
+            round(w2, w, base, false);
+        } else if (nr - i == 1) {
+            round(w, w2, base, false);
+        }
+    }
+    for (; !PF && base < KT; base += NW * U) {
         half8 b0[U], b1[TWO ? U : 1];
 #pragma unroll
         for (int u = 0; u < U; u++) {
@@ -247,7 +319,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
 #pragma unroll
             for (int t = 0; t < TPB; t++)
 #pragma unroll
-                for (int u = 0; u < U; u++) w[t][u] = (nb + u < KT) ? Wt[((int64_t)t * KT + nb + u) * 64] : z;
+                for (int u = 0; u < U; u++) w[t][u] = (nb + u < KT) ? ldw1<NT>(Wt + ((int64_t)t * KT + nb + u) * 64) : z;
         }
     }
 #pragma unroll
@@ -606,36 +678,54 @@ __global__ void linear_f32_kernel(const float *W, const float *X, int64_t ldx, i
 
 bool skinny_can_normalise(int M, int K) { return M <= 2 && (int64_t)M * K * 2 <= STAGE_MAX_BYTES; }
 
+// One skinny launch: N/16/TPB work-groups of eight waves; the weight stream is
+// read non-temporally (measured on every decode shape: 5-17% faster than
+// cached loads, with the same HBM bytes).
+template <int U, int TPB, bool TWO, bool STAGE, bool NORM, bool XT, bool PF>
+static void skinny(const GemmArgs &a, const half_t *W, const half_t *X, int64_t ldx, size_t lds, hipStream_t s)
+{
+    hipLaunchKernelGGL((gemm_skinny_kernel<8, U, TPB, TWO, STAGE, NORM, XT, PF, true>), dim3(a.N / 16 / TPB), dim3(512),
+                       lds, s, W, X, ldx, a.M, a.N, a.K, a.ep, (const half_t *)a.norm_w, a.eps, a.gather_tok,
+                       a.gather_ld, (half_t *)a.gather_out);
+}
+
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
 {
     if (a.M <= 0) return hipSuccess;
     const half_t *W = (const half_t *)a.W, *X = (const half_t *)a.X, *nw = (const half_t *)a.norm_w;
     if (nw && !skinny_can_normalise(a.M, a.K)) return hipErrorInvalidValue;
     if (a.gather_tok && (!nw || a.x_lay != ACT_ROWS)) return hipErrorInvalidValue;  // the staged, normalising form only
-    const dim3 blk(512);
-    if (a.x_lay == 1 || a.x_lay == 2) {
-        // fragment-major activations of a decode step, 2 < M <= 32
-        if (nw || a.M > 16 * a.x_lay || a.x_lay > 2) return hipErrorInvalidValue;
-        const int tiles = a.N / 16;
-        if (a.x_lay == 1 && tiles < 1024 && tiles % 2 == 0)
-            // up to 16 rows, fewer than 1024 row blocks: two per work-group
-            // (measured on the 13B shapes: wo and w2 12% faster than one)
-            hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 2, false, false, false, true>), dim3(tiles / 2), blk, 0, s,
-                               W, X, 0, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
-        else if (a.x_lay == 1)
-            hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, false, false, true>), dim3(tiles), blk, 0, s, W,
-                               X, 0, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
-        else if (tiles >= 640 && tiles < 1024 && tiles % 4 == 0)
-            // tall products: four row blocks per work-group share each activation fragment
-            hipLaunchKernelGGL((gemm_skinny_kernel<8, 2, 4, true, false, false, true>), dim3(tiles / 4), blk, 0, s,
-                               W, X, 0, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
-        else if (tiles >= 320 && tiles % 2 == 0)
-            hipLaunchKernelGGL((gemm_skinny_kernel<8, 4, 2, true, false, false, true>), dim3(tiles / 2), blk, 0, s,
-                               W, X, 0, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
+    const int tiles = a.N / 16;
+    // Work-group shapes below were chosen per product from cold-weight graph
+    // replays of every decode shape (one row: 7B; 8 rows: 13B; 32 rows: 7B and
+    // 70B).  PF (two weight rounds in flight per wave) pays where there are
+    // few work-groups.
+    if (a.x_lay == 1) {
+        // fragment-major activations, 3..16 rows
+        if (nw || a.M > 16) return hipErrorInvalidValue;
+        if (tiles < 1024 && tiles % 2 == 0)
+            skinny<8, 2, false, false, false, true, false>(a, W, X, 0, 0, s);
+        else if (tiles % 4 == 0)
+            skinny<2, 4, false, false, false, true, false>(a, W, X, 0, 0, s);
         else
-            // few row blocks: one per work-group keeps every CU streaming
-            hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, true, false, false, true>), dim3(tiles), blk, 0, s, W,
-                               X, 0, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
+            skinny<8, 1, false, false, false, true, false>(a, W, X, 0, 0, s);
+        return hipGetLastError();
+    }
+    if (a.x_lay == 2) {
+        // fragment-major activations, 17..32 rows (two 16-row halves)
+        if (nw || a.M > 32) return hipErrorInvalidValue;
+        if (tiles <= 256)
+            skinny<8, 1, true, false, false, true, true>(a, W, X, 0, 0, s);
+        else if (tiles <= 512 && tiles % 2 == 0)
+            skinny<4, 2, true, false, false, true, true>(a, W, X, 0, 0, s);
+        else if (tiles < 1024 && tiles % 4 == 0)
+            skinny<2, 4, true, false, false, true, true>(a, W, X, 0, 0, s);
+        else if (tiles < 1536 && tiles % 2 == 0)
+            skinny<2, 2, true, false, false, true, false>(a, W, X, 0, 0, s);
+        else if (tiles % 4 == 0)
+            skinny<2, 4, true, false, false, true, false>(a, W, X, 0, 0, s);
+        else
+            skinny<8, 1, true, false, false, true, false>(a, W, X, 0, 0, s);
         return hipGetLastError();
     }
     if (a.x_lay == ACT_TILED) {
@@ -644,24 +734,28 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
     }
     if (a.x_lay != ACT_ROWS) return hipErrorInvalidValue;
     if (a.M <= 2 && (int64_t)a.M * a.K * 2 <= STAGE_MAX_BYTES) {
+        // one or two rows, staged (and normalised) in LDS
         const size_t lds = (size_t)a.M * a.K * 2;
-        if (nw)
-            hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, true, true>), dim3(a.N / 16), blk, lds, s, W, X,
-                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
-        else
-            hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, true, false>), dim3(a.N / 16), blk, lds, s, W,
-                               X, a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
+        // four tiles per wave and round for every product, so that the sum
+        // order is the one of the one-launch decode layer
+        const bool pair = tiles >= 512 && tiles % 2 == 0, pf = tiles < 1024;
+        if (nw) {
+            if (pair && pf) skinny<4, 2, false, true, true, false, true>(a, W, X, a.ldx, lds, s);
+            else if (pair) skinny<4, 2, false, true, true, false, false>(a, W, X, a.ldx, lds, s);
+            else skinny<4, 1, false, true, true, false, true>(a, W, X, a.ldx, lds, s);
+        } else {
+            if (pair && pf) skinny<4, 2, false, true, false, false, true>(a, W, X, a.ldx, lds, s);
+            else if (pair) skinny<4, 2, false, true, false, false, false>(a, W, X, a.ldx, lds, s);
+            else skinny<4, 1, false, true, false, false, true>(a, W, X, a.ldx, lds, s);
+        }
     } else if (a.M <= 16) {
-        hipLaunchKernelGGL((gemm_skinny_kernel<8, 8, 1, false, false, false>), dim3(a.N / 16), blk, 0, s, W, X,
-                           a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
+        skinny<8, 1, false, false, false, false, false>(a, W, X, a.ldx, 0, s);
     } else if (a.M <= 32) {
         // two row blocks per work-group reuse each activation fragment twice
-        if ((a.N / 16) % 2 == 0)
-            hipLaunchKernelGGL((gemm_skinny_kernel<8, 4, 2, true, false, false>), dim3(a.N / 32), blk, 0, s, W, X,
-                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
+        if (tiles % 2 == 0)
+            skinny<4, 2, true, false, false, false, false>(a, W, X, a.ldx, 0, s);
         else
-            hipLaunchKernelGGL((gemm_skinny_kernel<8, 4, 1, true, false, false>), dim3(a.N / 16), blk, 0, s, W, X,
-                               a.ldx, a.M, a.N, a.K, a.ep, nw, a.eps, a.gather_tok, a.gather_ld, (half_t *)a.gather_out);
+            skinny<4, 1, true, false, false, false, false>(a, W, X, a.ldx, 0, s);
     } else if (a.M < 1024) {
         int NB = (a.N + BIG_BN - 1) / BIG_BN, MB = (a.M + BIG_BM - 1) / BIG_BM;
         hipLaunchKernelGGL(gemm_big_kernel, dim3(NB * MB), dim3(256), 0, s, W, X, a.ldx, a.M, a.N, a.K, a.ep);
