@@ -17,7 +17,7 @@
 // held in lanes and read with readlane.  COH: q and the step holding the
 // current position are read with device-coherent loads and the output is
 // stored device-coherently (data written and read inside one kernel by work
-// groups on different XCDs).
+// groups on different XCDs).  NT: K and V are read non-temporally.
 #pragma once
 #include "common.h"
 
@@ -31,9 +31,17 @@ __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c)
 // Key (0..31 within a step) held in row r of sub-tile t.
 __device__ __forceinline__ int perm_key(int t, int r) { return 8 * (r >> 2) + 4 * t + (r & 3); }
 
+// NT: K and V are read with non-temporal loads
+template <bool NT>
+__device__ __forceinline__ half8 ld_kv(const half_t *p)
+{
+    if (NT) return __builtin_nontemporal_load(reinterpret_cast<const half8 *>(p));
+    return *reinterpret_cast<const half8 *>(p);
+}
+
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp(m_old - m_new) is never NaN
 
-template <int NW, bool PF, bool PAGED, bool COH>
+template <int NW, bool PF, bool PAGED, bool COH, bool NT = false>
 __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, const half_t *__restrict__ kc,
                                                const half_t *__restrict__ vc, int H, int Hkv, int S, const KvPages &pg,
                                                int b, int kvh, int L, half_t *__restrict__ out, int out_lay,
@@ -99,7 +107,7 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
             const half_t *krow = kc + base + (ok ? kp : 0) * hd + 8 * g;
 #pragma unroll
             for (int s = 0; s < 4; s++)
-                kf[t][s] = ok ? (coh ? ld_coh_half8(krow + 32 * s) : *reinterpret_cast<const half8 *>(krow + 32 * s)) : z;
+                kf[t][s] = ok ? (coh ? ld_coh_half8(krow + 32 * s) : ld_kv<NT>(krow + 32 * s)) : z;
         }
         const int kk = k0 + 8 * g;
         const bool vok = kk + 8 <= L;
@@ -112,7 +120,7 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
 #pragma unroll
                 for (int e = 0; e < 8; e++) vf[dt][e] = (kk + e < L) ? v[e] : (half_t)0.f;
             } else if (vok) {
-                vf[dt] = *reinterpret_cast<const half8 *>(vrow);
+                vf[dt] = ld_kv<NT>(vrow);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; e++) vf[dt][e] = (kk + e < L) ? vrow[e] : (half_t)0.f;

@@ -95,6 +95,63 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64
     }
 }
 
+// The same RMSNorm for the few rows of a decode step: one row per work-group
+// of eight waves, so the row's loads are spread over eight times as many
+// CUs.  Thread t sums the squares of its elements 8t.., 8(t + 512).., ...,
+// each wave adds by butterflies and the waves' sums are added in wave order:
+// the order of the normalisation staged inside the one- and two-row
+// products, so a row normalises to the same bits on either path.
+__global__ __launch_bounds__(512) void rmsnorm_row_kernel(const half_t *x, int64_t ldx, const half_t *w, int D,
+                                                          float eps, half_t *y, int y_lay)
+{
+#pragma clang fp contract(off)
+    __shared__ float pss[8];
+    const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const half8 *xr = reinterpret_cast<const half8 *>(x + (int64_t)row * ldx);
+    const half8 *wr = reinterpret_cast<const half8 *>(w);
+    const int nv = D / 8;
+    constexpr int R = RMS_VEC / 8;  // D up to 8192
+    half8 v[R], wv[R];
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        const int i = tid + 512 * j;
+        if (i < nv) {
+            v[j] = xr[i];
+            wv[j] = wr[i];
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        if (tid + 512 * j < nv) {
+#pragma unroll
+            for (int e = 0; e < 8; e++) { float f = (float)v[j][e]; ss += f * f; }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if (lane == 0) pss[wave] = ss;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 8; ww++) t += pss[ww];
+    const float r = __frcp_rn(__fsqrt_rn(t / (float)D + eps));
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+        const int i = tid + 512 * j;
+        if (i < nv) {
+            half8 o;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                half_t n = (half_t)((float)v[j][e] * r);
+                o[e] = (half_t)((float)n * (float)wv[j][e]);
+            }
+            if (y_lay) *reinterpret_cast<half8 *>(y + act_offset(row, 8 * (int64_t)i, D, D, y_lay)) = o;
+            else reinterpret_cast<half8 *>(y + (int64_t)row * D)[i] = o;
+        }
+    }
+}
+
 __global__ void rmsnorm_f32_kernel(const float *x, int64_t ldx, const float *w, int D, float eps,
                                    float *y)
 {
@@ -135,7 +192,10 @@ hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int 
     if (M <= 0) return hipSuccess;
     if (y_lay && (dtype != 1 || D % 32)) return hipErrorInvalidValue;
     if ((y_lay == 1 || y_lay == 2) && M > 16 * y_lay) return hipErrorInvalidValue;
-    if (dtype == 1)
+    if (dtype == 1 && M <= 64)
+        hipLaunchKernelGGL(rmsnorm_row_kernel, dim3(M), dim3(512), 0, s, (const half_t *)x, ldx, (const half_t *)w, D,
+                           eps, (half_t *)y, y_lay);
+    else if (dtype == 1)
         hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((M + 3) / 4), dim3(256), 0, s, (const half_t *)x, ldx,
                            (const half_t *)w, M, D, eps, (half_t *)y, y_lay);
     else

@@ -229,7 +229,7 @@ def test_attention_decode(B, small, L):
                                      (64, 700, 1024), (160, 1000, 1024), (160, 3, 1024)])
 def test_attention_decode_many_pairs(B, Bn, L, S):
     """Bn * n_kv_heads (row, KV head) pairs: 128 pairs take the eight-wave
-    work-groups, 320 the four-wave ones, 512 the two-wave ones with the next
+    work-groups with non-temporal K/V loads, 320 the four-wave ones, 512 the two-wave ones with the next
     step prefetched; caches of 320 and 1024 positions, ragged last steps,
     long contexts and a single key included."""
     kw = small_f16(max_batch_size=Bn, max_seq_len=S)
