@@ -573,8 +573,8 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(const half_t *__re
 // each wave loads its four X fragments of a k-tile straight from global
 // memory into registers, two k-tiles ahead, and only W goes through the LDS
 // ring (NSW stages of 16 KiB).  A third fewer LDS reads and half the LDS
-// copies; measured 3-9% faster than the form above on the 7B..70B prefill
-// shapes except the 70B w1|w3 (equal), with the same sums.  Every wave
+// copies; measured 1.5-3.5% faster than the form above on the 7B..70B
+// prefill shapes (interleaved runs, medians), with the same sums.  Every wave
 // issues, per k-tile, its two W copies and then its four X loads, all
 // unconditionally (indexes past the end are clamped and the results never
 // used), so a single counter wait covers both: after X(kt) the wave has
@@ -635,11 +635,16 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t 
         issue_x(p, xb[p]);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the epilogue's scalar argument loads
+    // KT % PD == 0 (checked by the launcher): no guard inside the unrolled
+    // body, so every path into the loop head has issued the X loads in the
+    // same order and the compiler's own waits for them stay tight (a guard
+    // made it assume the worst order and wait for every load, the W copies
+    // it does not see included, once per PD k-tiles)
     for (int kt0 = 0; kt0 < KT; kt0 += PD) {
 #pragma unroll
         for (int p = 0; p < PD; p++) {
             const int kt = kt0 + p;
-            if (kt < KT) {
+            {
                 // X(kt) and, issued before it, W stage kt are in; the barrier
                 // makes every wave's W copies visible and tells this wave that
                 // all have finished reading buffer (kt - 1) % NSW
@@ -711,7 +716,11 @@ hipError_t launch_tile256_xreg(const GemmArgs &a, hipStream_t s)
 template <bool XT>
 hipError_t launch_tile256(const GemmArgs &a, hipStream_t s)
 {
-    if constexpr (XT) return launch_tile256_xreg<5>(a, s);
+    if constexpr (XT) {
+        // fp16 models have dim and ffn width multiples of 64: K/32 is even
+        if ((a.K >> 5) % 2) return hipErrorInvalidValue;
+        return launch_tile256_xreg<5>(a, s);
+    }
     // the eight-wave form with a five-stage ring (measured 4-16% faster than
     // four waves and four stages on the 7B..70B prefill shapes, same sums)
     constexpr int NS = 5;
