@@ -97,7 +97,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__re
     const int r = lane & 15, g = lane >> 4;
     const int q0 = blockIdx.y * PF_Q;
     const int wq0 = q0 + 32 * wave;  // this wave's first query
-    const float scale = 1.0f / sqrtf((float)hd);
+    // scores are kept in log2 units (scaled by log2(e) / sqrt(d)), so each
+    // softmax term is one native exp2: exp(s / sqrt(d) - m) = 2^(s log2(e) /
+    // sqrt(d) - m log2(e))
+    const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
     const half8 z = {};
 
     half8 qb[2][4];
@@ -207,7 +210,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__re
                     sc[c][ks][t] = a;
                 }
             }
-        // online softmax per column group
+        // online softmax per column group; tiles wholly before this wave's
+        // first query need no causal mask (a uniform test)
+        const bool unmasked = kbase + PF_K - 1 <= p0 + wq0;
         half8 pb[2][2];
         float fac[2];
 #pragma unroll
@@ -222,20 +227,21 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__re
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
                         const int key = kbase + 32 * ks + 8 * g + 4 * t + i;
-                        float v = key <= qi ? sc[c][ks][t][i] * scale : -INFINITY;
+                        float v = sc[c][ks][t][i] * sl2;
+                        if (!unmasked) v = key <= qi ? v : -INFINITY;
                         p[ks][4 * t + i] = v;
                         mx = fmaxf(mx, v);
                     }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float mnew = fmaxf(mrun[c], mx);
-            fac[c] = expf(mrun[c] - mnew);
+            fac[c] = __builtin_amdgcn_exp2f(mrun[c] - mnew);
             float ls = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 2; ks++)
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
-                    float ev = expf(p[ks][e] - mnew);
+                    float ev = __builtin_amdgcn_exp2f(p[ks][e] - mnew);
                     ls += ev;
                     pb[c][ks][e] = (half_t)ev;
                 }

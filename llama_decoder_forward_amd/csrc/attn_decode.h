@@ -55,7 +55,9 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
     const int r = lane & 15, g = lane >> 4;
     const bool qv = r < n_rep;
     const int h = kvh * n_rep + r;
-    const float scale = 1.0f / sqrtf((float)hd);
+    // scores in log2 units (scaled by log2(e) / sqrt(d)): each softmax term
+    // is one native exp2, as in the prefill kernel
+    const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
     const int nsteps = (L + 31) / 32;
     const half8 z = {};
 
@@ -144,19 +146,19 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int key = k0 + 8 * g + 4 * t + i;
-                float v = key < L ? sc[t][i] * scale : -INFINITY;
+                float v = key < L ? sc[t][i] * sl2 : -INFINITY;
                 p[4 * t + i] = v;
                 mx = fmaxf(mx, v);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mnew = fmaxf(mrun, mx);
-        const float fac = expf(mrun - mnew);
+        const float fac = __builtin_amdgcn_exp2f(mrun - mnew);
         float ls = 0.f;
         half8 pb;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            float ev = expf(p[e] - mnew);
+            float ev = __builtin_amdgcn_exp2f(p[e] - mnew);
             ls += ev;
             pb[e] = (half_t)ev;
         }
@@ -204,7 +206,7 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
         if (wave < half) {
             const float mo = sm[wave][r], lo = sl[wave][r];
             const float M = fmaxf(mrun, mo);
-            const float fa = expf(mrun - M), fb = expf(mo - M);
+            const float fa = __builtin_amdgcn_exp2f(mrun - M), fb = __builtin_amdgcn_exp2f(mo - M);
 #pragma unroll
             for (int dt = 0; dt < 8; dt++) acc[dt] = acc[dt] * fa + so[wave][dt][lane] * fb;
             lrun = lrun * fa + lo * fb;
