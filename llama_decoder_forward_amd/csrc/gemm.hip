@@ -878,7 +878,7 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
         if (tiles <= 256)
             skinny<8, 1, true, false, false, true, true>(a, W, X, 0, 0, s);
         else if (tiles <= 512 && tiles % 2 == 0)
-            skinny<4, 2, true, false, false, true, true>(a, W, X, 0, 0, s);
+            skinny<2, 2, true, false, false, true, true>(a, W, X, 0, 0, s);
         else if (tiles < 1024 && tiles % 4 == 0)
             skinny<2, 4, true, false, false, true, true>(a, W, X, 0, 0, s);
         else if (tiles < 1536 && tiles % 2 == 0)
