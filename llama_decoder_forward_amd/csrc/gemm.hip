@@ -128,7 +128,10 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
 // they are RMS-normalised there (walkthrough section 3.2: r = 1/sqrt(mean
 // x^2 + eps), round(round(x r) w)), so the normalisation costs no launch.
 // Without STAGE, activation fragments are loaded from global memory (cache)
-// once per round and reused for the TPB row blocks.
+// once per round and reused for the TPB row blocks.  XT: the activations are
+// fragment-major (one 1 KiB block per k-tile and 16-row half).  PF: two
+// weight rounds in flight per wave (below).  NT: non-temporal weight loads
+// (each weight byte is read once per step).  None of these changes the sums.
 // ---------------------------------------------------------------------------
 constexpr int STAGE_MAX_BYTES = 48 * 1024;
 
