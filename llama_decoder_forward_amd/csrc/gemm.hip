@@ -584,16 +584,18 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(const half_t *__re
 // used), so a single counter wait covers both: after X(kt) the wave has
 // issued exactly the (W, X) groups of PD-1 later k-tiles.
 // ---------------------------------------------------------------------------
-template <int KIND, int NSW, int PD>
+template <int KIND, int NSW, int PD, int TOK = 256>
 __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t *__restrict__ W, const half_t *X,
-                                                                      int M, int N, int K, Epilogue ep)
+                                                                      int M, int N, int K, int n_base, Epilogue ep)
 {
     static_assert(PD == 2 && NSW == 5, "the counter waits below are for this ring and two k-tiles of X in flight");
+    static_assert(TOK == 256 || TOK == 128, "token tiles of 256 or 128");
+    constexpr int XF = TOK / 64;  // X fragments per wave and k-tile
     extern __shared__ half8 lds[];
     half8 *lw = lds;  // [NSW][16 tiles][64 lanes]
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wn = wave >> 2, wm = wave & 3;
-    const int NB = (N + 255) / 256, MB = (M + 255) / 256;
+    const int NB = (N + 255) / 256, MB = (M + TOK - 1) / TOK;
     const int total = NB * MB;
     int pid = blockIdx.x;
     {  // XCD-aware remap, then groups of 4 token blocks per W block column
@@ -608,27 +610,27 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t 
 
     const int KT = K >> 5, NT = N >> 4, MT = (M + 15) >> 4;
     const half8 *Wv = reinterpret_cast<const half8 *>(W), *Xv = reinterpret_cast<const half8 *>(X);
-    const half8 *wsrc[2], *xsrc[4];
+    const half8 *wsrc[2], *xsrc[XF];
 #pragma unroll
     for (int q = 0; q < 2; q++) wsrc[q] = Wv + (int64_t)min(nb * 16 + wave * 2 + q, NT - 1) * KT * 64 + lane;
 #pragma unroll
-    for (int j = 0; j < 4; j++) xsrc[j] = Xv + (int64_t)min(mb * 16 + wm * 4 + j, MT - 1) * KT * 64 + lane;
+    for (int j = 0; j < XF; j++) xsrc[j] = Xv + (int64_t)min(mb * (TOK / 16) + wm * XF + j, MT - 1) * KT * 64 + lane;
     auto issue_w = [&](int st) {  // stage st into buffer st % NSW; past the end: never read
         const int buf = st % NSW, k = min(st, KT - 1);
 #pragma unroll
         for (int q = 0; q < 2; q++) lds_copy16(wsrc[q] + (int64_t)k * 64, lw + buf * 1024 + (wave * 2 + q) * 64);
     };
-    half8 xb[PD][4];
-    auto issue_x = [&](int kt, half8 (&d)[4]) {
+    half8 xb[PD][XF];
+    auto issue_x = [&](int kt, half8 (&d)[XF]) {
         const int k = min(kt, KT - 1);
 #pragma unroll
-        for (int j = 0; j < 4; j++) d[j] = xsrc[j][(int64_t)k * 64];
+        for (int j = 0; j < XF; j++) d[j] = xsrc[j][(int64_t)k * 64];
     };
-    floatx4 acc[8][4];
+    floatx4 acc[8][XF];
 #pragma unroll
     for (int i = 0; i < 8; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < XF; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // W stages 0..NSW-2-PD alone, then PD (W, X) groups as the loop issues them
     for (int st = 0; st <= NSW - 2 - PD; st++) issue_w(st);
@@ -641,10 +643,11 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t 
     // The A fragments of k-tile kt+1 are read from LDS while k-tile kt
     // multiplies (two register sets, alternating with the unrolled body).
     // Stage 0 first: after its copies this wave has issued W(1), W(2), X(0),
-    // W(3), X(1), i.e. 14 operations.  (X is not declared __restrict__: with
+    // W(3), X(1), i.e. 6 + 2 XF operations.  (X is not declared __restrict__: with
     // it, the compiler treated the X loads as invariant and moved them past
     // these counter waits, which then no longer counted what they assume.)
-    asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    if (XF == 4) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     half8 ab[PD][8];
 #pragma unroll
@@ -659,11 +662,13 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t 
         for (int p = 0; p < PD; p++) {
             const int kt = kt0 + p;
             {
-                // X(kt) and, issued before it, W stages up to kt+1 are in; the
-                // barrier makes every wave's W copies visible and tells this
-                // wave that all have finished reading buffer (kt - 1) % NSW
-                // (its fragments were read, and waited for, one k-tile ago)
-                asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+                // X(kt) and, issued before it, W stages up to kt+1 are in (the
+                // one later k-tile's group, 2 + XF operations, may be
+                // pending); the barrier makes every wave's W copies visible
+                // and tells this wave that all have finished reading buffer
+                // (kt - 1) % NSW (its fragments were read one k-tile ago)
+                if (XF == 4) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 issue_w(kt + NSW - 1);
                 const int nx = (kt + 1) % NSW;  // after the last k-tile: a stage never used
@@ -672,7 +677,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t 
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
+                for (int j = 0; j < XF; j++) {
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int i = 0; i < 8; i++) acc[i][j] = mfma16(ab[p][i], xb[p][j], acc[i][j]);
@@ -688,42 +693,66 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t 
     for (int i = 0; i < 8; i++) {
         const int n0 = (nb * 16 + wn * 8 + i) * 16;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int m = (mb * 16 + wm * 4 + j) * 16 + (lane & 15);
-            epilogue_frag<KIND>(ep, n0, m, m < M && n0 < N, acc[i][j], lane);
+        for (int j = 0; j < XF; j++) {
+            const int m = (mb * (TOK / 16) + wm * XF + j) * 16 + (lane & 15);
+            epilogue_frag<KIND>(ep, n_base + n0, m, m < M && n0 < N, acc[i][j], lane);
         }
     }
 }
 
-template <int NSW>
-hipError_t launch_tile256_xreg(const GemmArgs &a, hipStream_t s)
+// One launch over W rows [n_base, n_base + N) (a whole number of 256-row
+// blocks from the start of W, or the rest of it).
+template <int NSW, int TOK>
+hipError_t launch_xreg_part(const GemmArgs &a, int n_base, int N, hipStream_t s)
 {
     constexpr int PD = 2;
-    const int NB = (a.N + 255) / 256, MB = (a.M + 255) / 256;
+    const int NB = (N + 255) / 256, MB = (a.M + TOK - 1) / TOK;
     const dim3 grid(NB * MB), blk(512);
     const size_t lds = (size_t)NSW * 1024 * 16;
-    const half_t *W = (const half_t *)a.W, *X = (const half_t *)a.X;
+    const half_t *W = (const half_t *)a.W + (int64_t)n_base * a.K, *X = (const half_t *)a.X;
     switch (a.ep.kind) {
     case EP_STORE:
-        hipLaunchKernelGGL((gemm_tile256_xreg_kernel<EP_STORE, NSW, PD>), grid, blk, lds, s, W, X, a.M, a.N, a.K, a.ep);
+        hipLaunchKernelGGL((gemm_tile256_xreg_kernel<EP_STORE, NSW, PD, TOK>), grid, blk, lds, s, W, X, a.M, N, a.K,
+                           n_base, a.ep);
         break;
     case EP_RESID:
-        hipLaunchKernelGGL((gemm_tile256_xreg_kernel<EP_RESID, NSW, PD>), grid, blk, lds, s, W, X, a.M, a.N, a.K, a.ep);
+        hipLaunchKernelGGL((gemm_tile256_xreg_kernel<EP_RESID, NSW, PD, TOK>), grid, blk, lds, s, W, X, a.M, N, a.K,
+                           n_base, a.ep);
         break;
     case EP_LOGITS:
-        hipLaunchKernelGGL((gemm_tile256_xreg_kernel<EP_LOGITS, NSW, PD>), grid, blk, lds, s, W, X, a.M, a.N, a.K,
-                           a.ep);
+        hipLaunchKernelGGL((gemm_tile256_xreg_kernel<EP_LOGITS, NSW, PD, TOK>), grid, blk, lds, s, W, X, a.M, N, a.K,
+                           n_base, a.ep);
         break;
     case EP_QKV:
-        hipLaunchKernelGGL((gemm_tile256_xreg_kernel<EP_QKV, NSW, PD>), grid, blk, lds, s, W, X, a.M, a.N, a.K, a.ep);
+        hipLaunchKernelGGL((gemm_tile256_xreg_kernel<EP_QKV, NSW, PD, TOK>), grid, blk, lds, s, W, X, a.M, N, a.K,
+                           n_base, a.ep);
         break;
     case EP_SWIGLU:
-        hipLaunchKernelGGL((gemm_tile256_xreg_kernel<EP_SWIGLU, NSW, PD>), grid, blk, lds, s, W, X, a.M, a.N, a.K,
-                           a.ep);
+        hipLaunchKernelGGL((gemm_tile256_xreg_kernel<EP_SWIGLU, NSW, PD, TOK>), grid, blk, lds, s, W, X, a.M, N, a.K,
+                           n_base, a.ep);
         break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// 256 x 256 tiles, one per CU at a time, so a product takes as many tile
+// times as it has waves of 256 tiles.  When the last wave is at most half
+// full and made of whole W block columns (rem = tiles % 256 a multiple of the
+// token blocks), those columns go to a second launch of 256 x 128 tiles,
+// which fills one wave with twice as many half-size tiles.  Every output is
+// summed over K in the same order either way.
+template <int NSW>
+hipError_t launch_tile256_xreg(const GemmArgs &a, hipStream_t s)
+{
+    const int NB = (a.N + 255) / 256, MB = (a.M + 255) / 256;
+    const int rem = (NB * MB) % 256;
+    const int ncols = rem && rem <= 128 && rem % MB == 0 ? rem / MB : 0;
+    if (ncols == 0 || ncols >= NB) return launch_xreg_part<NSW, 256>(a, 0, a.N, s);
+    const int NA = (NB - ncols) * 256;
+    const hipError_t e = launch_xreg_part<NSW, 256>(a, 0, NA, s);
+    if (e != hipSuccess) return e;
+    return launch_xreg_part<NSW, 128>(a, NA, a.N - NA, s);
 }
 
 template <bool XT>
@@ -733,34 +762,35 @@ hipError_t launch_tile256(const GemmArgs &a, hipStream_t s)
         // fp16 models have dim and ffn width multiples of 64: K/32 is even
         if ((a.K >> 5) % 2) return hipErrorInvalidValue;
         return launch_tile256_xreg<5>(a, s);
+    } else {
+        // the eight-wave form with a five-stage ring (measured 4-16% faster than
+        // four waves and four stages on the 7B..70B prefill shapes, same sums)
+        constexpr int NS = 5;
+        const int NB = (a.N + 255) / 256, MB = (a.M + 255) / 256;
+        const dim3 grid(NB * MB), blk(512);
+        const size_t lds = (size_t)NS * 2 * 1024 * 16;
+        const half_t *W = (const half_t *)a.W, *X = (const half_t *)a.X;
+        const int64_t ldx = XT ? 0 : a.ldx;
+        switch (a.ep.kind) {
+        case EP_STORE:
+            hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_STORE, NS>), grid, blk, lds, s, W, X, ldx, a.M, a.N, a.K, a.ep);
+            break;
+        case EP_RESID:
+            hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_RESID, NS>), grid, blk, lds, s, W, X, ldx, a.M, a.N, a.K, a.ep);
+            break;
+        case EP_LOGITS:
+            hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_LOGITS, NS>), grid, blk, lds, s, W, X, ldx, a.M, a.N, a.K, a.ep);
+            break;
+        case EP_QKV:
+            hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_QKV, NS>), grid, blk, lds, s, W, X, ldx, a.M, a.N, a.K, a.ep);
+            break;
+        case EP_SWIGLU:
+            hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_SWIGLU, NS>), grid, blk, lds, s, W, X, ldx, a.M, a.N, a.K, a.ep);
+            break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
     }
-    // the eight-wave form with a five-stage ring (measured 4-16% faster than
-    // four waves and four stages on the 7B..70B prefill shapes, same sums)
-    constexpr int NS = 5;
-    const int NB = (a.N + 255) / 256, MB = (a.M + 255) / 256;
-    const dim3 grid(NB * MB), blk(512);
-    const size_t lds = (size_t)NS * 2 * 1024 * 16;
-    const half_t *W = (const half_t *)a.W, *X = (const half_t *)a.X;
-    const int64_t ldx = XT ? 0 : a.ldx;
-    switch (a.ep.kind) {
-    case EP_STORE:
-        hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_STORE, NS>), grid, blk, lds, s, W, X, ldx, a.M, a.N, a.K, a.ep);
-        break;
-    case EP_RESID:
-        hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_RESID, NS>), grid, blk, lds, s, W, X, ldx, a.M, a.N, a.K, a.ep);
-        break;
-    case EP_LOGITS:
-        hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_LOGITS, NS>), grid, blk, lds, s, W, X, ldx, a.M, a.N, a.K, a.ep);
-        break;
-    case EP_QKV:
-        hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_QKV, NS>), grid, blk, lds, s, W, X, ldx, a.M, a.N, a.K, a.ep);
-        break;
-    case EP_SWIGLU:
-        hipLaunchKernelGGL((gemm_tile256_kernel<XT, EP_SWIGLU, NS>), grid, blk, lds, s, W, X, ldx, a.M, a.N, a.K, a.ep);
-        break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

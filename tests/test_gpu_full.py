@@ -223,6 +223,30 @@ def test_70b_shape_short_prompt_end_to_end(B):
     check_logits(got, want)
 
 
+@pytest.mark.timeout(600)
+def test_13b_shape_one_layer_long_prefill(B):
+    """One 13B-shaped layer with the real embedding and head, the bench's
+    prefill of 8 rows x 1024 tokens: 640 tiles of 256 x 256 for wo and w2
+    and 128 more than whole waves for the others, so every prefill product
+    runs its last W block columns as a second launch of 256 x 128 tiles.
+    Rows 0 and 7 against the oracle."""
+    w = configs.L13B_BS8
+    kw = w.model_kwargs(max_seq_len=1088)
+    kw["n_layers"] = 1
+    T = w.prompt_len
+    toks = synth.tokens(w.token_seed, w.batch, T, w.vocab_size)
+    say("13B-shaped layer: gpu prefill", w.batch, T)
+    h = B.llm_create(B.make_params(**kw), w.weight_seed)
+    h.prefill(toks)
+    got = h.get_logits()
+    h.destroy()
+    rows = [0, w.batch - 1]
+    say("13B-shaped layer: oracle rows", rows)
+    cfg = oracle.Cfg(**dict(kw, max_batch_size=len(rows)))
+    want = oracle.forward_stream(cfg, w.weight_seed, toks[rows], T - 1)[:, 0]
+    check_logits(got[rows], want)
+
+
 @pytest.mark.timeout(900)
 def test_70b_full_depth_vs_oracle(B):
     """All 80 layers of the 70B model, one row, a 4-token prompt and 2 forced
