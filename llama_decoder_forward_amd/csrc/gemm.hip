@@ -152,7 +152,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
                                                               int64_t gtok_ld, half_t *__restrict__ xres)
 {
     extern __shared__ half8 xs[];  // STAGE: [M][K/8]
-    __shared__ floatx4 red[NW][TPB][TWO ? 2 : 1][64];
+    // per-wave partial fragments of RC row blocks at a time (at most 32 KiB)
+    constexpr int RC = TPB < 32 / (NW * (TWO ? 2 : 1)) ? TPB : 32 / (NW * (TWO ? 2 : 1));
+    __shared__ floatx4 red[NW][RC][TWO ? 2 : 1][64];
     __shared__ float pss[NW][2];
     const int nt0 = blockIdx.x * TPB;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -325,18 +327,25 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
                 for (int u = 0; u < U; u++) w[t][u] = (nb + u < KT) ? ldw1<NT>(Wt + ((int64_t)t * KT + nb + u) * 64) : z;
         }
     }
-#pragma unroll
-    for (int t = 0; t < TPB; t++)
-#pragma unroll
-        for (int c = 0; c < (TWO ? 2 : 1); c++) red[wave][t][c][lane] = acc[t][c];
-    __syncthreads();
-    // one accumulator fragment (row block t, row half c) per wave
+    // the waves' fragments are summed in wave order, RC row blocks at a
+    // time; one accumulator fragment (row block t, row half c) per wave
     constexpr int C = TWO ? 2 : 1;
-    for (int pi = wave; pi < TPB * C; pi += NW) {
-        const int t = pi / C, c = pi % C;
-        floatx4 s0 = red[0][t][c][lane];
-        for (int ww = 1; ww < NW; ww++) s0 += red[ww][t][c][lane];
-        epilogue_frag(ep, (nt0 + t) * 16, mc + 16 * c, c ? h1 : h0, s0, lane);
+#pragma unroll
+    for (int t0 = 0; t0 < TPB; t0 += RC) {
+        if (t0) __syncthreads();  // the previous chunk has been read
+#pragma unroll
+        for (int t = 0; t < RC; t++)
+#pragma unroll
+            for (int c = 0; c < C; c++)
+                if (t0 + t < TPB) red[wave][t][c][lane] = acc[t0 + t < TPB ? t0 + t : 0][c];
+        __syncthreads();
+        for (int pi = wave; pi < RC * C; pi += NW) {
+            const int t = pi / C, c = pi % C;
+            if (t0 + t >= TPB) continue;
+            floatx4 s0 = red[0][t][c][lane];
+            for (int ww = 1; ww < NW; ww++) s0 += red[ww][t][c][lane];
+            epilogue_frag(ep, (nt0 + t0 + t) * 16, mc + 16 * c, c ? h1 : h0, s0, lane);
+        }
     }
 }
 
@@ -916,6 +925,11 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
             skinny<2, 4, true, false, false, true, true>(a, W, X, 0, 0, s);
         else if (tiles < 1536 && tiles % 2 == 0)
             skinny<2, 2, true, false, false, true, false>(a, W, X, 0, 0, s);
+        else if (tiles >= 2048 && tiles % 8 == 0)
+            // eight row blocks per work-group read each activation fragment
+            // once for all of them (the CUs' streaming rate, not HBM, bounds
+            // these: 70B w1|w3 155 -> 145 us)
+            skinny<1, 8, true, false, false, true, false>(a, W, X, 0, 0, s);
         else if (tiles % 4 == 0)
             skinny<2, 4, true, false, false, true, false>(a, W, X, 0, 0, s);
         else
