@@ -188,7 +188,11 @@ struct Epilogue {
     KvPages pg;           // block tables of a paged cache (pg.tab NULL: static cache)
     int *pos_advance;     // EP_LOGITS: incremented once after the product (a captured decode step), or NULL
     int out_lay;          // EP_SWIGLU: layout of g (ACT_ROWS with ldo, 1/2 fragment-major, ACT_TILED)
+    // split-K decode products: fp32 workspace for the partial sums
+    // [splits][M][N] (kSplitMaxFloats floats), or NULL (no split)
+    float *part;
 };
+constexpr int64_t kSplitMaxFloats = 4ll * 32 * 8192;
 
 // ---------------------------------------------------------------------------
 // Kernel launchers (each file defines its own); all return hipError_t.

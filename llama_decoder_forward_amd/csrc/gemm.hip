@@ -143,7 +143,8 @@ __device__ __forceinline__ half8 ldw1(const half8 *p)
     return *p;
 }
 
-template <int NW, int U, int TPB, bool TWO, bool STAGE, bool NORM, bool XT = false, bool PF = false, bool NT = false>
+template <int NW, int U, int TPB, bool TWO, bool STAGE, bool NORM, bool XT = false, bool PF = false, bool NT = false,
+          int SPL = 1>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__restrict__ W,
                                                               const half_t *__restrict__ X,
                                                               int64_t ldx, int M, int N, int K,
@@ -156,10 +157,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
     constexpr int RC = TPB < 32 / (NW * (TWO ? 2 : 1)) ? TPB : 32 / (NW * (TWO ? 2 : 1));
     __shared__ floatx4 red[NW][RC][TWO ? 2 : 1][64];
     __shared__ float pss[NW][2];
+    // SPL > 1: split K, work-group (x, y) takes k-tiles [y KT/SPL, (y+1) KT/SPL)
+    // of its row blocks and stores fp32 partial sums (fragment-major X only)
+    static_assert(SPL == 1 || (XT && !STAGE), "split K takes fragment-major activations");
     const int nt0 = blockIdx.x * TPB;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int KT = K >> 5, K8 = K >> 3;
-    const half8 *Wt = reinterpret_cast<const half8 *>(W) + (int64_t)nt0 * KT * 64 + lane;
+    const int KS = K >> 5, K8 = K >> 3;        // k-tiles of a W row block (its stride)
+    const int KT = KS / SPL, kt0 = SPL > 1 ? blockIdx.y * KT : 0;  // this work-group's k-tiles
+    const half8 *Wt = reinterpret_cast<const half8 *>(W) + ((int64_t)nt0 * KS + kt0) * 64 + lane;
     const int mc = lane & 15, g = lane >> 4;
     const bool h0 = mc < M, h1 = mc + 16 < M;
     const half8 z = {};
@@ -170,8 +175,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
     for (int t = 0; t < TPB; t++)
 #pragma unroll
         for (int u = 0; u < U; u++)
-            w[t][u] = PF ? ldw1<NT>(Wt + ((int64_t)t * KT + min(base + u, KT - 1)) * 64)
-                         : (base + u < KT) ? ldw1<NT>(Wt + ((int64_t)t * KT + base + u) * 64) : z;
+            w[t][u] = PF ? ldw1<NT>(Wt + ((int64_t)t * KS + min(base + u, KT - 1)) * 64)
+                         : (base + u < KT) ? ldw1<NT>(Wt + ((int64_t)t * KS + base + u) * 64) : z;
 
     if (STAGE) {
         for (int m = 0; m < M; m++) {
@@ -224,8 +229,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
     const half_t *x1 = X + (int64_t)(h1 ? mc + 16 : 0) * ldx + 8 * g;
     const half8 *xl = STAGE ? xs + (h0 ? mc : 0) * K8 + g : nullptr;
     // fragment-major X: block (kt, half) is 64 lanes x 16 bytes
-    const half8 *xt = reinterpret_cast<const half8 *>(X) + lane;
     constexpr int MH = TWO ? 2 : 1;
+    const half8 *xt = reinterpret_cast<const half8 *>(X) + (int64_t)kt0 * MH * 64 + lane;
 
     floatx4 acc[TPB][TWO ? 2 : 1];
 #pragma unroll
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
 #pragma unroll
             for (int t = 0; t < TPB; t++)
 #pragma unroll
-                for (int u = 0; u < U; u++) d[t][u] = ldw1<NT>(Wt + ((int64_t)t * KT + min(b + u, KT - 1)) * 64);
+                for (int u = 0; u < U; u++) d[t][u] = ldw1<NT>(Wt + ((int64_t)t * KS + min(b + u, KT - 1)) * 64);
         };
         auto round = [&](half8 (&wc)[TPB][U], half8 (&wn)[TPB][U], int b, bool pre) {
             half8 b0[U], b1[TWO ? U : 1];
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
 #pragma unroll
             for (int t = 0; t < TPB; t++)
 #pragma unroll
-                for (int u = 0; u < U; u++) w[t][u] = (nb + u < KT) ? ldw1<NT>(Wt + ((int64_t)t * KT + nb + u) * 64) : z;
+                for (int u = 0; u < U; u++) w[t][u] = (nb + u < KT) ? ldw1<NT>(Wt + ((int64_t)t * KS + nb + u) * 64) : z;
         }
     }
     // the waves' fragments are summed in wave order, RC row blocks at a
@@ -344,7 +349,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
             if (t0 + t >= TPB) continue;
             floatx4 s0 = red[0][t][c][lane];
             for (int ww = 1; ww < NW; ww++) s0 += red[ww][t][c][lane];
-            epilogue_frag(ep, (nt0 + t0 + t) * 16, mc + 16 * c, c ? h1 : h0, s0, lane);
+            if (SPL > 1) {
+                const int m = mc + 16 * c;
+                if (c ? h1 : h0)
+                    *reinterpret_cast<floatx4 *>(ep.part + ((int64_t)blockIdx.y * M + m) * N + (nt0 + t0 + t) * 16 +
+                                                 4 * g) = s0;
+            } else {
+                epilogue_frag(ep, (nt0 + t0 + t) * 16, mc + 16 * c, c ? h1 : h0, s0, lane);
+            }
         }
     }
 }
@@ -881,6 +893,41 @@ __global__ void linear_f32_kernel(const float *W, const float *X, int64_t ldx, i
 
 bool skinny_can_normalise(int M, int K) { return M <= 2 && (int64_t)M * K * 2 <= STAGE_MAX_BYTES; }
 
+namespace {
+// The partial sums of a split-K product added in split order, then the
+// epilogue: one thread per four consecutive outputs of a row.
+template <int KIND>
+__global__ __launch_bounds__(256) void split_reduce_kernel(int S, int M, int N, Epilogue ep)
+{
+    const int n4 = N / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * n4) return;
+    const int m = (int)(i / n4), n = (int)(i % n4) * 4;
+    const floatx4 *p = reinterpret_cast<const floatx4 *>(ep.part + (int64_t)m * N + n);
+    const int64_t stride = (int64_t)M * n4;
+    floatx4 sum = p[0];
+    for (int s = 1; s < S; s++) sum += p[s * stride];
+    epilogue_frag<KIND>(ep, n, m, true, sum, 0);
+}
+}  // namespace
+
+// 17..32 fragment-major rows, residual epilogue: SPL work-groups share each
+// group of TPB row blocks, each over 1/SPL of K, then one reduce launch
+template <int U, int TPB, bool PF, int SPL>
+static hipError_t skinny_split(const GemmArgs &a, const half_t *W, const half_t *X, hipStream_t s)
+{
+    if (a.ep.kind != EP_RESID || !a.ep.part || (a.K >> 5) % SPL || (a.N / 16) % TPB || a.N % 16 ||
+        (int64_t)SPL * a.M * a.N > kSplitMaxFloats)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_skinny_kernel<8, U, TPB, true, false, false, true, PF, true, SPL>), dim3(a.N / 16 / TPB, SPL),
+                       dim3(512), 0, s, W, X, 0, a.M, a.N, a.K, a.ep, (const half_t *)nullptr, 0.f,
+                       (const int32_t *)nullptr, 0, (half_t *)nullptr);
+    const int64_t n4 = (int64_t)a.M * a.N / 4;
+    hipLaunchKernelGGL(split_reduce_kernel<EP_RESID>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, SPL, a.M,
+                       a.N, a.ep);
+    return hipGetLastError();
+}
+
 // One skinny launch: N/16/TPB work-groups of eight waves; the weight stream is
 // read non-temporally (measured on every decode shape: 5-17% faster than
 // cached loads, with the same HBM bytes).
@@ -917,6 +964,12 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
     if (a.x_lay == 2) {
         // fragment-major activations, 17..32 rows (two 16-row halves)
         if (nw || a.M > 32) return hipErrorInvalidValue;
+        if (a.ep.part && a.ep.kind == EP_RESID && a.K >= 16384 && tiles >= 512 && tiles % 8 == 0 &&
+            (a.K >> 5) % 4 == 0 && (int64_t)4 * a.M * a.N <= kSplitMaxFloats)
+            // long residual products (70B w2): eight row blocks per work-group
+            // over a quarter of K, a quarter of the activation block through
+            // each CU, then a reduce launch in split order (85 -> 75 us)
+            return skinny_split<1, 8, false, 4>(a, W, X, s);
         if (tiles <= 256)
             skinny<8, 1, true, false, false, true, true>(a, W, X, 0, 0, s);
         else if (tiles <= 512 && tiles % 2 == 0)

@@ -113,6 +113,7 @@ struct llm {
     char *x = nullptr, *xn = nullptr, *q = nullptr, *o = nullptr, *g = nullptr;
     int2 *rowmap = nullptr;   // varlen prefill: {b, pos} per packed row
     int32_t *vtok = nullptr;  // varlen prefill: packed tokens
+    float *part = nullptr;    // split-K partial sums of decode products (kSplitMaxFloats)
     // state.  Uniform mode: every row at last_pos.  Rows mode (after a varlen
     // prefill): row b at row_last[b], its next token column written when
     // row_next[b] is set.
@@ -191,8 +192,9 @@ int ensure_ws(llm_t *h, int64_t rows)
         h->ws_rows = 0;
     }
     void *p = nullptr;
-    const int64_t br = align256(rows * (int64_t)sizeof(int2)), bt = align256(rows * 4);
-    HIPM(h, hipMalloc(&p, 2 * bx + 2 * bq + bg + br + bt));
+    const int64_t br = align256(rows * (int64_t)sizeof(int2)), bt = align256(rows * 4),
+                  bp = align256(kSplitMaxFloats * (int64_t)sizeof(float));
+    HIPM(h, hipMalloc(&p, 2 * bx + 2 * bq + bg + br + bt + bp));
     h->ws = (char *)p;
     h->x = h->ws;
     h->xn = h->x + bx;
@@ -201,6 +203,7 @@ int ensure_ws(llm_t *h, int64_t rows)
     h->g = h->o + bq;
     h->rowmap = (int2 *)(h->g + bg);
     h->vtok = (int32_t *)((char *)h->rowmap + br);
+    h->part = (float *)((char *)h->vtok + bt);
     h->ws_rows = rows;
     // the captured decode graphs hold the old addresses
     if (h->gexec) {
@@ -560,7 +563,12 @@ hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused)
         return fused ? run_linear(h, l, MAT_W13, h->x, d.D, M, eg, nw)
                      : run_linear(h, l, MAT_W13, h->xn, d.D, M, eg, nullptr, lay);
     }
-    case MAT_W2: return run_linear(h, l, MAT_W2, h->g, d.F, M, make_ep(EP_RESID, h->x, d.D), nullptr, lay);
+    case MAT_W2: {
+        // a long product of 17..32 decode rows may split K (partials in part)
+        Epilogue er = make_ep(EP_RESID, h->x, d.D);
+        er.part = h->part;
+        return run_linear(h, l, MAT_W2, h->g, d.F, M, er, nullptr, lay);
+    }
     default: {
         const char *nw = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
         int64_t ld = 0;
