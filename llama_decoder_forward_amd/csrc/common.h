@@ -192,7 +192,7 @@ struct Epilogue {
     // [splits][M][N] (kSplitMaxFloats floats), or NULL (no split)
     float *part;
 };
-constexpr int64_t kSplitMaxFloats = 4ll * 32 * 8192;
+constexpr int64_t kSplitMaxFloats = 4ll * 32 * 16384;
 
 // ---------------------------------------------------------------------------
 // Kernel launchers (each file defines its own); all return hipError_t.

@@ -548,6 +548,7 @@ hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused)
         eq.T = ps.T;
         eq.H = d.H; eq.Hkv = d.Hkv; eq.hd = d.hd; eq.S = stream_len(h);
         eq.pg = kv_pages(h);
+        eq.part = h->part;  // 17..32 decode rows may split K
         const char *nw = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
         // fused, layer 0: the product gathers the embedding rows itself and
         // stores them into x (no embedding launch)
