@@ -911,17 +911,18 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int S, int M, int N, 
 }
 }  // namespace
 
-// 17..32 fragment-major rows: SPL work-groups share each group of TPB row
-// blocks, each over 1/SPL of K, then one reduce launch applies the epilogue
-// (kinds that work on four outputs of a row at a time: store, residual, qkv)
-template <int U, int TPB, bool PF, int SPL>
+// Fragment-major rows (TWO: 17..32, else up to 16): SPL work-groups share
+// each group of TPB row blocks, each over 1/SPL of K, then one reduce launch
+// applies the epilogue (kinds that work on four outputs of a row at a time:
+// store, residual, qkv)
+template <int U, int TPB, bool PF, int SPL, bool TWO = true>
 static hipError_t skinny_split(const GemmArgs &a, const half_t *W, const half_t *X, hipStream_t s)
 {
     const int kind = a.ep.kind;
     if ((kind != EP_RESID && kind != EP_STORE && kind != EP_QKV) || !a.ep.part || (a.K >> 5) % SPL ||
         (a.N / 16) % TPB || a.N % 16 || (int64_t)SPL * a.M * a.N > kSplitMaxFloats)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_skinny_kernel<8, U, TPB, true, false, false, true, PF, true, SPL>), dim3(a.N / 16 / TPB, SPL),
+    hipLaunchKernelGGL((gemm_skinny_kernel<8, U, TPB, TWO, false, false, true, PF, true, SPL>), dim3(a.N / 16 / TPB, SPL),
                        dim3(512), 0, s, W, X, 0, a.M, a.N, a.K, a.ep, (const half_t *)nullptr, 0.f,
                        (const int32_t *)nullptr, 0, (half_t *)nullptr);
     if (SPL == 1) return hipGetLastError();  // the product applied the epilogue itself
@@ -958,6 +959,12 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
     if (a.x_lay == 1) {
         // fragment-major activations, 3..16 rows
         if (nw || a.M > 16) return hipErrorInvalidValue;
+        if (a.ep.part && a.ep.kind == EP_RESID && a.K >= 8192 && tiles % 5 == 0 && tiles / 5 == 64 &&
+            (a.K >> 5) % 4 == 0 && (int64_t)4 * a.M * a.N <= kSplitMaxFloats)
+            // 320 row blocks of a long K (13B w2): 64 groups of five over a
+            // quarter of K each, 256 work-groups instead of 160 (28.5 -> 26.6 us
+            // in isolation, 26.7 -> 25.7 us in the step)
+            return skinny_split<4, 5, false, 4, false>(a, W, X, s);
         if (tiles < 1024 && tiles % 2 == 0)
             skinny<8, 2, false, false, false, true, false>(a, W, X, 0, 0, s);
         else if (tiles % 4 == 0)
