@@ -213,6 +213,11 @@ struct GemmArgs {
     const int32_t *gather_tok;
     int64_t gather_ld;
     void *gather_out;
+    // residual products of 3..32 fragment-major rows: if not NULL, a split-K
+    // form may leave its partial sums in ep.part for the caller's next
+    // normalisation launch (launch_rmsnorm_resid) instead of reducing them;
+    // *pending is set to the number of splits left there, else 0
+    int *pending;
 };
 
 // Whether the fp16 product normalises its own input rows for M rows of K.
@@ -239,6 +244,11 @@ hipError_t launch_gather_rows(const void *x, const int *idx, int n, int D, int e
 // y_lay: layout of y (fp16 only for non-row-major layouts).
 hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int D, float eps,
                           int dtype, void *y, hipStream_t s, int y_lay = ACT_ROWS);
+// fp16, M <= 64 rows of x [M][D] (row stride D): first adds the split-K
+// partial sums part[S][M][D] of a residual product to x (in split order, with
+// the residual epilogue's rounding) and stores x, then normalises as above
+hipError_t launch_rmsnorm_resid(const float *part, int S, void *x, const void *w, int M, int D, float eps, void *y,
+                                hipStream_t s, int y_lay);
 
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s);
 hipError_t launch_linear_f32(const GemmArgs &a, hipStream_t s);

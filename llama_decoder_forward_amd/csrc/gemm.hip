@@ -916,7 +916,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int S, int M, int N, 
 // applies the epilogue (kinds that work on four outputs of a row at a time:
 // store, residual, qkv)
 template <int U, int TPB, bool PF, int SPL, bool TWO = true>
-static hipError_t skinny_split(const GemmArgs &a, const half_t *W, const half_t *X, hipStream_t s)
+static hipError_t skinny_split(const GemmArgs &a, const half_t *W, const half_t *X, hipStream_t s, bool reduce = true)
 {
     const int kind = a.ep.kind;
     if ((kind != EP_RESID && kind != EP_STORE && kind != EP_QKV) || !a.ep.part || (a.K >> 5) % SPL ||
@@ -925,7 +925,7 @@ static hipError_t skinny_split(const GemmArgs &a, const half_t *W, const half_t 
     hipLaunchKernelGGL((gemm_skinny_kernel<8, U, TPB, TWO, false, false, true, PF, true, SPL>), dim3(a.N / 16 / TPB, SPL),
                        dim3(512), 0, s, W, X, 0, a.M, a.N, a.K, a.ep, (const half_t *)nullptr, 0.f,
                        (const int32_t *)nullptr, 0, (half_t *)nullptr);
-    if (SPL == 1) return hipGetLastError();  // the product applied the epilogue itself
+    if (SPL == 1 || !reduce) return hipGetLastError();  // epilogue applied by the product / left to the caller
     const int64_t n4 = (int64_t)a.M * a.N / 4;
     const dim3 grid((unsigned)((n4 + 255) / 256));
     if (kind == EP_RESID) hipLaunchKernelGGL(split_reduce_kernel<EP_RESID>, grid, dim3(256), 0, s, SPL, a.M, a.N, a.ep);
@@ -947,6 +947,7 @@ static void skinny(const GemmArgs &a, const half_t *W, const half_t *X, int64_t 
 
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
 {
+    if (a.pending) *a.pending = 0;
     if (a.M <= 0) return hipSuccess;
     const half_t *W = (const half_t *)a.W, *X = (const half_t *)a.X, *nw = (const half_t *)a.norm_w;
     if (nw && !skinny_can_normalise(a.M, a.K)) return hipErrorInvalidValue;
@@ -959,12 +960,6 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
     if (a.x_lay == 1) {
         // fragment-major activations, 3..16 rows
         if (nw || a.M > 16) return hipErrorInvalidValue;
-        if (a.ep.part && a.ep.kind == EP_RESID && a.K >= 8192 && tiles % 5 == 0 && tiles / 5 == 64 &&
-            (a.K >> 5) % 4 == 0 && (int64_t)4 * a.M * a.N <= kSplitMaxFloats)
-            // 320 row blocks of a long K (13B w2): 64 groups of five over a
-            // quarter of K each, 256 work-groups instead of 160 (28.5 -> 26.6 us
-            // in isolation, 26.7 -> 25.7 us in the step)
-            return skinny_split<4, 5, false, 4, false>(a, W, X, s);
         if (tiles < 1024 && tiles % 2 == 0)
             skinny<8, 2, false, false, false, true, false>(a, W, X, 0, 0, s);
         else if (tiles % 4 == 0)
@@ -977,11 +972,28 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
         // fragment-major activations, 17..32 rows (two 16-row halves)
         if (nw || a.M > 32) return hipErrorInvalidValue;
         if (a.ep.part && a.ep.kind == EP_RESID && a.K >= 16384 && tiles >= 512 && tiles % 8 == 0 &&
-            (a.K >> 5) % 4 == 0 && (int64_t)4 * a.M * a.N <= kSplitMaxFloats)
+            (a.K >> 5) % 4 == 0 && (int64_t)4 * a.M * a.N <= kSplitMaxFloats) {
             // long residual products (70B w2): eight row blocks per work-group
             // over a quarter of K, a quarter of the activation block through
-            // each CU, then a reduce launch in split order (85 -> 75 us)
-            return skinny_split<1, 8, false, 4>(a, W, X, s);
+            // each CU, then a reduce launch in split order (85 -> 75 us; 72 us
+            // when the next normalisation adds the partials)
+            if (a.pending) *a.pending = 4;
+            return skinny_split<1, 8, false, 4>(a, W, X, s, !a.pending);
+        }
+        if (a.pending && a.ep.part && a.ep.kind == EP_RESID && tiles == 256 && (int64_t)4 * a.M * a.N <= kSplitMaxFloats) {
+            // 256 row blocks (7B wo, w2) only when the next normalisation adds
+            // the partials (a reduce launch of their own costs more than the
+            // split gains): four row blocks over a quarter of K for long K
+            // (w2: 22.8 -> 18.3 us), else two over half of K (wo: 10.3 -> 9.0 us)
+            if (a.K >= 8192 && (a.K >> 5) % 4 == 0) {
+                *a.pending = 4;
+                return skinny_split<2, 4, false, 4>(a, W, X, s, false);
+            }
+            if ((a.K >> 5) % 2 == 0) {
+                *a.pending = 2;
+                return skinny_split<2, 2, true, 2>(a, W, X, s, false);
+            }
+        }
         if (a.ep.part && a.ep.kind == EP_QKV && tiles % 5 == 0 && tiles / 5 == 128 && (a.K >> 5) % 2 == 0 &&
             (int64_t)2 * a.M * a.N <= kSplitMaxFloats)
             // 640 row blocks (70B wq|wk|wv): 128 groups of five over half of

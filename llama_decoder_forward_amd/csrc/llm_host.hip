@@ -397,9 +397,10 @@ const char *mat_ptr(llm_t *h, int layer, int mat)
 
 hipError_t run_linear(llm_t *h, int layer, int mat, const void *X, int64_t ldx, int M,
                       const Epilogue &ep, const void *norm_w = nullptr, int x_lay = ACT_ROWS,
-                      const int32_t *gather_tok = nullptr)
+                      const int32_t *gather_tok = nullptr, int *pending = nullptr)
 {
     GemmArgs a{};
+    a.pending = pending;
     a.gather_tok = gather_tok;
     a.gather_ld = h->d.S;
     a.gather_out = h->x;
@@ -529,7 +530,9 @@ const char *head_rows(llm_t *h, const Pass &ps, int64_t *ld)
     return h->x + (int64_t)(ps.T - 1) * h->d.D * h->d.es;
 }
 
-hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused)
+// pending (wo, w2): see GemmArgs::pending; NULL to have the product reduce
+// any split itself
+hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused, int *pending = nullptr)
 {
     const Dims &d = h->d;
     const int M = ps.M;
@@ -556,7 +559,11 @@ hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused)
         return fused ? run_linear(h, l, MAT_QKV, h->x, d.D, M, eq, nw)
                      : run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq, nullptr, lay);
     }
-    case MAT_O: return run_linear(h, l, MAT_O, h->o, qd, M, make_ep(EP_RESID, h->x, d.D), nullptr, lay);
+    case MAT_O: {
+        Epilogue er = make_ep(EP_RESID, h->x, d.D);
+        er.part = h->part;
+        return run_linear(h, l, MAT_O, h->o, qd, M, er, nullptr, lay, nullptr, pending);
+    }
     case MAT_W13: {
         const char *nw = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
         Epilogue eg = make_ep(EP_SWIGLU, h->g, d.F);
@@ -568,7 +575,7 @@ hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused)
         // a long product of 17..32 decode rows may split K (partials in part)
         Epilogue er = make_ep(EP_RESID, h->x, d.D);
         er.part = h->part;
-        return run_linear(h, l, MAT_W2, h->g, d.F, M, er, nullptr, lay);
+        return run_linear(h, l, MAT_W2, h->g, d.F, M, er, nullptr, lay, nullptr, pending);
     }
     default: {
         const char *nw = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
@@ -629,11 +636,24 @@ hipError_t forward(llm_t *h, const Pass &ps, Prof *pf = nullptr)
         TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, M, ps.T, ps.pos_dev, ps.pos0, ps.pos_rows, ps.rowmap, d.D,
                                     d.dtype, h->x, s));
     const int lay = act_layout(h, ps);
+    // split-K partial sums the last residual product left in h->part for the
+    // next normalisation launch to add to x (0: none); only where a
+    // normalisation launch follows every residual product
+    int pend = 0;
+    int *defer = fused ? nullptr : &pend;
+    auto norm = [&](const void *nw_, int rows) -> hipError_t {
+        if (pend) {
+            const int sp = pend;
+            pend = 0;
+            return launch_rmsnorm_resid(h->part, sp, h->x, nw_, rows, d.D, h->p.norm_eps, h->xn, s, lay);
+        }
+        return launch_rmsnorm(h->x, d.D, nw_, rows, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay);
+    };
     for (int l = 0; l < d.NL; l++) {
         const char *nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
         const char *nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
         // attention_norm -> wq|wk|wv with RoPE and the KV-cache write
-        if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_attn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay));
+        if (!fused) TRYC(PC_NORM, norm(nw_attn, M));
         TRYC(PC_QKV, product(h, l, MAT_QKV, ps, fused));
         // attention over the cache
         AttnArgs aa{};
@@ -649,11 +669,11 @@ hipError_t forward(llm_t *h, const Pass &ps, Prof *pf = nullptr)
         else if (ps.decode()) TRYC(PC_ATTN, launch_attn_decode_f16(aa, s));
         else TRYC(PC_ATTN, launch_attn_prefill_f16(aa, s));
         // wo + residual
-        TRYC(PC_O, product(h, l, MAT_O, ps, fused));
+        TRYC(PC_O, product(h, l, MAT_O, ps, fused, defer));
         // ffn_norm -> w1|w3 with SwiGLU -> w2 + residual
-        if (!fused) TRYC(PC_NORM, launch_rmsnorm(h->x, d.D, nw_ffn, M, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay));
+        if (!fused) TRYC(PC_NORM, norm(nw_ffn, M));
         TRYC(PC_W13, product(h, l, MAT_W13, ps, fused));
-        TRYC(PC_W2, product(h, l, MAT_W2, ps, fused));
+        TRYC(PC_W2, product(h, l, MAT_W2, ps, fused, l + 1 < d.NL ? defer : nullptr));
     }
     // final norm on the last position of each row, output head, fp32 logits
     if (ps.rowmap) TRYC(PC_HEAD, launch_gather_rows(h->x, ps.last_rows, B, d.D, d.es, h->q, s));

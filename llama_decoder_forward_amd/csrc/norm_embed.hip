@@ -101,8 +101,13 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64
 // each wave adds by butterflies and the waves' sums are added in wave order:
 // the order of the normalisation staged inside the one- and two-row
 // products, so a row normalises to the same bits on either path.
+// PART: x first receives the split-K partial sums part[S][M][D] of the
+// residual product that wrote it (added in split order, then rounded as the
+// residual epilogue rounds), and the new row is stored back to x.
+template <bool PART = false>
 __global__ __launch_bounds__(512) void rmsnorm_row_kernel(const half_t *x, int64_t ldx, const half_t *w, int D,
-                                                          float eps, half_t *y, int y_lay)
+                                                          float eps, half_t *y, int y_lay, const float *part = nullptr,
+                                                          int S = 0)
 {
 #pragma clang fp contract(off)
     __shared__ float pss[8];
@@ -118,6 +123,26 @@ __global__ __launch_bounds__(512) void rmsnorm_row_kernel(const half_t *x, int64
         if (i < nv) {
             v[j] = xr[i];
             wv[j] = wr[i];
+        }
+    }
+    if (PART) {
+        const int64_t plane = (int64_t)gridDim.x * D;
+#pragma unroll
+        for (int j = 0; j < R; j++) {
+            const int i = tid + 512 * j;
+            if (i < nv) {
+                const float4 *p = reinterpret_cast<const float4 *>(part + (int64_t)row * D + 8 * i);
+                float4 a0 = p[0], a1 = p[1];
+                for (int sp = 1; sp < S; sp++) {
+                    const float4 b0 = p[sp * plane / 4], b1 = p[sp * plane / 4 + 1];
+                    a0.x += b0.x; a0.y += b0.y; a0.z += b0.z; a0.w += b0.w;
+                    a1.x += b1.x; a1.y += b1.y; a1.z += b1.z; a1.w += b1.w;
+                }
+                const float t[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+                for (int e = 0; e < 8; e++) v[j][e] = (half_t)((float)v[j][e] + (float)(half_t)t[e]);
+                reinterpret_cast<half8 *>(const_cast<half_t *>(x) + (int64_t)row * ldx)[i] = v[j];
+            }
         }
     }
     float ss = 0.f;
@@ -193,13 +218,24 @@ hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int 
     if (y_lay && (dtype != 1 || D % 32)) return hipErrorInvalidValue;
     if ((y_lay == 1 || y_lay == 2) && M > 16 * y_lay) return hipErrorInvalidValue;
     if (dtype == 1 && M <= 64)
-        hipLaunchKernelGGL(rmsnorm_row_kernel, dim3(M), dim3(512), 0, s, (const half_t *)x, ldx, (const half_t *)w, D,
-                           eps, (half_t *)y, y_lay);
+        hipLaunchKernelGGL(rmsnorm_row_kernel<false>, dim3(M), dim3(512), 0, s, (const half_t *)x, ldx,
+                           (const half_t *)w, D, eps, (half_t *)y, y_lay, (const float *)nullptr, 0);
     else if (dtype == 1)
         hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((M + 3) / 4), dim3(256), 0, s, (const half_t *)x, ldx,
                            (const half_t *)w, M, D, eps, (half_t *)y, y_lay);
     else
         hipLaunchKernelGGL(rmsnorm_f32_kernel, dim3(M), dim3(kThreads), 0, s, (const float *)x, ldx,
                            (const float *)w, D, eps, (float *)y);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_resid(const float *part, int S, void *x, const void *w, int M, int D, float eps, void *y,
+                                hipStream_t s, int y_lay)
+{
+    if (M <= 0) return hipSuccess;
+    if (!part || S < 1 || M > 64 || D % 32 || D > 64 * 8 * RMS_VEC) return hipErrorInvalidValue;
+    if ((y_lay == 1 || y_lay == 2) && M > 16 * y_lay) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rmsnorm_row_kernel<true>, dim3(M), dim3(512), 0, s, (const half_t *)x, (int64_t)D,
+                       (const half_t *)w, D, eps, (half_t *)y, y_lay, part, S);
     return hipGetLastError();
 }

@@ -61,6 +61,13 @@ hipError_t launch_read_weights(const void *, int, int, int64_t, int64_t, int, in
 hipError_t launch_embed(const void *, const int32_t *, int64_t, int, int, const int *, int, const int *, const int2 *, int, int, void *, hipStream_t) { return hipSuccess; }
 hipError_t launch_gather_rows(const void *, const int *, int, int, int, void *, hipStream_t) { return hipSuccess; }
 hipError_t launch_rmsnorm(const void *, int64_t, const void *, int, int, float, int, void *, hipStream_t, int) { return hipSuccess; }
+// the partial sums and the rows the residual form reads and writes
+hipError_t launch_rmsnorm_resid(const float *part, int S, void *x, const void *, int M, int D, float, void *, hipStream_t, int)
+{
+    CHECK(part, (size_t)S * M * D * sizeof(float));
+    CHECK(x, (size_t)M * D * 2);
+    return hipSuccess;
+}
 
 // the cache addresses the KV write of rows (b, pos) touches
 static int g_es = 2;

@@ -9,8 +9,8 @@
   B = 8 / 32, attended length of a mid-run decode step), sampled outputs
   checked one by one against the oracle; a 70B-shaped model (two layers:
   weights depend only on (seed, layer, tensor)) end to end on a short prompt,
-  one such layer at 32 rows and a 13B-shaped one at 8 rows (the decode
-  products' split-K forms);
+  two such layers at 32 rows (the decode products' split-K forms) and two
+  13B-shaped ones at 8 rows;
   and properties of the full models that hold at any size (bit-identical
   reruns, batch-row permutation, prefill vs prefill + decode).
 """
@@ -227,20 +227,22 @@ def test_70b_shape_short_prompt_end_to_end(B):
 
 @pytest.mark.timeout(600)
 def test_70b_shape_32_rows_decode(B):
-    """One 70B-shaped layer with the real embedding and head at 32 rows: the
+    """Two 70B-shaped layers with the real embedding and head at 32 rows: the
     decode products take their 17..32-row forms, w2 (K = 28672) split over K
-    into four partial sums added by a second launch.  A 12-token prompt and 3
-    forced decode steps; rows 0 and 31 against the oracle."""
+    into four partial sums, added by the next layer's attention_norm launch
+    (layer 0) or by a reduce launch of their own (the last layer).  A
+    12-token prompt and 3 forced decode steps; rows 0 and 31 against the
+    oracle."""
     w = configs.L70B_BS32
     kw = w.model_kwargs(max_batch_size=32, max_seq_len=64)
-    kw["n_layers"] = 1
+    kw["n_layers"] = 2
     toks = synth.tokens(w.token_seed, 32, 15, w.vocab_size)
-    say("70B-shaped layer, 32 rows: gpu")
+    say("70B-shaped layers, 32 rows: gpu")
     h = B.llm_create(B.make_params(**kw), w.weight_seed)
     got = forced(h, toks, 12, 3)
     h.destroy()
     rows = [0, 31]
-    say("70B-shaped layer, 32 rows: oracle rows", rows)
+    say("70B-shaped layers, 32 rows: oracle rows", rows)
     cfg = oracle.Cfg(**dict(kw, max_batch_size=len(rows)))
     want = oracle.forward_stream(cfg, w.weight_seed, toks[rows], 11)
     check_logits(got[rows], want)
@@ -248,20 +250,19 @@ def test_70b_shape_32_rows_decode(B):
 
 @pytest.mark.timeout(600)
 def test_13b_shape_8_rows_decode(B):
-    """One 13B-shaped layer with the real embedding and head at 8 rows: the
-    decode products take their 3..16-row forms, w2 (K = 13824) split over K
-    into four partial sums added by a second launch.  A 12-token prompt and 3
-    forced decode steps; rows 0 and 7 against the oracle."""
+    """Two 13B-shaped layers with the real embedding and head at 8 rows (the
+    decode products' 3..16-row forms).  A 12-token prompt and 3 forced
+    decode steps; rows 0 and 7 against the oracle."""
     w = configs.L13B_BS8
     kw = w.model_kwargs(max_batch_size=8, max_seq_len=64)
-    kw["n_layers"] = 1
+    kw["n_layers"] = 2
     toks = synth.tokens(w.token_seed, 8, 15, w.vocab_size)
-    say("13B-shaped layer, 8 rows: gpu")
+    say("13B-shaped layers, 8 rows: gpu")
     h = B.llm_create(B.make_params(**kw), w.weight_seed)
     got = forced(h, toks, 12, 3)
     h.destroy()
     rows = [0, 7]
-    say("13B-shaped layer, 8 rows: oracle rows", rows)
+    say("13B-shaped layers, 8 rows: oracle rows", rows)
     cfg = oracle.Cfg(**dict(kw, max_batch_size=len(rows)))
     want = oracle.forward_stream(cfg, w.weight_seed, toks[rows], 11)
     check_logits(got[rows], want)
