@@ -359,9 +359,9 @@ hipError_t launch_decode(const AttnArgs &a, hipStream_t s)
     const int pairs = a.B * a.Hkv;
     const half_t *q = (const half_t *)a.q, *kc = (const half_t *)a.kcache, *vc = (const half_t *)a.vcache;
     half_t *o = (half_t *)a.out;
-    if (pairs >= 512)
-        hipLaunchKernelGGL((attn_decode_kernel<2, true, PAGED>), dim3(pairs), dim3(128), 0, s, q, kc, vc, a.H, a.Hkv,
-                           a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
+    if (pairs >= 512)  // non-temporal K/V loads: 7B bs32 30.9 -> 29.6 us (L = 204), 51.9 -> 48.5 us (L = 512)
+        hipLaunchKernelGGL((attn_decode_kernel<2, true, PAGED, true>), dim3(pairs), dim3(128), 0, s, q, kc, vc, a.H,
+                           a.Hkv, a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
     else if (pairs >= 300)  // 320 pairs (13B bs8); 256 (70B bs32) do better with eight
         hipLaunchKernelGGL((attn_decode_kernel<4, false, PAGED>), dim3(pairs), dim3(256), 0, s, q, kc, vc, a.H, a.Hkv,
                            a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);

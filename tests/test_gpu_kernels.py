@@ -230,7 +230,7 @@ def test_attention_decode(B, small, L):
 def test_attention_decode_many_pairs(B, Bn, L, S):
     """Bn * n_kv_heads (row, KV head) pairs: 128 pairs take the eight-wave
     work-groups with non-temporal K/V loads, 320 the four-wave ones, 512 the two-wave ones with the next
-    step prefetched; caches of 320 and 1024 positions, ragged last steps,
+    step prefetched (non-temporal too); caches of 320 and 1024 positions, ragged last steps,
     long contexts and a single key included."""
     kw = small_f16(max_batch_size=Bn, max_seq_len=S)
     h = B.llm_create(B.make_params(**kw), 78)
