@@ -34,7 +34,7 @@ constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp(m_old 
 // ...; each wave keeps the running max / sum / unnormalised output of all
 // n_rep query heads of the group, so every K/V byte is read once per query
 // group.  PF: a wave's next step is loaded while the current one computes.
-// The NW waves are merged in LDS in halving rounds (fixed order), and the
+// The NW waves are merged in LDS in one round (fixed order), and the
 // normalised output written.  Few (row, KV head) pairs take 8 waves (the
 // work-group count, not the bandwidth, is the limit there); many pairs
 // take 2 or 4 so that more of them fit the CUs at once.  PAGED: each 32-key
@@ -48,8 +48,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
     int H, int Hkv, int S, KvPages pg, const int *pos_dev, int pos_imm, const int *pos_rows,
     half_t *__restrict__ out, int out_lay)
 {
-    __shared__ floatx4 so[NW / 2][8][64];
-    __shared__ float sm[NW / 2][16], sl[NW / 2][16];
+    __shared__ floatx4 so[NW][8][64];
+    __shared__ float sm[NW][16], sl[NW][16];
     const int bk = blockIdx.x, b = bk / Hkv, kvh = bk % Hkv;
     const int L = (pos_rows ? pos_rows[b] : (pos_dev ? *pos_dev : pos_imm)) + 1;
     adec::attn_decode_wg<NW, PF, PAGED, false, NT>(q, kc, vc, H, Hkv, S, pg, b, kvh, L, out, out_lay, so, sm, sl);

@@ -11,13 +11,13 @@
 // sub-tile t is key 8*(r/4) + 4*t + r%4, so the accumulator lane group g
 // holds keys 8g..8g+7 of the step -- exactly the B-operand k-group of P^T --
 // and the matching V^T operand is one contiguous 16-byte load.  PF: a wave's
-// next step is loaded while the current one computes.  The NW waves are
-// merged in LDS in halving rounds (fixed order).  PAGED: each 32-key step
+// next step is loaded while the current one computes.  PAGED: each 32-key step
 // lies in one block of the row's table; the table entries the row uses are
 // held in lanes and read with readlane.  COH: q and the step holding the
 // current position are read with device-coherent loads and the output is
 // stored device-coherently (data written and read inside one kernel by work
-// groups on different XCDs).  NT: K and V are read non-temporally.
+// groups on different XCDs).  NT: K and V are read non-temporally.  The NW
+// waves' states are merged in one round through LDS (fixed wave order).
 #pragma once
 #include "common.h"
 
@@ -46,6 +46,7 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
                                                const half_t *__restrict__ vc, int H, int Hkv, int S, const KvPages &pg,
                                                int b, int kvh, int L, half_t *__restrict__ out, int out_lay,
                                                floatx4 (*so)[8][64], float (*sm)[16], float (*sl)[16])
+// so, sm, sl: LDS for the states of all NW waves
 {
     constexpr int hd = 128;
     // the wave index is uniform across the wave: in a scalar register, so the
@@ -191,37 +192,36 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
         }
     }
 
-    // merge: in each round the upper half of the live waves hands its state to
-    // the lower half (lane (r, g) holds O^T[16 dt + 4 g + i][head r])
-    for (int half = NW / 2; half >= 1; half >>= 1) {
-        if (wave >= half && wave < 2 * half) {
+    // merge in one round: every wave hands its state to LDS; after one
+    // barrier wave w combines the column blocks dt = w, w + NW, ... over all
+    // waves in wave order and stores them (lane (r, g) holds
+    // O^T[16 dt + 4 g + i][head r])
 #pragma unroll
-            for (int dt = 0; dt < 8; dt++) so[wave - half][dt][lane] = acc[dt];
-            if (g == 0) {
-                sm[wave - half][r] = mrun;
-                sl[wave - half][r] = lrun;
-            }
-        }
-        __syncthreads();
-        if (wave < half) {
-            const float mo = sm[wave][r], lo = sl[wave][r];
-            const float M = fmaxf(mrun, mo);
-            const float fa = __builtin_amdgcn_exp2f(mrun - M), fb = __builtin_amdgcn_exp2f(mo - M);
-#pragma unroll
-            for (int dt = 0; dt < 8; dt++) acc[dt] = acc[dt] * fa + so[wave][dt][lane] * fb;
-            lrun = lrun * fa + lo * fb;
-            mrun = M;
-        }
-        __syncthreads();
+    for (int dt = 0; dt < 8; dt++) so[wave][dt][lane] = acc[dt];
+    if (g == 0) {
+        sm[wave][r] = mrun;
+        sl[wave][r] = lrun;
     }
-    if (wave == 0 && qv) {
-        half_t *orow = out + ((int64_t)b * H + h) * hd;
-        const float inv = 1.0f / lrun;
+    __syncthreads();
+    float M = sm[0][r];
 #pragma unroll
-        for (int dt = 0; dt < 8; dt++) {
+    for (int w = 1; w < NW; w++) M = fmaxf(M, sm[w][r]);
+    float fw[NW], l = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+        fw[w] = __builtin_amdgcn_exp2f(sm[w][r] - M);
+        l += sl[w][r] * fw[w];
+    }
+    const float inv = 1.0f / l;
+    for (int dt = wave; dt < 8; dt += NW) {
+        floatx4 o = so[0][dt][lane] * fw[0];
+#pragma unroll
+        for (int w = 1; w < NW; w++) o += so[w][dt][lane] * fw[w];
+        if (qv) {
             half4 hv;
-            for (int i = 0; i < 4; i++) hv[i] = (half_t)(acc[dt][i] * inv);
+            for (int i = 0; i < 4; i++) hv[i] = (half_t)(o[i] * inv);
             const int c = 16 * dt + 4 * g;  // 4 consecutive columns inside one 8-column group
+            half_t *orow = out + ((int64_t)b * H + h) * hd;
             if (COH) st_coh_half4(orow + c, hv);
             else if (out_lay) *reinterpret_cast<half4 *>(out + act_offset(b, (int64_t)h * hd + c, (int64_t)H * hd, 0, out_lay)) = hv;
             else *reinterpret_cast<half4 *>(orow + c) = hv;

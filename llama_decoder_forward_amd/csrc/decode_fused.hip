@@ -183,8 +183,8 @@ __global__ __launch_bounds__(FNT, 1) void decode_layer_kernel(LayerArgs a)
     extern __shared__ half8 xs[];  // the staged activation row
     __shared__ floatx4 red[2][FNW][64];
     __shared__ float pss[FNW];
-    __shared__ floatx4 so[FNW / 2][8][64];
-    __shared__ float sm[FNW / 2][16], sl[FNW / 2][16];
+    __shared__ floatx4 so[FNW][8][64];
+    __shared__ float sm[FNW][16], sl[FNW][16];
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int mc = lane & 15, g = lane >> 4;
     const int wg = blockIdx.x, G = gridDim.x;
