@@ -103,11 +103,11 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64
 // products, so a row normalises to the same bits on either path.
 // PART: x first receives the split-K partial sums part[S][M][D] of the
 // residual product that wrote it (added in split order, then rounded as the
-// residual epilogue rounds), and the new row is stored back to x.
+// residual epilogue rounds), and the new row is stored to xout (x itself).
 template <bool PART = false>
 __global__ __launch_bounds__(512) void rmsnorm_row_kernel(const half_t *x, int64_t ldx, const half_t *w, int D,
                                                           float eps, half_t *y, int y_lay, const float *part = nullptr,
-                                                          int S = 0)
+                                                          int S = 0, half_t *xout = nullptr)
 {
 #pragma clang fp contract(off)
     __shared__ float pss[8];
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(512) void rmsnorm_row_kernel(const half_t *x, int64
                 const float t[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
                 for (int e = 0; e < 8; e++) v[j][e] = (half_t)((float)v[j][e] + (float)(half_t)t[e]);
-                reinterpret_cast<half8 *>(const_cast<half_t *>(x) + (int64_t)row * ldx)[i] = v[j];
+                reinterpret_cast<half8 *>(xout + (int64_t)row * ldx)[i] = v[j];
             }
         }
     }
@@ -219,7 +219,8 @@ hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int 
     if ((y_lay == 1 || y_lay == 2) && M > 16 * y_lay) return hipErrorInvalidValue;
     if (dtype == 1 && M <= 64)
         hipLaunchKernelGGL(rmsnorm_row_kernel<false>, dim3(M), dim3(512), 0, s, (const half_t *)x, ldx,
-                           (const half_t *)w, D, eps, (half_t *)y, y_lay, (const float *)nullptr, 0);
+                           (const half_t *)w, D, eps, (half_t *)y, y_lay, (const float *)nullptr, 0,
+                           (half_t *)nullptr);
     else if (dtype == 1)
         hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((M + 3) / 4), dim3(256), 0, s, (const half_t *)x, ldx,
                            (const half_t *)w, M, D, eps, (half_t *)y, y_lay);
@@ -236,6 +237,6 @@ hipError_t launch_rmsnorm_resid(const float *part, int S, void *x, const void *w
     if (!part || S < 1 || M > 64 || D % 32 || D > 64 * 8 * RMS_VEC) return hipErrorInvalidValue;
     if ((y_lay == 1 || y_lay == 2) && M > 16 * y_lay) return hipErrorInvalidValue;
     hipLaunchKernelGGL(rmsnorm_row_kernel<true>, dim3(M), dim3(512), 0, s, (const half_t *)x, (int64_t)D,
-                       (const half_t *)w, D, eps, (half_t *)y, y_lay, part, S);
+                       (const half_t *)w, D, eps, (half_t *)y, y_lay, part, S, (half_t *)x);
     return hipGetLastError();
 }
