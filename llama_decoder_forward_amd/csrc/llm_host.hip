@@ -1569,15 +1569,22 @@ hipError_t projection_pass(llm_t *h, int kind, int reps, bool fused, int *launch
     const int B = h->cur_B, NL = h->d.NL;
     hipError_t e = hipSuccess;
     *launches = 0;
+    // the products take the forms of a decode step: wo, and w2 but the last
+    // layer's, may hand split-K partials to the next normalisation launch
+    // (not run here: only the products are timed)
+    int unused = 0;
+    auto hand = [&](int mat, int l) -> int * {
+        return !fused && (mat == MAT_O || (mat == MAT_W2 && l + 1 < NL)) ? &unused : nullptr;
+    };
     for (int r = 0; r < reps && e == hipSuccess; r++) {
         if (kind < 5) {
             const int per_rep = kinds[kind] == MAT_HEAD ? 1 : NL;
             for (int l = 0; l < per_rep && e == hipSuccess; l++, ++*launches)
-                e = product(h, l, kinds[kind], uniform_pass(B, 1, h->pos_dev), fused);
+                e = product(h, l, kinds[kind], uniform_pass(B, 1, h->pos_dev), fused, hand(kinds[kind], l));
         } else {
             for (int l = 0; l < NL && e == hipSuccess; l++)
                 for (int k = 0; k < 4 && e == hipSuccess; k++, ++*launches)
-                    e = product(h, l, kinds[k], uniform_pass(B, 1, h->pos_dev), fused);
+                    e = product(h, l, kinds[k], uniform_pass(B, 1, h->pos_dev), fused, hand(kinds[k], l));
             if (e == hipSuccess) e = product(h, 0, MAT_HEAD, uniform_pass(B, 1, h->pos_dev), fused);
             ++*launches;
         }
