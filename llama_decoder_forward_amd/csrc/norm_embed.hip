@@ -101,15 +101,18 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64
 // each wave adds by butterflies and the waves' sums are added in wave order:
 // the order of the normalisation staged inside the one- and two-row
 // products, so a row normalises to the same bits on either path.
-// PART: x first receives the split-K partial sums part[S][M][D] of the
+// S > 0: x first receives the split-K partial sums part[S][M][D] of the
 // residual product that wrote it (added in split order, then rounded as the
 // residual epilogue rounds), and the new row is stored to xout (x itself).
-template <bool PART = false>
+// S is a template argument so that the loads of all S planes are issued
+// before the first addition.
+template <int S = 0>
 __global__ __launch_bounds__(512) void rmsnorm_row_kernel(const half_t *x, int64_t ldx, const half_t *w, int D,
                                                           float eps, half_t *y, int y_lay, const float *part = nullptr,
-                                                          int S = 0, half_t *xout = nullptr)
+                                                          half_t *xout = nullptr)
 {
 #pragma clang fp contract(off)
+    constexpr bool PART = S > 0;
     __shared__ float pss[8];
     const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const half8 *xr = reinterpret_cast<const half8 *>(x + (int64_t)row * ldx);
@@ -132,11 +135,17 @@ __global__ __launch_bounds__(512) void rmsnorm_row_kernel(const half_t *x, int64
             const int i = tid + 512 * j;
             if (i < nv) {
                 const float4 *p = reinterpret_cast<const float4 *>(part + (int64_t)row * D + 8 * i);
-                float4 a0 = p[0], a1 = p[1];
+                float4 b0[S > 0 ? S : 1], b1[S > 0 ? S : 1];
+#pragma unroll
+                for (int sp = 0; sp < S; sp++) {
+                    b0[sp] = p[sp * plane / 4];
+                    b1[sp] = p[sp * plane / 4 + 1];
+                }
+                float4 a0 = b0[0], a1 = b1[0];
+#pragma unroll
                 for (int sp = 1; sp < S; sp++) {
-                    const float4 b0 = p[sp * plane / 4], b1 = p[sp * plane / 4 + 1];
-                    a0.x += b0.x; a0.y += b0.y; a0.z += b0.z; a0.w += b0.w;
-                    a1.x += b1.x; a1.y += b1.y; a1.z += b1.z; a1.w += b1.w;
+                    a0.x += b0[sp].x; a0.y += b0[sp].y; a0.z += b0[sp].z; a0.w += b0[sp].w;
+                    a1.x += b1[sp].x; a1.y += b1[sp].y; a1.z += b1[sp].z; a1.w += b1[sp].w;
                 }
                 const float t[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
@@ -218,9 +227,8 @@ hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int 
     if (y_lay && (dtype != 1 || D % 32)) return hipErrorInvalidValue;
     if ((y_lay == 1 || y_lay == 2) && M > 16 * y_lay) return hipErrorInvalidValue;
     if (dtype == 1 && M <= 64)
-        hipLaunchKernelGGL(rmsnorm_row_kernel<false>, dim3(M), dim3(512), 0, s, (const half_t *)x, ldx,
-                           (const half_t *)w, D, eps, (half_t *)y, y_lay, (const float *)nullptr, 0,
-                           (half_t *)nullptr);
+        hipLaunchKernelGGL(rmsnorm_row_kernel<0>, dim3(M), dim3(512), 0, s, (const half_t *)x, ldx,
+                           (const half_t *)w, D, eps, (half_t *)y, y_lay, (const float *)nullptr, (half_t *)nullptr);
     else if (dtype == 1)
         hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((M + 3) / 4), dim3(256), 0, s, (const half_t *)x, ldx,
                            (const half_t *)w, M, D, eps, (half_t *)y, y_lay);
@@ -236,7 +244,13 @@ hipError_t launch_rmsnorm_resid(const float *part, int S, void *x, const void *w
     if (M <= 0) return hipSuccess;
     if (!part || S < 1 || M > 64 || D % 32 || D > 64 * 8 * RMS_VEC) return hipErrorInvalidValue;
     if ((y_lay == 1 || y_lay == 2) && M > 16 * y_lay) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(rmsnorm_row_kernel<true>, dim3(M), dim3(512), 0, s, (const half_t *)x, (int64_t)D,
-                       (const half_t *)w, D, eps, (half_t *)y, y_lay, part, S, (half_t *)x);
+    if (S == 2)
+        hipLaunchKernelGGL(rmsnorm_row_kernel<2>, dim3(M), dim3(512), 0, s, (const half_t *)x, (int64_t)D,
+                           (const half_t *)w, D, eps, (half_t *)y, y_lay, part, (half_t *)x);
+    else if (S == 4)
+        hipLaunchKernelGGL(rmsnorm_row_kernel<4>, dim3(M), dim3(512), 0, s, (const half_t *)x, (int64_t)D,
+                           (const half_t *)w, D, eps, (half_t *)y, y_lay, part, (half_t *)x);
+    else
+        return hipErrorInvalidValue;  // the products split K in two or four
     return hipGetLastError();
 }
