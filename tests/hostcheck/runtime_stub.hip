@@ -62,12 +62,15 @@ hipError_t launch_embed(const void *, const int32_t *, int64_t, int, int, const 
 hipError_t launch_gather_rows(const void *, const int *, int, int, int, void *, hipStream_t) { return hipSuccess; }
 hipError_t launch_rmsnorm(const void *, int64_t, const void *, int, int, float, int, void *, hipStream_t, int) { return hipSuccess; }
 // the partial sums and the rows the residual form reads and writes
+static int g_resid_norms = 0;  // normalisations that added handed-over partials
 hipError_t launch_rmsnorm_resid(const float *part, int S, void *x, const void *, int M, int D, float, void *, hipStream_t, int)
 {
     CHECK(part, (size_t)S * M * D * sizeof(float));
     CHECK(x, (size_t)M * D * 2);
+    g_resid_norms++;
     return hipSuccess;
 }
+int hostcheck_resid_norms() { return g_resid_norms; }
 
 // the cache addresses the KV write of rows (b, pos) touches
 static int g_es = 2;
@@ -104,7 +107,21 @@ static void check_qkv_ep(const GemmArgs &a)
         check_kv(ep.kcache, ep.vcache, ep.pg, ep.S, ep.Hkv, ep.hd, b, pos);
     }
 }
-hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t) { g_es = 2; check_qkv_ep(a); return hipSuccess; }
+hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t)
+{
+    g_es = 2;
+    check_qkv_ep(a);
+    if (a.pending) {
+        // as a split-K form would: residual products of fragment-major rows
+        // leave four partial planes for the next normalisation launch
+        *a.pending = 0;
+        if (a.ep.kind == EP_RESID && a.ep.part && (a.x_lay == 1 || a.x_lay == 2)) {
+            CHECK(a.ep.part, (size_t)4 * a.M * a.N * sizeof(float));
+            *a.pending = 4;
+        }
+    }
+    return hipSuccess;
+}
 hipError_t launch_linear_f32(const GemmArgs &a, hipStream_t) { g_es = 4; check_qkv_ep(a); return hipSuccess; }
 
 static void check_attn(const AttnArgs &a, int es)
