@@ -48,10 +48,15 @@ _lib = None
 
 
 def lib():
+    """The loaded oracle library.  ORACLE_LIB names another build of
+    oracle.c to load instead (the planted-mistake tests use it)."""
     global _lib
     if _lib is None:
-        build()
-        L = C.CDLL(_LIB)
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            build()
+            path = _LIB
+        L = C.CDLL(path)
         P = C.POINTER
         vp = C.c_void_p
         sig = {
@@ -74,6 +79,9 @@ def lib():
             "orc_model_weights": (C.c_int, [vp, C.c_int32, C.c_uint64, C.c_uint64, vp]),
             "orc_forward_stream": (C.c_int, [P(Params), C.c_uint64, C.c_int32, vp, C.c_int32,
                                              C.c_int32, C.c_int32, vp]),
+            "orc_model_forward_resid": (C.c_int, [vp, vp, C.c_int32, C.c_int32, C.c_int32, vp, vp]),
+            "orc_forward_stream_resid": (C.c_int, [P(Params), C.c_uint64, C.c_int32, vp, C.c_int32,
+                                                   C.c_int32, C.c_int32, vp, vp]),
             "orc_argmax": (C.c_int32, [vp, C.c_int32]),
             "orc_softmax_temp": (None, [vp, C.c_int32, C.c_float, vp]),
             "orc_top_p": (C.c_int32, [vp, C.c_int32, C.c_float, C.c_float, P(C.c_int32)]),
@@ -273,16 +281,21 @@ class Model:
         if not self._h:
             raise MemoryError("oracle model allocation failed")
 
-    def forward(self, tokens, start_pos: int) -> np.ndarray:
+    def forward(self, tokens, start_pos: int, resid: bool = False):
         """tokens[B][T] at positions start_pos.. -> fp32 logits[B][V] of the
-        last position of each row; the KV cache is updated."""
+        last position of each row; the KV cache is updated.  With resid the
+        residual stream at every layer boundary is returned too, shaped
+        [n_layers + 1][B][T][dim] (entry 0 the embedding rows, entry l + 1
+        the output of layer l): (logits, resid)."""
         t = np.ascontiguousarray(tokens, dtype=np.int32)
         B, T = t.shape
         out = np.empty((B, self.cfg.vocab_size), np.float32)
-        rc = lib().orc_model_forward(self._h, _ptr(t), B, T, start_pos, _ptr(out))
+        r = np.empty((self.cfg.n_layers + 1, B, T, self.cfg.dim), np.float32) if resid else None
+        rc = lib().orc_model_forward_resid(self._h, _ptr(t), B, T, start_pos, _ptr(out),
+                                           None if r is None else _ptr(r))
         if rc != 0:
             raise ValueError("oracle forward rejected its arguments")
-        return out
+        return (out, r) if resid else out
 
     def weights(self, tensor_id: int, first: int, count: int) -> np.ndarray:
         out = np.empty(count, dtype=np.uint16 if self.cfg.dtype == F16 else np.float32)
@@ -304,14 +317,19 @@ class Model:
         self.close()
 
 
-def forward_stream(cfg: Cfg, seed: int, tokens, first_pos: int, acc64: bool = False) -> np.ndarray:
+def forward_stream(cfg: Cfg, seed: int, tokens, first_pos: int, acc64: bool = False,
+                   resid: bool = False):
     """Layer-major forward of whole sequences tokens[B][N]; returns the fp32
-    logits of positions first_pos..N-1, shaped [B][N-first_pos][V]."""
+    logits of positions first_pos..N-1, shaped [B][N-first_pos][V].  With
+    resid also the residual stream at every layer boundary, shaped
+    [n_layers + 1][B][N][dim]: (logits, resid)."""
     t = np.ascontiguousarray(tokens, dtype=np.int32)
     B, N = t.shape
     out = np.empty((B, N - first_pos, cfg.vocab_size), np.float32)
+    r = np.empty((cfg.n_layers + 1, B, N, cfg.dim), np.float32) if resid else None
     p = cfg.params()
-    rc = lib().orc_forward_stream(C.byref(p), seed, int(acc64), _ptr(t), B, N, first_pos, _ptr(out))
+    rc = lib().orc_forward_stream_resid(C.byref(p), seed, int(acc64), _ptr(t), B, N, first_pos,
+                                        _ptr(out), None if r is None else _ptr(r))
     if rc != 0:
         raise ValueError("oracle stream forward rejected its arguments")
-    return out
+    return (out, r) if resid else out

@@ -192,10 +192,9 @@ void orc_rope_table(int32_t head_dim, int32_t n_pos, float base, float *cos_t, f
 }
 
 /* ------------------------------------------------------------------------ */
-/* Dot product with fp32 (or fp64) accumulation.  The order of the sum is    */
-/* not fixed by the pages; this one keeps eight running partial sums (terms  */
-/* k, k+8, k+16, ... in partial k mod 8) added together at the end, a fixed  */
-/* order that lets the compiler use vector lanes without -ffast-math.        */
+/* Dot product with fp32 (or fp64) accumulation: the plain sum of the        */
+/* products in index order, one rounding per addition.  The pages fix no     */
+/* summation order, so the oracle takes the definition as written.           */
 /* ------------------------------------------------------------------------ */
 static float dot_f32(const float *a, const float *b, int n, int acc64)
 {
@@ -204,12 +203,9 @@ static float dot_f32(const float *a, const float *b, int n, int acc64)
         for (int k = 0; k < n; k++) s += (double)a[k] * (double)b[k];
         return (float)s;
     }
-    float p[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int k = 0;
-    for (; k + 8 <= n; k += 8)
-        for (int j = 0; j < 8; j++) p[j] += a[k + j] * b[k + j];
-    for (; k < n; k++) p[k & 7] += a[k] * b[k];
-    return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    float s = 0.0f;
+    for (int k = 0; k < n; k++) s += a[k] * b[k];
+    return s;
 }
 
 /* A weight matrix W[rows][cols] (logical out x in, row-major). */
@@ -517,9 +513,13 @@ void orc_model_destroy(orc_model *m)
 /* Transformer.forward(tokens, start_pos) (P1 sections 2 and 3.8): B rows of
  * T tokens at positions start_pos..start_pos+T-1, KV cache updated, and the
  * fp32 logits of the last position of each row written to logits[B][V].
- * With T=1 this is a decode step (P2 section 3).  Returns 0 or -1. */
-int orc_model_forward(orc_model *m, const int32_t *tokens, int32_t B, int32_t T,
-                      int32_t start_pos, float *logits)
+ * With T=1 this is a decode step (P2 section 3).  When resid is not NULL it
+ * receives the residual stream at every layer boundary, resid[l][B*T][D]
+ * for l = 0..NL: entry 0 is the embedding rows, entry l + 1 the output of
+ * layer l (the input of the next TransformerBlock, P1 section 3.7).
+ * Returns 0 or -1. */
+int orc_model_forward_resid(orc_model *m, const int32_t *tokens, int32_t B, int32_t T,
+                            int32_t start_pos, float *logits, float *resid)
 {
     orc_dims *d = &m->d;
     if (B < 1 || B > m->p.max_batch_size || T < 1 || start_pos < 0 || start_pos + T > d->S) return -1;
@@ -528,15 +528,24 @@ int orc_model_forward(orc_model *m, const int32_t *tokens, int32_t B, int32_t T,
     float *x = (float *)malloc(sizeof(float) * M * d->D);
     float *last = (float *)malloc(sizeof(float) * (size_t)B * d->D);
     embed(&m->emb, tokens, (int)M, x);
+    if (resid) memcpy(resid, x, sizeof(float) * M * d->D);
     size_t per_layer = (size_t)m->p.max_batch_size * d->S * d->Hkv * d->hd;
-    for (int l = 0; l < d->NL; l++)
+    for (int l = 0; l < d->NL; l++) {
         layer_forward(&m->layers[l], d, x, B, T, start_pos, m->kc + l * per_layer,
                       m->vc + l * per_layer, m->cos_t, m->sin_t, m->acc64);
+        if (resid) memcpy(resid + (size_t)(l + 1) * M * d->D, x, sizeof(float) * M * d->D);
+    }
     for (int bb = 0; bb < B; bb++)
         memcpy(last + (size_t)bb * d->D, x + ((size_t)bb * T + T - 1) * d->D, sizeof(float) * d->D);
     head_forward(&m->out, d, last, B, logits, m->acc64);
     free(x); free(last);
     return 0;
+}
+
+int orc_model_forward(orc_model *m, const int32_t *tokens, int32_t B, int32_t T,
+                      int32_t start_pos, float *logits)
+{
+    return orc_model_forward_resid(m, tokens, B, T, start_pos, logits, NULL);
 }
 
 /* Read back stored weights of the resident model (for generator checks). */
@@ -560,9 +569,13 @@ int orc_model_weights(const orc_model *m, int32_t tid, uint64_t first, uint64_t 
 /* first_pos..N-1 of each row to logits[B][N-first_pos][V].  Because every   */
 /* query attends to keys 0..p with the same arithmetic, each position's      */
 /* logits equal those of incremental prefill + decode over the same tokens.  */
+/* When resid is not NULL it receives the residual stream at every layer     */
+/* boundary, resid[l][B][N][D] for l = 0..NL (entry 0: the embedding rows,   */
+/* entry l + 1: the output of layer l).                                      */
 /* ------------------------------------------------------------------------ */
-int orc_forward_stream(const orc_params *p, uint64_t seed, int32_t acc64, const int32_t *tokens,
-                       int32_t B, int32_t N, int32_t first_pos, float *logits)
+int orc_forward_stream_resid(const orc_params *p, uint64_t seed, int32_t acc64,
+                             const int32_t *tokens, int32_t B, int32_t N, int32_t first_pos,
+                             float *logits, float *resid)
 {
     orc_dims d;
     dims_from_params(p, &d);
@@ -581,11 +594,13 @@ int orc_forward_stream(const orc_params *p, uint64_t seed, int32_t acc64, const 
     if (tensor_alloc_gen(&t, d.V, d.D, d.dtype, seed, 0)) return -1;
     embed(&t, tokens, (int)M, x);
     tensor_free(&t);
+    if (resid) memcpy(resid, x, sizeof(float) * M * d.D);
     for (int l = 0; l < d.NL; l++) {
         orc_layer L;
         if (layer_gen(&L, &d, seed, l)) return -1;
         layer_forward(&L, &d, x, B, N, 0, kc, vc, cos_t, sin_t, acc64);
         layer_free(&L);
+        if (resid) memcpy(resid + (size_t)(l + 1) * M * d.D, x, sizeof(float) * M * d.D);
     }
     if (tensor_alloc_gen(&t, d.V, d.D, d.dtype, seed, 1)) return -1;
     int R = N - first_pos;
@@ -597,6 +612,12 @@ int orc_forward_stream(const orc_params *p, uint64_t seed, int32_t acc64, const 
     tensor_free(&t);
     free(rows); free(x); free(cos_t); free(sin_t); free(kc); free(vc);
     return 0;
+}
+
+int orc_forward_stream(const orc_params *p, uint64_t seed, int32_t acc64, const int32_t *tokens,
+                       int32_t B, int32_t N, int32_t first_pos, float *logits)
+{
+    return orc_forward_stream_resid(p, seed, acc64, tokens, B, N, first_pos, logits, NULL);
 }
 
 /* ------------------------------------------------------------------------ */
