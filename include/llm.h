@@ -308,6 +308,22 @@ int llm_op_kv_write(llm_t *h, int32_t layer, const void *k_d, const void *v_d, i
 int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_t T,
                      int32_t pos0, void *out_d);
 
+/* One TransformerBlock (walkthrough section 3.7: h = x +
+ * attention(attention_norm(x)), out = h + feed_forward(ffn_norm(h))) of
+ * layer `layer` on caller rows: x_d is [B][T][dim] in the storage type, the
+ * residual rows entering the layer for positions pos0..pos0+T-1 of batch
+ * rows 0..B-1; on return it holds the rows leaving the layer.  The kernels,
+ * launch forms and rounding are those a whole pass uses for the same rows:
+ * T == 1 with pos0 >= 1 runs the decode-step forms (attention over cached
+ * keys 0..pos0), anything else the prefill forms (causal over the T rows
+ * after the cached prefix [0, pos0)).  Writes the layer's KV cache at
+ * positions pos0..pos0+T-1; keys below pos0 must have been written before
+ * (by a pass or by earlier calls for this layer).  Leaves the handle's
+ * tokens, logits and positions as they were; overwrites the activation
+ * workspace.  For checking the forward pass one layer at a time against
+ * the oracle fed the same input.  Synchronises. */
+int llm_op_layer(llm_t *h, int32_t layer, void *x_d, int32_t B, int32_t T, int32_t pos0);
+
 /* Run `reps` decode steps at prev_pos without the captured graph, with HIP
  * events on the handle's stream around every kernel, and write the mean
  * milliseconds per step of each kernel class to ms_out[9]: 0 embedding,

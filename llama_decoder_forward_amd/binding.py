@@ -83,6 +83,7 @@ EXPORTS = {
     "llm_op_linear": (C.c_int, [_vp, C.c_int32, C.c_int32, _vp, C.c_int32, _vp]),
     "llm_op_kv_write": (C.c_int, [_vp, C.c_int32, _vp, _vp, C.c_int32, C.c_int32, C.c_int32]),
     "llm_op_attention": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32, C.c_int32, C.c_int32, _vp]),
+    "llm_op_layer": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32, C.c_int32, C.c_int32]),
     "llm_kv_block_bytes": (C.c_int64, [_P, C.c_int32]),
     "llm_create_paged": (C.c_int, [_P, _PG, C.c_uint64, _vp, C.POINTER(_vp)]),
     "llm_create_paged_dry": (C.c_int, [_P, _PG, C.POINTER(_vp)]),
@@ -294,6 +295,9 @@ class Handle:
 
     def op_attention(self, layer: int, q_ptr: int, B: int, T: int, pos0: int, out_ptr: int):
         self._ck(_lib.llm_op_attention(self.ptr, layer, C.c_void_p(q_ptr), B, T, pos0, C.c_void_p(out_ptr)))
+
+    def op_layer(self, layer: int, x_ptr: int, B: int, T: int, pos0: int):
+        self._ck(_lib.llm_op_layer(self.ptr, layer, C.c_void_p(x_ptr), B, T, pos0))
 
     def kv_num_blocks(self) -> int:
         return _lib.llm_kv_num_blocks(self.ptr)

@@ -437,6 +437,7 @@ struct Pass {
     const int *cu = nullptr, *last_rows = nullptr;
     int Tmax = 0;
     bool advance = false;  // the head's product moves *pos_dev on by one (captured decode steps)
+    bool x_given = false;  // the residual rows are already in x: layer 0 does not gather embeddings
     bool decode() const { return pos_dev || pos_rows; }
 };
 
@@ -555,7 +556,7 @@ hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused, int *pe
         const char *nw = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
         // fused, layer 0: the product gathers the embedding rows itself and
         // stores them into x (no embedding launch)
-        if (fused && l == 0) return run_linear(h, l, MAT_QKV, h->emb, d.D, M, eq, nw, ACT_ROWS, h->tok);
+        if (fused && l == 0 && !ps.x_given) return run_linear(h, l, MAT_QKV, h->emb, d.D, M, eq, nw, ACT_ROWS, h->tok);
         return fused ? run_linear(h, l, MAT_QKV, h->x, d.D, M, eq, nw)
                      : run_linear(h, l, MAT_QKV, h->xn, d.D, M, eq, nullptr, lay);
     }
@@ -587,6 +588,82 @@ hipError_t product(llm_t *h, int l, int mat, const Pass &ps, bool fused, int *pe
                      : run_linear(h, 0, MAT_HEAD, h->xn, d.D, ps.B, el, nullptr, head_layout(lay));
     }
     }
+}
+
+// State one pass carries from layer to layer: whether RMSNorm runs inside
+// the products, the activation layout, and the split count of split-K
+// partial sums the last residual product left in h->part for the next
+// normalisation launch to add to x (0: none).
+struct LayerRun {
+    bool fused = false;
+    int lay = ACT_ROWS;
+    int pend = 0;
+};
+
+// The normalisation in front of a product (non-fused forms): adds the
+// pending split-K partials to x first when the last residual product handed
+// them over, then normalises x into xn.
+hipError_t norm_launch(llm_t *h, LayerRun &lr, const void *nw, int rows)
+{
+    const Dims &d = h->d;
+    if (lr.pend) {
+        const int sp = lr.pend;
+        lr.pend = 0;
+        return launch_rmsnorm_resid(h->part, sp, h->x, nw, rows, d.D, h->p.norm_eps, h->xn, h->stream, lr.lay);
+    }
+    return launch_rmsnorm(h->x, d.D, nw, rows, d.D, h->p.norm_eps, d.dtype, h->xn, h->stream, lr.lay);
+}
+
+// TransformerBlock l (walkthrough section 3.7) of the pass ps on the residual
+// rows in x: h = x + wo(attention(RoPE(wq|wk|wv(attention_norm(x))))), then
+// out = h + w2(silu(w1 ffn_norm(h)) * w3 ffn_norm(h)).  With defer_w2 the
+// w2 product may leave split-K partials for the next normalisation launch
+// (lr.pend); wo may always do so, the ffn normalisation adds them.
+hipError_t layer_pass(llm_t *h, const Pass &ps, int l, LayerRun &lr, bool defer_w2, Prof *pf)
+{
+    const Dims &d = h->d;
+    const int M = ps.M, B = ps.B;
+    hipStream_t s = h->stream;
+    hipError_t e;
+    int *defer = lr.fused ? nullptr : &lr.pend;
+    const char *nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
+    const char *nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
+#define TRY_RAW(x)                    \
+    do {                              \
+        if ((e = (x)) != hipSuccess) \
+            return e;                 \
+    } while (0)
+#define TRYC(cls, x)                       \
+    do {                                   \
+        TRY_RAW(prof_mark(pf, (cls), s)); \
+        TRY_RAW(x);                        \
+        TRY_RAW(prof_end(pf, s));          \
+    } while (0)
+    // attention_norm -> wq|wk|wv with RoPE and the KV-cache write
+    if (!lr.fused) TRYC(PC_NORM, norm_launch(h, lr, nw_attn, M));
+    TRYC(PC_QKV, product(h, l, MAT_QKV, ps, lr.fused));
+    // attention over the cache
+    AttnArgs aa{};
+    aa.q = h->q; aa.kcache = layer_kc(h, l); aa.vcache = layer_vc(h, l); aa.out = h->o;
+    aa.B = B; aa.T = ps.rowmap ? ps.Tmax : ps.T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
+    aa.Sb = stream_len(h);
+    aa.pg = kv_pages(h);
+    aa.pos_dev = ps.pos_dev; aa.pos_imm = ps.pos0;
+    aa.pos_rows = ps.pos_rows;
+    aa.cu = ps.cu;
+    aa.out_lay = lr.lay;
+    if (d.dtype == LLM_F32) TRYC(PC_ATTN, launch_attn_f32(aa, s));
+    else if (ps.decode()) TRYC(PC_ATTN, launch_attn_decode_f16(aa, s));
+    else TRYC(PC_ATTN, launch_attn_prefill_f16(aa, s));
+    // wo + residual
+    TRYC(PC_O, product(h, l, MAT_O, ps, lr.fused, defer));
+    // ffn_norm -> w1|w3 with SwiGLU -> w2 + residual
+    if (!lr.fused) TRYC(PC_NORM, norm_launch(h, lr, nw_ffn, M));
+    TRYC(PC_W13, product(h, l, MAT_W13, ps, lr.fused));
+    TRYC(PC_W2, product(h, l, MAT_W2, ps, lr.fused, defer_w2 ? defer : nullptr));
+#undef TRYC
+#undef TRY_RAW
+    return hipSuccess;
 }
 
 // The forward pass (walkthrough sections 2, 3.5-3.8) described by ps.
@@ -635,46 +712,10 @@ hipError_t forward(llm_t *h, const Pass &ps, Prof *pf = nullptr)
     if (!fused)  // else layer 0's wq|wk|wv product gathers the embedding rows
         TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, M, ps.T, ps.pos_dev, ps.pos0, ps.pos_rows, ps.rowmap, d.D,
                                     d.dtype, h->x, s));
-    const int lay = act_layout(h, ps);
-    // split-K partial sums the last residual product left in h->part for the
-    // next normalisation launch to add to x (0: none); only where a
-    // normalisation launch follows every residual product
-    int pend = 0;
-    int *defer = fused ? nullptr : &pend;
-    auto norm = [&](const void *nw_, int rows) -> hipError_t {
-        if (pend) {
-            const int sp = pend;
-            pend = 0;
-            return launch_rmsnorm_resid(h->part, sp, h->x, nw_, rows, d.D, h->p.norm_eps, h->xn, s, lay);
-        }
-        return launch_rmsnorm(h->x, d.D, nw_, rows, d.D, h->p.norm_eps, d.dtype, h->xn, s, lay);
-    };
-    for (int l = 0; l < d.NL; l++) {
-        const char *nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
-        const char *nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
-        // attention_norm -> wq|wk|wv with RoPE and the KV-cache write
-        if (!fused) TRYC(PC_NORM, norm(nw_attn, M));
-        TRYC(PC_QKV, product(h, l, MAT_QKV, ps, fused));
-        // attention over the cache
-        AttnArgs aa{};
-        aa.q = h->q; aa.kcache = layer_kc(h, l); aa.vcache = layer_vc(h, l); aa.out = h->o;
-        aa.B = B; aa.T = ps.rowmap ? ps.Tmax : ps.T; aa.H = d.H; aa.Hkv = d.Hkv; aa.hd = d.hd; aa.S = d.S;
-        aa.Sb = stream_len(h);
-        aa.pg = kv_pages(h);
-        aa.pos_dev = ps.pos_dev; aa.pos_imm = ps.pos0;
-        aa.pos_rows = ps.pos_rows;
-        aa.cu = ps.cu;
-        aa.out_lay = lay;
-        if (d.dtype == LLM_F32) TRYC(PC_ATTN, launch_attn_f32(aa, s));
-        else if (ps.decode()) TRYC(PC_ATTN, launch_attn_decode_f16(aa, s));
-        else TRYC(PC_ATTN, launch_attn_prefill_f16(aa, s));
-        // wo + residual
-        TRYC(PC_O, product(h, l, MAT_O, ps, fused, defer));
-        // ffn_norm -> w1|w3 with SwiGLU -> w2 + residual
-        if (!fused) TRYC(PC_NORM, norm(nw_ffn, M));
-        TRYC(PC_W13, product(h, l, MAT_W13, ps, fused));
-        TRYC(PC_W2, product(h, l, MAT_W2, ps, fused, l + 1 < d.NL ? defer : nullptr));
-    }
+    LayerRun lr;
+    lr.fused = fused;
+    lr.lay = act_layout(h, ps);
+    for (int l = 0; l < d.NL; l++) TRY_RAW(layer_pass(h, ps, l, lr, l + 1 < d.NL, pf));
     // final norm on the last position of each row, output head, fp32 logits
     if (ps.rowmap) TRYC(PC_HEAD, launch_gather_rows(h->x, ps.last_rows, B, d.D, d.es, h->q, s));
     const bool fused_head = fuse_norm(h, B);
@@ -682,7 +723,7 @@ hipError_t forward(llm_t *h, const Pass &ps, Prof *pf = nullptr)
         const char *nw_final = h->norm_w + (int64_t)(2 * d.NL) * d.D * d.es;
         int64_t ld = 0;
         const char *xl = head_rows(h, ps, &ld);
-        TRYC(PC_NORM, launch_rmsnorm(xl, ld, nw_final, B, d.D, h->p.norm_eps, d.dtype, h->xn, s, head_layout(lay)));
+        TRYC(PC_NORM, launch_rmsnorm(xl, ld, nw_final, B, d.D, h->p.norm_eps, d.dtype, h->xn, s, head_layout(lr.lay)));
     }
     TRYC(PC_HEAD, product(h, 0, MAT_HEAD, ps, fused_head));
 #undef TRYC
@@ -1807,6 +1848,38 @@ int llm_op_attention(llm_t *h, int32_t layer, const void *q_d, int32_t B, int32_
     else if (T == 1) e = launch_attn_decode_f16(aa, h->stream);
     else if (pos0 == 0) e = launch_attn_prefill_f16(aa, h->stream);
     else return fail(h, LLM_EINVAL, "fp16 multi-token attention starts at position 0");
+    return op_end(h, e);
+}
+
+int llm_op_layer(llm_t *h, int32_t layer, void *x_d, int32_t B, int32_t T, int32_t pos0)
+{
+    int rc = op_begin(h);
+    if (rc) return rc;
+    const Dims &d = h->d;
+    if (!x_d || layer < 0 || layer >= d.NL || B < 1 || B > d.maxB || T < 1 || pos0 < 0 || (int64_t)pos0 + T > d.S)
+        return fail(h, LLM_EINVAL, "bad arguments");
+    if ((rc = ensure_ws(h, (int64_t)B * T))) return rc;
+    if ((rc = kv_reserve_uniform(h, B, pos0, pos0 + T, false))) return rc;
+    if ((rc = kv_upload(h))) return rc;
+    const bool decode = T == 1 && pos0 >= 1;
+    if (decode) {
+        HIPC(h, launch_set_int(h->pos_dev, pos0, h->stream));
+        h->dev_pos = pos0;
+    }
+    Pass ps = uniform_pass(B, T, decode ? h->pos_dev : nullptr, decode ? 0 : pos0);
+    ps.x_given = true;
+    const int64_t bytes = (int64_t)B * T * d.D * d.es;
+    HIPC(h, hipMemcpyAsync(h->x, x_d, bytes, hipMemcpyDeviceToDevice, h->stream));
+    LayerRun lr;
+    lr.fused = fuse_norm(h, ps.M);
+    lr.lay = act_layout(h, ps);
+    const bool next = layer + 1 < d.NL;
+    hipError_t e = layer_pass(h, ps, layer, lr, next, nullptr);
+    // w2's split-K partials are added by the normalisation that opens the
+    // next layer, as in a whole pass; its normalised rows are not used
+    if (e == hipSuccess && lr.pend)
+        e = norm_launch(h, lr, h->norm_w + (int64_t)(2 * (layer + 1)) * d.D * d.es, ps.M);
+    if (e == hipSuccess) e = hipMemcpyAsync(x_d, h->x, bytes, hipMemcpyDeviceToDevice, h->stream);
     return op_end(h, e);
 }
 

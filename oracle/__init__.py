@@ -79,6 +79,8 @@ def lib():
             "orc_model_weights": (C.c_int, [vp, C.c_int32, C.c_uint64, C.c_uint64, vp]),
             "orc_forward_stream": (C.c_int, [P(Params), C.c_uint64, C.c_int32, vp, C.c_int32,
                                              C.c_int32, C.c_int32, vp]),
+            "orc_layer_apply": (C.c_int, [P(Params), C.c_uint64, C.c_int32, C.c_int32, vp, C.c_int32,
+                                          C.c_int32]),
             "orc_model_forward_resid": (C.c_int, [vp, vp, C.c_int32, C.c_int32, C.c_int32, vp, vp]),
             "orc_forward_stream_resid": (C.c_int, [P(Params), C.c_uint64, C.c_int32, vp, C.c_int32,
                                                    C.c_int32, C.c_int32, vp, vp]),
@@ -333,3 +335,14 @@ def forward_stream(cfg: Cfg, seed: int, tokens, first_pos: int, acc64: bool = Fa
     if rc != 0:
         raise ValueError("oracle stream forward rejected its arguments")
     return (out, r) if resid else out
+
+
+def layer_apply(cfg: Cfg, seed: int, layer: int, x, acc64: bool = False) -> np.ndarray:
+    """One TransformerBlock of the seeded model on residual rows x[B][N][dim]
+    (positions 0..N-1 of each row, causal); returns the rows leaving it."""
+    y = np.array(x, dtype=np.float32, order="C", copy=True)
+    B, N, _ = y.shape
+    p = cfg.params()
+    if lib().orc_layer_apply(C.byref(p), seed, layer, int(acc64), _ptr(y), B, N) != 0:
+        raise ValueError("oracle layer_apply rejected its arguments")
+    return y

@@ -620,6 +620,31 @@ int orc_forward_stream(const orc_params *p, uint64_t seed, int32_t acc64, const 
     return orc_forward_stream_resid(p, seed, acc64, tokens, B, N, first_pos, logits, NULL);
 }
 
+/* One TransformerBlock (P1 section 3.7) of a model too large to keep       */
+/* resident, applied to caller rows: x[B][N][D] holds the residual entering  */
+/* layer `layer` at positions 0..N-1 of each row (causal over those N, P1    */
+/* section 3.8) and receives the residual leaving it.  The layer's weights   */
+/* are generated for the call and freed.  Returns 0 or -1.                   */
+int orc_layer_apply(const orc_params *p, uint64_t seed, int32_t layer, int32_t acc64, float *x,
+                    int32_t B, int32_t N)
+{
+    orc_dims d;
+    dims_from_params(p, &d);
+    if (layer < 0 || layer >= d.NL || B < 1 || N < 1 || N > d.S) return -1;
+    float *cos_t = (float *)malloc(sizeof(float) * (size_t)d.S * (d.hd / 2));
+    float *sin_t = (float *)malloc(sizeof(float) * (size_t)d.S * (d.hd / 2));
+    size_t cache = (size_t)B * d.S * d.Hkv * d.hd;
+    float *kc = (float *)calloc(cache, sizeof(float));
+    float *vc = (float *)calloc(cache, sizeof(float));
+    orc_layer L;
+    if (!cos_t || !sin_t || !kc || !vc || layer_gen(&L, &d, seed, layer)) return -1;
+    orc_rope_table(d.hd, d.S, p->rope_theta, cos_t, sin_t);
+    layer_forward(&L, &d, x, B, N, 0, kc, vc, cos_t, sin_t, acc64);
+    layer_free(&L);
+    free(cos_t); free(sin_t); free(kc); free(vc);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Sampling (P1 section 4.2 / 4.3, P2 section 4)                            */
 /* ------------------------------------------------------------------------ */

@@ -292,15 +292,39 @@ def test_13b_shape_one_layer_long_prefill(B):
     check_logits(got[rows], want)
 
 
+@pytest.mark.timeout(1200)
+def test_13b_full_depth_vs_oracle(B):
+    """All 40 layers of the 13B model at the workload's 8 rows (copies of two
+    token rows, so the decode products run their 8-row forms), an 8-token
+    prompt and 3 forced decode steps, against the oracle at the stated
+    tolerance (5e-2 / cosine 0.9999)."""
+    w = configs.L13B_BS8
+    kw = w.model_kwargs(max_seq_len=64)
+    base = synth.tokens(w.token_seed + 5, 2, 11, w.vocab_size)
+    toks = base[np.arange(w.batch) % 2]
+    say("13B full depth, 8 rows: gpu")
+    h = B.llm_create(B.make_params(**kw), w.weight_seed)
+    got = forced(h, toks, 8, 3)
+    h.destroy()
+    for b in range(w.batch):
+        assert np.array_equal(got[b], got[b % 2])
+    say("13B full depth: oracle rows 0, 1")
+    want = oracle.forward_stream(oracle.Cfg(**dict(kw, max_batch_size=2)), w.weight_seed, base, 7)
+    check_logits(got[:2], want)
+
+
 @pytest.mark.timeout(900)
 def test_70b_full_depth_vs_oracle(B):
     """All 80 layers of the 70B model, one row, a 4-token prompt and 2 forced
-    decode steps.  At this depth the fp16 rounding points amplify any change
-    of fp32 summation order: the oracle's own fp32 and fp64-accumulation modes
-    differ by about 0.11 in the logits (cosine 0.9999), more than the 5e-2
-    budget.  The bound is therefore the larger of the stated tolerance and
-    1.25 x the oracle's own fp32 / fp64 spread on the same inputs, measured
-    here."""
+    decode steps.  The stated tolerance (5e-2 / cosine 0.9999) is NOT met at
+    this depth and this test does not claim it: the fp16 rounding points
+    amplify any change of fp32 summation order over 80 layers, and the
+    oracle's own fp32 and fp64-accumulation modes differ by about 0.11
+    (cosine 0.9999) on the same inputs.  The assertion is a departure from
+    the stated tolerance: the GPU must stay within 1.25 x that spread, i.e.
+    as close to the oracle as the oracle is to itself.  The layer-by-layer
+    check (test_per_layer_70b_full_depth) is what shows that no layer adds
+    more than its rounding noise."""
     w = configs.L70B_BS32
     kw = w.model_kwargs(max_batch_size=1, max_seq_len=64)
     toks = synth.tokens(w.token_seed, 1, 6, w.vocab_size)
@@ -317,7 +341,9 @@ def test_70b_full_depth_vs_oracle(B):
     cos_spread = cosine(o32.reshape(-1, o32.shape[-1]), o64.reshape(-1, o64.shape[-1])).min()
     d = np.abs(got - o32).max()
     cos = cosine(got.reshape(-1, got.shape[-1]), o32.reshape(-1, o32.shape[-1])).min()
-    say(f"  gpu-oracle max|d|={d:.4f} cos={cos:.7f}; oracle fp32-fp64 spread {spread:.4f} cos {cos_spread:.7f}")
+    met = d <= LOGIT_TOL and cos >= COS_TOL
+    say(f"  gpu-oracle max|d|={d:.4f} cos={cos:.7f}; oracle fp32-fp64 spread {spread:.4f} cos {cos_spread:.7f}; "
+        f"stated tolerance 5e-2 / 0.9999 {'met' if met else 'MISSED'}")
     assert d <= max(LOGIT_TOL, 1.25 * spread)
     assert cos >= min(COS_TOL, 1 - 1.25 * (1 - cos_spread))
 
