@@ -110,22 +110,43 @@ __device__ float block_sumf(float v, float *red)
     return r;
 }
 
+__device__ double block_sumd(double v, double *red)
+{
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    double r = 0.0;
+    for (int k = 0; k < (int)(blockDim.x >> 6); k++) r += red[k];
+    return r;
+}
+
+// One term of the temperature softmax: exp of the max-subtracted scaled
+// logit d (fp32), evaluated in double and rounded once to fp32, so that it is
+// the correctly rounded value (up to a double-rounding tie) on any machine.
+__device__ __forceinline__ float softmax_term(float d) { return (float)exp((double)d); }
+
 __global__ __launch_bounds__(kSampThreads) void softmax_temp_kernel(const float *logits, int V,
                                                                     float temperature, float *probs)
 {
     __shared__ float red[kSampThreads / 64];
+    __shared__ double redd[kSampThreads / 64];
     const float *row = logits + (int64_t)blockIdx.x * V;
     float *pr = probs + (int64_t)blockIdx.x * V;
     float mx = -INFINITY;
     for (int i = threadIdx.x; i < V; i += blockDim.x) mx = fmaxf(mx, row[i] / temperature);
     mx = block_max(mx, red);
-    float s = 0.f;
+    // the normaliser: the exact sum of the fp32 terms (accumulated in
+    // double, whose error over V terms is far below one fp32 step), rounded
+    // once to fp32
+    double sd = 0.0;
     for (int i = threadIdx.x; i < V; i += blockDim.x) {
-        float e = expf(row[i] / temperature - mx);
+        const float e = softmax_term(row[i] / temperature - mx);
         pr[i] = e;
-        s += e;
+        sd += (double)e;
     }
-    s = block_sumf(s, red);
+    const float s = (float)block_sumd(sd, redd);
     for (int i = threadIdx.x; i < V; i += blockDim.x) pr[i] = pr[i] / s;
 }
 
@@ -254,8 +275,10 @@ __global__ __launch_bounds__(kSampThreads) void top_p_kernel(const float *probs,
 // ---------------------------------------------------------------------------
 // Top-p for vocabularies of up to TP_MAXV tokens: one work-group per row with
 // the row's probability patterns resident in LDS (computed there from the
-// logits when the temperature softmax is fused in, with the same arithmetic
-// as softmax_temp_kernel).  Same definition and result as top_p_kernel; the
+// logits when the temperature softmax is fused in, with the arithmetic of
+// softmax_temp_kernel: divisions by t and by the normaliser, terms and
+// normaliser rounded once from double, so the probabilities do not depend
+// on the order of the sum).  Same definition and result as top_p_kernel; the
 // radix select runs in three passes over 11, 10 and 10 bits of the pattern
 // (bit 31 is zero for P >= 0), fine enough that few tokens share a bucket,
 // and the bucket scans are block-parallel instead of one thread's loop.
@@ -281,6 +304,7 @@ struct TpShared {
     uint64_t hsum[TP_NB];
     uint32_t wcnt[kSampThreads / 64];
     float wf[kSampThreads / 64];
+    double wd[kSampThreads / 64];
     SelectResult res;
     int found;
 };
@@ -366,34 +390,32 @@ __global__ __launch_bounds__(kSampThreads) void top_p_lds_kernel(const float *sr
     const int b = blockIdx.x;
     const float *row = src + (int64_t)b * V;
     if (from_logits) {
-        // P = softmax(logits * (1/t)) in fp32 with the maximum subtracted; the
-        // scaling and the normalisation multiply by correctly rounded
-        // reciprocals (a division per token made this VALU-bound)
-        const float invt = 1.0f / temperature;
+        // P = softmax(logits / t) in fp32 with the maximum subtracted, the
+        // scaling and the normalisation as divisions (as softmax_temp_kernel)
         const float4 *r4 = reinterpret_cast<const float4 *>(row);
         float mx = -INFINITY;
         for (int i = threadIdx.x; i < V / 4; i += blockDim.x) {
             const float4 v = r4[i];
-            mx = fmaxf(mx, fmaxf(fmaxf(v.x * invt, v.y * invt), fmaxf(v.z * invt, v.w * invt)));
+            mx = fmaxf(mx, fmaxf(fmaxf(v.x / temperature, v.y / temperature),
+                                 fmaxf(v.z / temperature, v.w / temperature)));
         }
         mx = block_max(mx, sh.wf);
-        float s = 0.f;
+        double sd = 0.0;
         uint4 *k4 = reinterpret_cast<uint4 *>(keys);
         for (int i = threadIdx.x; i < V / 4; i += blockDim.x) {
             const float4 v = r4[i];
-            const float e0 = expf(v.x * invt - mx), e1 = expf(v.y * invt - mx);
-            const float e2 = expf(v.z * invt - mx), e3 = expf(v.w * invt - mx);
+            const float e0 = softmax_term(v.x / temperature - mx), e1 = softmax_term(v.y / temperature - mx);
+            const float e2 = softmax_term(v.z / temperature - mx), e3 = softmax_term(v.w / temperature - mx);
             k4[i] = make_uint4(__float_as_uint(e0), __float_as_uint(e1), __float_as_uint(e2), __float_as_uint(e3));
-            s += (e0 + e1) + (e2 + e3);
+            sd += ((double)e0 + (double)e1) + ((double)e2 + (double)e3);
         }
-        s = block_sumf(s, sh.wf);
-        const float invs = 1.0f / s;
+        const float s = (float)block_sumd(sd, sh.wd);
         for (int i = threadIdx.x; i < V / 4; i += blockDim.x) {
             uint4 k = k4[i];
-            k.x = __float_as_uint(__uint_as_float(k.x) * invs) & 0x7fffffffu;
-            k.y = __float_as_uint(__uint_as_float(k.y) * invs) & 0x7fffffffu;
-            k.z = __float_as_uint(__uint_as_float(k.z) * invs) & 0x7fffffffu;
-            k.w = __float_as_uint(__uint_as_float(k.w) * invs) & 0x7fffffffu;
+            k.x = __float_as_uint(__uint_as_float(k.x) / s) & 0x7fffffffu;
+            k.y = __float_as_uint(__uint_as_float(k.y) / s) & 0x7fffffffu;
+            k.z = __float_as_uint(__uint_as_float(k.z) / s) & 0x7fffffffu;
+            k.w = __float_as_uint(__uint_as_float(k.w) / s) & 0x7fffffffu;
             k4[i] = k;
         }
     } else {

@@ -659,7 +659,15 @@ int32_t orc_argmax(const float *logits, int32_t V)
 }
 
 /* Temperature softmax in fp32: P_i = exp(z_i/t - max) / sum (P2 section 4,
- * formula for p_i(T); maximum subtracted per P4 section 5.4). */
+ * formula for p_i(T); P1 section 4.2 divides the logits by t; maximum
+ * subtracted per P4 section 5.4).  The pages fix neither the exp routine nor
+ * the order of the normaliser's sum, and either changes the last bits of P
+ * and so, at the nucleus edge, the drawn token.  The oracle therefore takes
+ * each term and the normaliser as their correctly rounded fp32 values: the
+ * exp of the fp32 argument evaluated in double and rounded once, and the sum
+ * of the fp32 terms accumulated in double (relative error below V 2^-53,
+ * under 2^-31 for V <= 2^22, far below one fp32 step) and rounded once.
+ * z_i/t and P_i = e_i/s are fp32 divisions. */
 void orc_softmax_temp(const float *logits, int32_t V, float temperature, float *probs)
 {
     float mx = -INFINITY;
@@ -667,8 +675,12 @@ void orc_softmax_temp(const float *logits, int32_t V, float temperature, float *
         probs[i] = logits[i] / temperature;
         if (probs[i] > mx) mx = probs[i];
     }
-    float s = 0.0f;
-    for (int i = 0; i < V; i++) { probs[i] = expf(probs[i] - mx); s += probs[i]; }
+    double sd = 0.0;
+    for (int i = 0; i < V; i++) {
+        probs[i] = (float)exp((double)(probs[i] - mx));
+        sd += (double)probs[i];
+    }
+    float s = (float)sd;
     for (int i = 0; i < V; i++) probs[i] = probs[i] / s;
 }
 

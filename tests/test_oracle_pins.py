@@ -264,6 +264,26 @@ def test_softmax_temperature():
     assert p[oracle.argmax(lg)] > 0.999
 
 
+def test_softmax_temperature_order_independent():
+    """The probabilities do not depend on the order of the vocabulary:
+    permuting the logits permutes P bit for bit (each term and the
+    normaliser are correctly rounded fp32 values, so no summation order shows
+    through), and every P_i is within three fp32 roundings (term, normaliser,
+    quotient) of the float64 softmax of the max-subtracted fp32 scaled
+    logits."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(8)
+    lg = (rng.standard_normal(32000) * 1.8).astype(np.float32)
+    for t in [0.6, 0.95]:
+        p = oracle.softmax_temp(lg, t)
+        for s in range(3):
+            perm = np.random.default_rng(s).permutation(lg.size)
+            assert np.array_equal(oracle.softmax_temp(lg[perm], t), p[perm])
+        z = (lg / np.float32(t)).astype(np.float32)
+        ref = softmax((z - z.max()).astype(np.float32).astype(np.float64))
+        assert np.all(np.abs(p - ref) <= 3 * np.spacing(ref.astype(np.float32)))
+
+
 def _brute_nucleus(P, top_p, u):
     """Top-p without sorting, from the definition: E_i is the integer mass of
     every token ranked above i (higher probability, or equal probability and
