@@ -106,6 +106,8 @@ int llm_create(const llm_params *p, uint64_t seed, void *hip_stream, llm_t **out
 int llm_create_dry(const llm_params *p, llm_t **out);
 
 void llm_destroy(llm_t *h);
+/* The handle's last error message; with h == NULL the calling thread's last
+ * message from a handle-free call (llm_sample_logits_static). */
 const char *llm_last_error(const llm_t *h);
 /* The hipStream_t all of the handle's work is ordered on (owned by the
  * handle unless one was passed to llm_create); NULL for a dry handle. */
@@ -262,6 +264,22 @@ int llm_get_logits_d(llm_t *h, float *out_d);
 /* Copy the token buffer rows [0, B) columns [0, n_cols) into host memory as
  * int32[B][n_cols] (syncs). */
 int llm_get_tokens(llm_t *h, int32_t n_cols, int32_t *out);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the draw of
+ * llm_sample_d on caller logits, with no handle and no allocation.
+ * logits_d[B][V] (fp32), uniforms_d[B] and out_d[B] are device pointers
+ * owned by the caller; the work is queued on hip_stream (NULL: the default
+ * stream) and the call does not synchronise.  temperature <= 0 is greedy
+ * argmax; otherwise the temperature softmax and exact top-p of llm_sample.
+ * Vocabularies above 32768 (or not a multiple of 4) stage the probabilities
+ * in a static device buffer of 4194304 floats (16 MiB, one per GPU, held
+ * until the process ends): B * V beyond that is LLM_EINVAL.  Calls that
+ * overlap on one GPU share that buffer and race.  Returns LLM_OK, LLM_EINVAL
+ * (arguments; nothing queued) or LLM_EDEVICE (a failed launch);
+ * llm_last_error(NULL) gives the calling thread's last message. */
+int llm_sample_logits_static(const float *logits_d, int32_t B, int32_t V, float temperature,
+                             float top_p, const float *uniforms_d, int32_t *out_d, void *hip_stream);
 
 /* Top-p draw on caller-supplied probabilities probs[B][vocab] (host, fp32)
  * with the exact rule of llm_sample; out[B] receives the token ids (syncs).

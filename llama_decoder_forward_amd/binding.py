@@ -84,6 +84,7 @@ EXPORTS = {
     "llm_op_kv_write": (C.c_int, [_vp, C.c_int32, _vp, _vp, C.c_int32, C.c_int32, C.c_int32]),
     "llm_op_attention": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32, C.c_int32, C.c_int32, _vp]),
     "llm_op_layer": (C.c_int, [_vp, C.c_int32, _vp, C.c_int32, C.c_int32, C.c_int32]),
+    "llm_sample_logits_static": (C.c_int, [_vp, C.c_int32, C.c_int32, C.c_float, C.c_float, _vp, _vp, _vp]),
     "llm_kv_block_bytes": (C.c_int64, [_P, C.c_int32]),
     "llm_create_paged": (C.c_int, [_P, _PG, C.c_uint64, _vp, C.POINTER(_vp)]),
     "llm_create_paged_dry": (C.c_int, [_P, _PG, C.POINTER(_vp)]),
@@ -334,6 +335,17 @@ class Handle:
             self.destroy()
         except Exception:
             pass
+
+
+def llm_sample_logits_static(logits_ptr: int, B: int, V: int, temperature: float, top_p: float,
+                             uniforms_ptr: int, out_ptr: int, hip_stream: int | None = None) -> None:
+    """Handle-free, allocation-free sampling on device buffers (asynchronous)."""
+    rc = _lib.llm_sample_logits_static(C.c_void_p(logits_ptr), B, V, temperature, top_p,
+                                       C.c_void_p(uniforms_ptr) if uniforms_ptr else None,
+                                       C.c_void_p(out_ptr), C.c_void_p(hip_stream) if hip_stream else None)
+    if rc != LLM_OK:
+        msg = _lib.llm_last_error(None)
+        raise LlmError(rc, msg.decode() if msg else "error")
 
 
 def llm_create(params: llm_params, seed: int, hip_stream: int | None = None) -> Handle:

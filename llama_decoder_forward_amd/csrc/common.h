@@ -306,6 +306,8 @@ hipError_t launch_top_p(const float *probs, int B, int V, float top_p, const flo
 hipError_t launch_sample_top_p(const float *src, bool from_logits, float temperature, int B, int V, float top_p,
                                const float *uniforms, int32_t *tok, int64_t tok_ld, int write_col,
                                const int *col_rows, int32_t *out, float *probs_scratch, hipStream_t s);
+// Message of the last failed handle-free call on this thread ("" if none).
+const char *static_call_error();
 hipError_t launch_set_int(int *dst, int v, hipStream_t s);
 // dst[i] += 1 for i < n
 hipError_t launch_inc_ints(int *dst, int n, hipStream_t s);

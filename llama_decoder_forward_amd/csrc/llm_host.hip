@@ -1265,7 +1265,7 @@ void llm_destroy(llm_t *h)
     delete h;
 }
 
-const char *llm_last_error(const llm_t *h) { return h ? h->err.c_str() : "null handle"; }
+const char *llm_last_error(const llm_t *h) { return h ? h->err.c_str() : static_call_error(); }
 
 void *llm_get_stream(llm_t *h) { return h ? (void *)h->stream : nullptr; }
 

@@ -15,6 +15,11 @@
 // value.  Tokens of equal P occupy consecutive ranks in id order, each with
 // the same Q, so the rank inside a tie group is an integer division, and the
 // id is found by a counting pass in id order.
+#include <cmath>
+#include <mutex>
+#include <string>
+
+#include "../../include/llm.h"
 #include "common.h"
 
 namespace {
@@ -594,4 +599,81 @@ hipError_t launch_set_tokens(int32_t *tok, int64_t tok_ld, int B, int col, const
     hipLaunchKernelGGL(set_tokens_kernel, dim3((B + 63) / 64), dim3(64), 0, s, tok, tok_ld, B, col,
                        vals, mask);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Sampling without allocation, for callers that cannot allocate device
+// memory.  The probability rows of the two-launch path live in a file-scope
+// device array instead of a handle's buffer.  Host code never uses the
+// array's name as an address: the address is looked up once per device with
+// hipGetSymbolAddress and passed to the kernels.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kStaticProbFloats = (int64_t)1 << 22;  // 16 MiB: B * V floats
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) float scratch[kStaticProbFloats];
+
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (NULL on error).
+float *static_scratch(hipError_t *err)
+{
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = (float *)ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+static thread_local std::string g_static_err;
+
+static int static_fail(int code, const char *msg)
+{
+    g_static_err = msg;
+    return code;
+}
+
+const char *static_call_error() { return g_static_err.c_str(); }
+
+extern "C" int llm_sample_logits_static(const float *logits_d, int32_t B, int32_t V, float temperature,
+                                        float top_p, const float *uniforms_d, int32_t *out_d,
+                                        void *hip_stream)
+{
+    g_static_err.clear();
+    if (!logits_d || !out_d) return static_fail(LLM_EINVAL, "logits and out must not be NULL");
+    if (B < 1 || V < 2 || V > (1 << 22)) return static_fail(LLM_EINVAL, "need B >= 1 and 2 <= V <= 2^22");
+    if (!std::isfinite(temperature)) return static_fail(LLM_EINVAL, "temperature must be finite");
+    hipStream_t s = (hipStream_t)hip_stream;
+    hipError_t e;
+    if (temperature <= 0.f) {
+        e = launch_argmax(logits_d, B, V, nullptr, 0, -1, nullptr, out_d, s);
+        return e == hipSuccess ? LLM_OK : static_fail(LLM_EDEVICE, hipGetErrorString(e));
+    }
+    if (!(top_p > 0.f && top_p <= 1.f)) return static_fail(LLM_EINVAL, "top_p must be in (0, 1]");
+    if (!uniforms_d) return static_fail(LLM_EINVAL, "uniforms are required when temperature > 0");
+    float *probs = nullptr;
+    if (!(V <= TP_MAXV && V % 4 == 0)) {  // the two-launch path stages B x V probabilities
+        if ((int64_t)B * V > kStaticProbFloats)
+            return static_fail(LLM_EINVAL, "B * V exceeds the static probability buffer (4194304 floats)");
+        probs = static_scratch(&e);
+        if (!probs) return static_fail(LLM_EDEVICE, hipGetErrorString(e));
+    }
+    e = launch_sample_top_p(logits_d, true, temperature, B, V, top_p, uniforms_d, nullptr, 0, -1, nullptr, out_d,
+                            probs, s);
+    return e == hipSuccess ? LLM_OK : static_fail(LLM_EDEVICE, hipGetErrorString(e));
 }

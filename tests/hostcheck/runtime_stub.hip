@@ -150,6 +150,7 @@ hipError_t launch_softmax_temp(const float *, int, int, float, float *, hipStrea
 hipError_t launch_top_p(const float *, int, int, float, const float *, int32_t *, int64_t, int, const int *, int32_t *, hipStream_t) { return hipSuccess; }
 hipError_t launch_sample_top_p(const float *, bool, float, int, int, float, const float *, int32_t *, int64_t, int, const int *, int32_t *, float *, hipStream_t) { return hipSuccess; }
 hipError_t launch_set_int(int *d, int v, hipStream_t) { *d = v; return hipSuccess; }
+const char *static_call_error() { return ""; }
 hipError_t launch_inc_ints(int *d, int n, hipStream_t) { for (int i = 0; i < n; i++) d[i]++; return hipSuccess; }
 hipError_t launch_set_tokens_rows(int32_t *, int64_t, int, const int *, const int32_t *, const uint8_t *, hipStream_t) { return hipSuccess; }
 hipError_t launch_scatter_tokens(int32_t *, int64_t, int, const int2 *, const int32_t *, hipStream_t) { return hipSuccess; }
