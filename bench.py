@@ -71,32 +71,34 @@ def prefill_flops(w, B, T):
     return lin + att + head
 
 
-def cpu_baseline(w, prompt, n_steps=4):
-    """The oracle (untuned) on this host: decode cost of one layer and of the
-    head measured on 1- and 2-layer models of the workload's shape for one
-    row, scaled to the full depth and the batch."""
+def cpu_baseline(w, prompt, budget_s=15.0, max_steps=64):
+    """The oracle (untuned) on this host, end to end on the whole model of
+    the workload: one row, the prompt's prefill, then greedy decode steps
+    until about budget_s seconds of decoding have run (at least two).  The
+    value is the decode rate of that row (tok/s); rows of a batch would run
+    one after another."""
     import oracle
-    kw = w.model_kwargs(max_batch_size=1, max_seq_len=w.max_seq_len)
-    T0 = min(len(prompt), 16)
-    times = {}
-    for nl in (1, 2):
-        kw["n_layers"] = nl
-        m = oracle.Model(oracle.Cfg(**kw), w.weight_seed)
-        m.forward(np.asarray(prompt[:T0], np.int32)[None], 0)
-        t0 = time.perf_counter()
-        for i in range(n_steps):
-            m.forward(np.asarray([[prompt[i % T0]]], np.int32), T0 + i)
-        times[nl] = (time.perf_counter() - t0) / n_steps
-        m.close()
-    per_layer = max(times[2] - times[1], 1e-9)
-    head = max(times[1] - per_layer, 0.0)
-    t_token = w.n_layers * per_layer + head
-    return {"value": 1.0 / t_token, "unit": "tok/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{n_steps} decode steps of one row on 1- and 2-layer models of the "
-                      f"workload's shape after a {T0}-token prefill; per-layer and head time "
-                      f"scaled to {w.n_layers} layers; batch rows run one after another",
-            "seconds_per_token_row": t_token}
+    T0 = len(prompt)
+    kw = w.model_kwargs(max_batch_size=1, max_seq_len=min(w.max_seq_len, T0 + max_steps + 1))
+    t0 = time.perf_counter()
+    m = oracle.Model(oracle.Cfg(**kw), w.weight_seed)
+    t_create = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    lg = m.forward(np.asarray(prompt, np.int32)[None], 0)
+    t_prefill = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    n = 0
+    while n < max_steps and (n < 2 or time.perf_counter() - t0 < budget_s):
+        lg = m.forward(np.asarray([[int(lg[0].argmax())]], np.int32), T0 + n)
+        n += 1
+    t_dec = time.perf_counter() - t0
+    m.close()
+    return {"value": n / t_dec, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the whole {w.n_layers}-layer model end to end on one row: {T0}-token prefill "
+                      f"({t_prefill:.2f} s) then {n} greedy decode steps ({t_dec:.2f} s); value = decode "
+                      f"tok/s of those steps; weights generated in {t_create:.1f} s (not timed)",
+            "nproc": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "seconds_per_token_row": t_dec / n, "prefill_s": t_prefill}
 
 
 def main():
@@ -107,6 +109,9 @@ def main():
     ap.add_argument("--workload", default=configs.L7B_BS1.name,
                     choices=sorted(k for k, v in configs.WORKLOADS.items() if v.dtype == configs.F16))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--second", default=configs.L70B_BS32.name,
+                    help="a second workload measured in the same run (its decode and prefill rates go "
+                         "into detail.second_workload); 'none' to skip")
     ap.add_argument("--profile-reps", type=int, default=5)
     ap.add_argument("--kv-block", type=int, default=0,
                     help="run with a paged KV cache of blocks of this many positions (a pool with room "
@@ -137,11 +142,46 @@ def main():
         sys.exit(2)
 
     import torch
-    from llama_decoder_forward_amd import binding as Bd
-
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     w = configs.WORKLOADS[args.workload]
+    out = measure(w, args.steps, args.warmup, args.profile_reps, args.kv_block)
+    if args.second and args.second != "none" and args.second != w.name:
+        # the metric's second configuration, measured in the same run: one
+        # warm-up and one timed generate pass
+        w2 = configs.WORKLOADS[args.second]
+        o2 = measure(w2, 1, 1, 2, args.kv_block)
+        d2 = o2["detail"]
+        out["detail"]["second_workload"] = {
+            "workload": w2.name, "batch": w2.batch, "generate_tok_s": o2["value"],
+            "ms_per_generate_pass": o2["ms_per_step"],
+            "decode_tok_s_incl_sampling": d2["decode_tok_s_incl_sampling"],
+            "decode_roofline_tok_s": d2["decode_roofline_tok_s"],
+            "decode_frac_of_roofline": d2["decode_frac_of_roofline"],
+            "prefill_ms": d2["prefill_ms"], "prefill_tok_s": d2["prefill_tok_s"],
+            "prefill_tflops": d2["prefill_tflops"],
+            "prefill_frac_of_mfma": round(d2["prefill_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+            "prefill_products_tflops": d2["prefill_products_tflops"],
+            "decode_products": {k: o2["roofline"][k] for k in ("achieved", "frac", "avg_launch_us")},
+            "profile_ms_per_decode_step": d2["profile_ms_per_decode_step"],
+            "create_s": d2["create_s"],
+        }
+    if not args.no_cpu_baseline:
+        T0 = out["detail"]["prefill_rows_per_batch_row"]
+        prompt = synth.tokens(w.token_seed, 1, T0, w.vocab_size)[0]
+        out["cpu_baseline"] = cpu_baseline(w, prompt[:16].tolist())
+        if T0 > 16:
+            out["cpu_baseline"]["sample"] += f" (the first 16 of the {T0} prompt tokens)"
+    out["detail"].pop("prefill_rows_per_batch_row")
+    print(json.dumps(out), flush=True)
+
+
+def measure(w, n_steps, warmup, profile_reps, kv_block):
+    """Time n_steps whole generate passes of workload w (after warmup ones)
+    and profile its kernels; returns the bench line without cpu_baseline."""
+    import torch
+    from llama_decoder_forward_amd import binding as Bd
+
     B = w.batch
     ragged = bool(w.prompt_range)
     if ragged:
@@ -157,9 +197,9 @@ def main():
     temp, top_p = w.temperature, w.top_p
 
     t_create = time.perf_counter()
-    if args.kv_block:
-        nblk = B * -(-w.max_seq_len // args.kv_block)
-        h = Bd.llm_create_paged(Bd.params_for(w), Bd.make_paging(args.kv_block, nblk), w.weight_seed)
+    if kv_block:
+        nblk = B * -(-w.max_seq_len // kv_block)
+        h = Bd.llm_create_paged(Bd.params_for(w), Bd.make_paging(kv_block, nblk), w.weight_seed)
     else:
         h = Bd.llm_create(Bd.params_for(w), w.weight_seed)
     t_create = time.perf_counter() - t_create
@@ -190,19 +230,19 @@ def main():
             h.decode(p)
             h.sample_d(temp, top_p, uni_dev[i + 1].data_ptr() if temp > 0 else 0, 0)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         generate()
     h.sync()
     torch.cuda.synchronize()
 
     ev_start = torch.cuda.Event(enable_timing=True)
     ev_end = torch.cuda.Event(enable_timing=True)
-    ev_pf = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_st = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_pf = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
+    ev_st = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev_start.record(stream)
-    for k in range(args.steps):
+    for k in range(n_steps):
         ev_st[k].record(stream)
         generate(ev_pf[k])
     ev_end.record(stream)
@@ -210,21 +250,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev_start.elapsed_time(ev_end)
-    prefill_ms = float(np.mean([ev_st[k].elapsed_time(ev_pf[k]) for k in range(args.steps)]))
+    prefill_ms = float(np.mean([ev_st[k].elapsed_time(ev_pf[k]) for k in range(n_steps)]))
 
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / n_steps
     value = B * steps / (ms_per_step / 1e3)
     decode_ms = ms_per_step - prefill_ms
     decode_tok_s = B * steps / (decode_ms / 1e3)
 
     # live per-kernel-class timing of one decode step (HIP events on the
     # library's stream), at the last position of the generate pass
-    prof = h.profile_decode(T0 + steps - 1, args.profile_reps)
+    prof = h.profile_decode(T0 + steps - 1, profile_reps)
     # the dominant kernel, the skinny GEMV of the decode weight products:
     # the products of a decode step in forward order, replayed from a
     # captured graph between two HIP events on the library's stream (and
     # each kind on its own for the breakdown)
-    prod_us = h.profile_projections(args.profile_reps)
+    prod_us = h.profile_projections(profile_reps)
     # prefill kernels by class (eager, HIP events around every kernel); the
     # weight products' share of the prefill flops against the MFMA peak
     pf_prof = h.profile_prefill_d(tok_dev.data_ptr(), B, T0, 1)
@@ -249,8 +289,8 @@ def main():
         "value": round(value, 2),
         "unit": "tok/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": n_steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True,
         "scaling": "weak",
@@ -261,9 +301,12 @@ def main():
                    "decode_steps": steps, "temperature": temp, "top_p": top_p,
                    "layers": w.n_layers, "dim": w.dim, "heads": f"{w.n_heads}/{w.n_kv_heads}",
                    "ffn": w.ffn_hidden(), "vocab": w.vocab_size, "max_seq_len": S,
-                   "kv_cache": f"paged, blocks of {args.kv_block}" if args.kv_block else "static"},
+                   "kv_cache": f"paged, blocks of {kv_block}" if kv_block else "static"},
         "roofline": {"bound": "hbm",
                      "kernel": "gemm_skinny_kernel (decode weight products: wq|wk|wv, wo, w1|w3, w2, head)",
+                     "scope": "the weight products of a decode step only, replayed from a captured graph; "
+                              "the whole step (attention, sampling, launch gaps included) against the "
+                              "step's roofline is detail.decode_frac_of_roofline",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": round(step_prod_bytes / launches),
@@ -273,7 +316,7 @@ def main():
                                                   if k != "step_order"},
                      "bytes_per_launch_by_product": pbytes},
         "detail": {
-            "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
+            "gpu_event_ms_per_step": round(gpu_ms / n_steps, 3),
             "prefill_ms": round(prefill_ms, 3),
             "prefill_tok_s": round(prefill_tok_s, 1),
             "prefill_tflops": round(pf_flops / (prefill_ms / 1e3) / 1e12, 2),
@@ -290,12 +333,12 @@ def main():
             "create_s": round(t_create, 2),
         },
     }
+    out["detail"]["prefill_rows_per_batch_row"] = T0
     h.destroy()
     del tok_dev, uni_dev, force_tok_dev, force_mask_dev
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, prompts[0].tolist())
-    print(json.dumps(out), flush=True)
+    return out
+
 
 
 if __name__ == "__main__":

@@ -93,11 +93,7 @@ int llm_check_params(const llm_params *p);
  * Errors: LLM_EINVAL (parameters), LLM_ENOMEM, LLM_EDEVICE.  On error *out is
  * NULL.
  * Environment read at creation: LLM_NO_GRAPH=1 runs decode steps eagerly
- * instead of replaying a captured graph; LLM_FUSED_LAYER=1 runs every layer
- * of a one-row fp16 decode step as one persistent launch (grid barriers
- * between its phases; bit-identical results).  A grid barrier that does not
- * settle raises a device flag instead of hanging; llm_get_logits and
- * llm_sync then return LLM_EDEVICE. */
+ * instead of replaying a captured graph. */
 int llm_create(const llm_params *p, uint64_t seed, void *hip_stream, llm_t **out);
 
 /* A handle that validates arguments and tracks state exactly like a real
@@ -237,8 +233,9 @@ int llm_decode(llm_t *h, int32_t prev_pos);
  * the drawn token is the first kept i with E_{i+1} > floor(U * S / 2^24).
  * uniforms[B] are in [0, 1).  The token is written to tok[:, last_pos + 1]
  * when last_pos + 1 < max_seq_len and copied to out_tokens[B] when it is not
- * NULL (then the call synchronises).  top_p must lie in (0, 1], temperature
- * must be finite. */
+ * NULL (then the call synchronises; otherwise it is asynchronous: the host
+ * uniforms are staged in pinned memory before it returns).  top_p must lie
+ * in (0, 1], temperature must be finite. */
 int llm_sample(llm_t *h, float temperature, float top_p, const float *uniforms,
                int32_t *out_tokens);
 /* Same with uniforms and output in device memory; never synchronises.
@@ -254,7 +251,10 @@ int llm_set_tokens(llm_t *h, int32_t pos, const int32_t *tokens, const uint8_t *
 
 /* Same with tokens[B] and mask[B] (or NULL) in device memory; asynchronous.
  * Token ids are not range-checked on the host: the caller guarantees
- * [0, vocab). */
+ * [0, vocab).  The host cannot read a device mask, so with a mask the
+ * column counts as written for llm_decode only if it already was (the
+ * reference's forcing of some rows over a sampled column); with mask NULL
+ * it is written. */
 int llm_set_tokens_d(llm_t *h, int32_t pos, const int32_t *tokens_d, const uint8_t *mask_d);
 
 /* Copy fp32 logits[B][vocab] of the last forward into host memory (syncs). */
@@ -347,8 +347,7 @@ int llm_op_layer(llm_t *h, int32_t layer, void *x_d, int32_t B, int32_t T, int32
  * milliseconds per step of each kernel class to ms_out[9]: 0 embedding,
  * 1 RMSNorm, 2 wq|wk|wv product (with RoPE and the KV write), 3 attention,
  * 4 wo product, 5 w1|w3 product (with SwiGLU), 6 w2 product, 7 output head,
- * 8 first-to-last event (with LLM_FUSED_LAYER=1 and one row, class 2 holds
- * the whole fused layer).  Same preconditions and effects as llm_decode;
+ * 8 first-to-last event.  Same preconditions and effects as llm_decode;
  * synchronises. */
 int llm_profile_decode(llm_t *h, int32_t prev_pos, int32_t reps, float *ms_out);
 

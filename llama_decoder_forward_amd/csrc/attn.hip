@@ -52,7 +52,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
     __shared__ float sm[NW][16], sl[NW][16];
     const int bk = blockIdx.x, b = bk / Hkv, kvh = bk % Hkv;
     const int L = (pos_rows ? pos_rows[b] : (pos_dev ? *pos_dev : pos_imm)) + 1;
-    adec::attn_decode_wg<NW, PF, PAGED, false, NT>(q, kc, vc, H, Hkv, S, pg, b, kvh, L, out, out_lay, so, sm, sl);
+    adec::attn_decode_wg<NW, PF, PAGED, NT>(q, kc, vc, H, Hkv, S, pg, b, kvh, L, out, out_lay, so, sm, sl);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,6 +1,6 @@
 // Decode attention of one (batch row, KV head) pair by one work-group of NW
-// waves (walkthrough section 3.5 step 5, GQA of section 3.4): shared by the
-// stand-alone decode attention kernel and the fused one-row decode layer.
+// waves (walkthrough section 3.5 step 5, GQA of section 3.4), the body of the
+// decode attention kernel.
 //
 // The attended length L = pos + 1 is walked in 32-key steps, wave w taking
 // steps w, w+NW, ...; each wave keeps the running max / sum / unnormalised
@@ -13,10 +13,7 @@
 // and the matching V^T operand is one contiguous 16-byte load.  PF: a wave's
 // next step is loaded while the current one computes.  PAGED: each 32-key step
 // lies in one block of the row's table; the table entries the row uses are
-// held in lanes and read with readlane.  COH: q and the step holding the
-// current position are read with device-coherent loads and the output is
-// stored device-coherently (data written and read inside one kernel by work
-// groups on different XCDs).  NT: K and V are read non-temporally.  The NW
+// held in lanes and read with readlane.  NT: K and V are read non-temporally.  The NW
 // waves' states are merged in one round through LDS (fixed wave order).
 #pragma once
 #include "common.h"
@@ -41,7 +38,7 @@ __device__ __forceinline__ half8 ld_kv(const half_t *p)
 
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp(m_old - m_new) is never NaN
 
-template <int NW, bool PF, bool PAGED, bool COH, bool NT = false>
+template <int NW, bool PF, bool PAGED, bool NT = false>
 __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, const half_t *__restrict__ kc,
                                                const half_t *__restrict__ vc, int H, int Hkv, int S, const KvPages &pg,
                                                int b, int kvh, int L, half_t *__restrict__ out, int out_lay,
@@ -66,7 +63,7 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
     const half_t *qrow = q + ((int64_t)b * H + (qv ? h : 0)) * hd;
 #pragma unroll
     for (int s = 0; s < 4; s++)
-        qb[s] = qv ? (COH ? ld_coh_half8(qrow + 32 * s + 8 * g) : *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g)) : z;
+        qb[s] = qv ? *reinterpret_cast<const half8 *>(qrow + 32 * s + 8 * g) : z;
 
     // PAGED: lane j holds entries j and 64 + j of the row's block table (the
     // entries its L positions use), so a step finds its block with a lane
@@ -98,11 +95,8 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
     float mrun = kNegBig, lrun = 0.f;
 
     // all K and V operands of a step are loaded before any of its arithmetic
-    // COH: the step holding the current position (written by this kernel)
-    // is read with device-coherent loads
     auto load = [&](int st, int64_t base, half8 (&kf)[2][4], half8 (&vf)[8]) {
         const int k0 = 32 * st;
-        const bool coh = COH && st == nsteps - 1;
 #pragma unroll
         for (int t = 0; t < 2; t++) {
             const int kp = perm_key(t, r);
@@ -110,7 +104,7 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
             const half_t *krow = kc + base + (ok ? kp : 0) * hd + 8 * g;
 #pragma unroll
             for (int s = 0; s < 4; s++)
-                kf[t][s] = ok ? (coh ? ld_coh_half8(krow + 32 * s) : ld_kv<NT>(krow + 32 * s)) : z;
+                kf[t][s] = ok ? ld_kv<NT>(krow + 32 * s) : z;
         }
         const int kk = k0 + 8 * g;
         const bool vok = kk + 8 <= L;
@@ -118,11 +112,7 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) {
             const half_t *vrow = vblk + (16 * dt + r) * 32;
-            if (coh) {  // the whole 8-key chunk lies in the step's block
-                const half8 v = ld_coh_half8(vrow);
-#pragma unroll
-                for (int e = 0; e < 8; e++) vf[dt][e] = (kk + e < L) ? v[e] : (half_t)0.f;
-            } else if (vok) {
+            if (vok) {
                 vf[dt] = ld_kv<NT>(vrow);
             } else {
 #pragma unroll
@@ -222,8 +212,7 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
             for (int i = 0; i < 4; i++) hv[i] = (half_t)(o[i] * inv);
             const int c = 16 * dt + 4 * g;  // 4 consecutive columns inside one 8-column group
             half_t *orow = out + ((int64_t)b * H + h) * hd;
-            if (COH) st_coh_half4(orow + c, hv);
-            else if (out_lay) *reinterpret_cast<half4 *>(out + act_offset(b, (int64_t)h * hd + c, (int64_t)H * hd, 0, out_lay)) = hv;
+            if (out_lay) *reinterpret_cast<half4 *>(out + act_offset(b, (int64_t)h * hd + c, (int64_t)H * hd, 0, out_lay)) = hv;
             else *reinterpret_cast<half4 *>(orow + c) = hv;
         }
     }

@@ -72,34 +72,6 @@ __host__ __device__ inline int64_t v32_offset(int64_t st, int off, int d, int Sb
     return (st * hd + d) * Sb + off;
 }
 
-// Device-coherent accesses (agent scope, relaxed) for data that one work
-// group writes and work groups on other XCDs read inside the same kernel:
-// they bypass the XCDs' private L2 caches.
-typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ half8 ld_coh_half8(const half_t *p)
-{
-    const unsigned long long *u = reinterpret_cast<const unsigned long long *>(p);
-    u64x2 v;
-    v.x = __hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    v.y = __hip_atomic_load(u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __builtin_bit_cast(half8, v);
-}
-__device__ __forceinline__ half4 ld_coh_half4(const half_t *p)
-{
-    return __builtin_bit_cast(half4, __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p), __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ void st_coh_half4(half_t *p, half4 v)
-{
-    __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), __builtin_bit_cast(unsigned long long, v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coh_half(half_t *p, half_t v)
-{
-    __hip_atomic_store(reinterpret_cast<unsigned short *>(p), __builtin_bit_cast(unsigned short, v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // One 16-byte global -> LDS copy per lane (LDS address m0 + 16 * lane).  It
 // is issued from inline assembly: with the compiler's own LDS-DMA builtin in
 // the loop, its wait-count model stops trusting the in-order completion of
@@ -274,23 +246,6 @@ hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_kv_write(const void *k, const void *v, int B, int T, int pos0, int Hkv, int hd,
                            int Sb, const KvPages &pg, int dtype, void *kcache, void *vcache, hipStream_t s);
 
-// One decoder layer of a one-row decode step in one launch (decode_fused.hip).
-struct FusedLayer {
-    const void *wqkv, *wo, *w13, *w2;  // the layer's packed, tiled matrices
-    const void *nw_attn, *nw_ffn;      // RMSNorm weights
-    void *kc, *vc;                     // the layer's cache
-    KvPages pg;
-    int S;                             // positions per cache stream
-    const float *rope;
-    const int *pos;                    // the row's position (device memory)
-    void *x, *q, *o, *g;               // residual row, q, attention output, SwiGLU output
-    unsigned *bar, *bar_reset, *err;   // barrier counters (8 lines of 32 words), the next launch's, error flag
-    int D, H, Hkv, F;
-    float eps;
-};
-// Whether the fused layer fits G work-groups and the LDS.
-bool fused_layer_fits(int D, int H, int Hkv, int F, int G);
-hipError_t launch_decode_layer(const FusedLayer &f, int G, hipStream_t s);
 
 // Samplers write token column write_col of every row, or with col_rows
 // column col_rows[b] + 1 of row b (none when that reaches tok_ld).

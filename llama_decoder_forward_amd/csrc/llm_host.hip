@@ -102,6 +102,8 @@ struct llm {
     int32_t *tok = nullptr;
     float *logits = nullptr, *probs = nullptr, *uni = nullptr;
     int32_t *outtok = nullptr, *stage_i32 = nullptr;
+    float *uni_stage = nullptr;    // pinned staging of host uniforms
+    hipEvent_t uni_ev = nullptr;   // the last copy out of uni_stage
     uint8_t *stage_mask = nullptr;
     int *pos_dev = nullptr;
     int dev_pos = -1;         // what *pos_dev holds once the queued work has run (-1: unknown)
@@ -130,10 +132,6 @@ struct llm {
     hipGraphExec_t gexec_rows = nullptr;
     int graph_rows_B = -1;
     bool use_graph = true;
-    // one-row decode steps: each layer in one persistent launch (fp16)
-    bool use_fused = false;
-    int fused_G = 0;           // its work-groups: one per CU
-    unsigned *fbar = nullptr;  // barrier counters, one set of kFusedBarWords per layer, then the error flag
 };
 
 namespace {
@@ -171,8 +169,6 @@ int guard(llm_t *h)
     if (h->poisoned) return LLM_EDEVICE;
     return LLM_OK;
 }
-
-constexpr int kFusedBarWords = 8 * 32;  // eight group counters, one 128-byte line each
 
 char *layer_kc(llm_t *h, int l) { return h->kv + (int64_t)l * h->kv_layer_bytes; }
 char *layer_vc(llm_t *h, int l) { return h->kv + (int64_t)l * h->kv_layer_bytes + h->kv_layer_bytes / 2; }
@@ -686,28 +682,6 @@ hipError_t forward(llm_t *h, const Pass &ps, Prof *pf = nullptr)
         TRY_RAW(x);                        \
         TRY_RAW(prof_end(pf, s));          \
     } while (0)
-    if (h->use_fused && ps.decode() && M == 1) {
-        // one row: every layer in one launch, then the final norm and the head
-        TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, M, ps.T, ps.pos_dev, ps.pos0, ps.pos_rows, ps.rowmap, d.D,
-                                    d.dtype, h->x, s));
-        for (int l = 0; l < d.NL; l++) {
-            FusedLayer f{};
-            f.wqkv = h->wqkv[l]; f.wo = h->wo[l]; f.w13 = h->w13[l]; f.w2 = h->w2[l];
-            f.nw_attn = h->norm_w + (int64_t)(2 * l) * d.D * d.es;
-            f.nw_ffn = h->norm_w + (int64_t)(2 * l + 1) * d.D * d.es;
-            f.kc = layer_kc(h, l); f.vc = layer_vc(h, l); f.pg = kv_pages(h); f.S = stream_len(h);
-            f.rope = h->rope;
-            f.pos = ps.pos_rows ? ps.pos_rows : ps.pos_dev;
-            f.x = h->x; f.q = h->q; f.o = h->o; f.g = h->g;
-            f.bar = h->fbar + (int64_t)l * kFusedBarWords;
-            f.bar_reset = h->fbar + (int64_t)((l + 1) % d.NL) * kFusedBarWords;
-            f.err = h->fbar + (int64_t)d.NL * kFusedBarWords;
-            f.D = d.D; f.H = d.H; f.Hkv = d.Hkv; f.F = d.F; f.eps = h->p.norm_eps;
-            TRYC(PC_QKV, launch_decode_layer(f, h->fused_G, s));
-        }
-        TRYC(PC_HEAD, product(h, 0, MAT_HEAD, ps, true));
-        return hipSuccess;
-    }
     const bool fused = fuse_norm(h, M);
     if (!fused)  // else layer 0's wq|wk|wv product gathers the embedding rows
         TRYC(PC_EMBED, launch_embed(h->emb, h->tok, d.S, M, ps.T, ps.pos_dev, ps.pos0, ps.pos_rows, ps.rowmap, d.D,
@@ -834,27 +808,14 @@ int create_impl(llm_t *h, uint64_t seed)
     h->pos_rows = h->stage_i32 + d.maxB;
     h->cu = h->pos_rows + d.maxB;  // maxB + 1 starts, then maxB last rows
     h->stage_mask = (uint8_t *)(h->cu + 2 * d.maxB + 1);
+    HIPM(h, hipHostMalloc(&p, (size_t)d.maxB * sizeof(float), hipHostMallocDefault));
+    h->uni_stage = (float *)p;
+    HIPC(h, hipEventCreateWithFlags(&h->uni_ev, hipEventDisableTiming));
     int rc = ensure_ws(h, d.maxB);
     if (rc) return rc;
     rc = build_weights(h, seed);
     if (rc) return rc;
     if (h->bs && (rc = alloc_pool(h))) return rc;
-    if (d.dtype == LLM_F16 && d.NL >= 2) {
-        int dev = 0, cus = 0;
-        HIPC(h, hipGetDevice(&dev));
-        HIPC(h, hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-        // opt-in (LLM_FUSED_LAYER=1): bit-identical, but measured slower than
-        // the separate launches on the 7B one-row step (95 vs 89 us a layer)
-        const char *fl = std::getenv("LLM_FUSED_LAYER");
-        if (cus > 0 && fused_layer_fits(d.D, d.H, d.Hkv, d.F, cus) && fl && fl[0] == '1') {
-            const int64_t bytes = ((int64_t)d.NL * kFusedBarWords + 32) * sizeof(unsigned);
-            HIPM(h, hipMalloc(&p, bytes));
-            h->fbar = (unsigned *)p;
-            HIPC(h, launch_zero_bytes(h->fbar, bytes, h->stream));
-            h->fused_G = cus;
-            h->use_fused = true;
-        }
-    }
     HIPC(h, hipStreamSynchronize(h->stream));
     return LLM_OK;
 }
@@ -864,10 +825,12 @@ void release(llm_t *h)
     if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
     if (h->gexec_rows) (void)hipGraphExecDestroy(h->gexec_rows);
     void *bufs[] = {h->wts, h->emb, h->norm_w, h->kv, h->rope, h->tok, h->logits, h->probs,
-                    h->pos_dev, h->ws, h->btab_d, h->fbar};
+                    h->pos_dev, h->ws, h->btab_d};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (h->btab_stage) (void)hipHostFree(h->btab_stage);
+    if (h->uni_stage) (void)hipHostFree(h->uni_stage);
+    if (h->uni_ev) (void)hipEventDestroy(h->uni_ev);
     if (h->btab_ev) (void)hipEventDestroy(h->btab_ev);
     if (h->own_stream && h->stream) (void)hipStreamDestroy(h->stream);
 }
@@ -877,20 +840,6 @@ bool tokens_ok(const int32_t *t, int64_t n, int V)
     for (int64_t i = 0; i < n; i++)
         if (t[i] < 0 || t[i] >= V) return false;
     return true;
-}
-
-// The fused decode layer raises a flag when a grid barrier did not settle
-// (its waits are bounded, so the launch still ended).  Checked by the calls
-// that synchronise.
-int check_fused_flag(llm_t *h)
-{
-    if (!h->fbar || h->dry) return LLM_OK;
-    unsigned flag = 0;
-    HIPC(h, hipMemcpyAsync(&flag, h->fbar + (int64_t)h->d.NL * kFusedBarWords, sizeof(flag), hipMemcpyDeviceToHost,
-                           h->stream));
-    HIPC(h, hipStreamSynchronize(h->stream));
-    if (flag) return fail(h, LLM_EDEVICE, "fused decode layer: a grid barrier did not settle (results invalid)");
-    return LLM_OK;
 }
 
 int after_forward(llm_t *h, hipError_t e)
@@ -933,16 +882,23 @@ int check_prefill_args(llm_t *h, int B, int T, int start = 0)
     return LLM_OK;
 }
 
-int sample_common(llm_t *h, float temperature, float top_p, const float *uniforms_d, bool have_u,
-                  int32_t *out_d)
+int sample_check(llm_t *h, float temperature, float top_p, bool have_u)
 {
-    const Dims &d = h->d;
     if (!h->logits_valid) return fail(h, LLM_ESTATE, "no logits: run llm_prefill or llm_decode first");
     if (!std::isfinite(temperature)) return fail(h, LLM_EINVAL, "temperature must be finite");
     if (temperature > 0.f) {
         if (!(top_p > 0.f && top_p <= 1.f)) return fail(h, LLM_EINVAL, "top_p must be in (0, 1]");
         if (!have_u) return fail(h, LLM_EINVAL, "uniforms are required when temperature > 0");
     }
+    return LLM_OK;
+}
+
+int sample_common(llm_t *h, float temperature, float top_p, const float *uniforms_d, bool have_u,
+                  int32_t *out_d)
+{
+    const Dims &d = h->d;
+    int rc0 = sample_check(h, temperature, top_p, have_u);
+    if (rc0) return rc0;
     // uniform rows write column last_pos + 1; rows mode column row_last[b] + 1
     const int col = h->last_pos + 1 < d.S ? h->last_pos + 1 : -1;
     const int *col_rows = h->rows_mode ? h->pos_rows : nullptr;
@@ -1499,10 +1455,15 @@ int llm_sample(llm_t *h, float temperature, float top_p, const float *uniforms, 
     if (rc) return rc;
     if (h->dry && out_tokens) return fail(h, LLM_ESTATE, "dry handle returns no tokens");
     bool have_u = uniforms != nullptr;
-    if (!h->dry && have_u && temperature > 0.f && h->logits_valid) {
-        HIPC(h, hipMemcpyAsync(h->uni, uniforms, (size_t)h->cur_B * sizeof(float), hipMemcpyHostToDevice,
+    if ((rc = sample_check(h, temperature, top_p, have_u))) return rc;
+    if (!h->dry && have_u && temperature > 0.f) {
+        // host uniforms go through pinned staging, so the call need not wait
+        // for the copy; the previous call's copy must have read the staging
+        HIPC(h, hipEventSynchronize(h->uni_ev));
+        memcpy(h->uni_stage, uniforms, (size_t)h->cur_B * sizeof(float));
+        HIPC(h, hipMemcpyAsync(h->uni, h->uni_stage, (size_t)h->cur_B * sizeof(float), hipMemcpyHostToDevice,
                                h->stream));
-        HIPC(h, hipStreamSynchronize(h->stream));
+        HIPC(h, hipEventRecord(h->uni_ev, h->stream));
     }
     rc = sample_common(h, temperature, top_p, h->uni, have_u, out_tokens ? h->outtok : nullptr);
     if (rc) return rc;
@@ -1693,7 +1654,7 @@ int llm_get_logits(llm_t *h, float *out)
     HIPC(h, hipMemcpyAsync(out, h->logits, (size_t)h->cur_B * h->d.V * sizeof(float), hipMemcpyDeviceToHost,
                            h->stream));
     HIPC(h, hipStreamSynchronize(h->stream));
-    return check_fused_flag(h);
+    return LLM_OK;
 }
 
 int llm_get_logits_d(llm_t *h, float *out_d)
@@ -1743,7 +1704,7 @@ int llm_sync(llm_t *h)
     int rc = guard(h);
     if (rc) return rc;
     if (!h->dry) HIPC(h, hipStreamSynchronize(h->stream));
-    return check_fused_flag(h);
+    return LLM_OK;
 }
 
 int llm_read_weights(llm_t *h, int32_t tensor_id, int64_t first, int64_t count, void *out)

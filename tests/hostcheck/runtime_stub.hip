@@ -156,15 +156,3 @@ hipError_t launch_set_tokens_rows(int32_t *, int64_t, int, const int *, const in
 hipError_t launch_scatter_tokens(int32_t *, int64_t, int, const int2 *, const int32_t *, hipStream_t) { return hipSuccess; }
 hipError_t launch_set_tokens(int32_t *, int64_t, int, int, const int32_t *, const uint8_t *, hipStream_t) { return hipSuccess; }
 
-bool fused_layer_fits(int, int, int Hkv, int, int G) { return Hkv <= G; }
-hipError_t launch_decode_layer(const FusedLayer &f, int, hipStream_t)
-{
-    g_es = 2;
-    CHECK(f.pos, 4);
-    const int pos = *f.pos;
-    for (int p = 0; p <= pos; p++) check_kv(f.kc, f.vc, f.pg, f.S, f.Hkv, 128, 0, p);
-    CHECK(f.bar, 8 * 32 * 4);
-    CHECK(f.bar_reset, 8 * 32 * 4);
-    CHECK(f.err, 4);
-    return hipSuccess;
-}

@@ -33,7 +33,6 @@ def test_host_logic_under_asan(tmp_path):
                    check=True, capture_output=True)
     exe = str(tmp_path / "hostcheck")
     subprocess.run(["g++", "-no-pie", "-fsanitize=address", drv, *objs, "-o", exe], check=True, capture_output=True)
-    # LLM_FUSED_LAYER=1: one-row decode steps take the fused layer
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", LLM_FUSED_LAYER="1")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1")
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 0 and r.stdout.strip().endswith("done"), r.stdout[-3000:] + r.stderr[-3000:]
