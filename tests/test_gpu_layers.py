@@ -51,14 +51,20 @@ def f16_ulp_at(v):
     return np.spacing(np.asarray(v, np.float16)).astype(np.float64)
 
 
-def check_layer(l, got, want, want64, stats):
-    """got/want/want64: [rows][tokens][D] float32 (the oracle rows the GPU
-    rows copy).  Per (row, position): the max error against the bound."""
+def check_layer(l, got, want, want64_fn, stats):
+    """got/want: [rows][tokens][D] float32 (the oracle rows the GPU rows
+    copy).  Per (row, position): the max error against the bound; the
+    oracle's fp64 spread (want64_fn, a float64-accumulation run of the same
+    layer on the same input) is computed only where 4 fp16 steps of the row
+    maximum do not already cover the error."""
     d = np.abs(got.astype(np.float64) - want)
-    spread = np.abs(want64.astype(np.float64) - want)
     ymax = np.abs(want).max(-1)
-    bound = np.maximum(4 * f16_ulp_at(ymax), 4 * spread.max(-1))
     worst = d.max(-1)
+    bound = 4 * f16_ulp_at(ymax)
+    spread = np.zeros_like(worst)
+    if np.any(worst > bound):
+        spread = np.abs(want64_fn().astype(np.float64) - want).max(-1)
+        bound = np.maximum(bound, 4 * spread)
     cos = cosine(got.reshape(-1, got.shape[-1]), want.reshape(-1, want.shape[-1]))
     stats.append((l, float(worst.max()), float((worst / f16_ulp_at(ymax)).max()), float(spread.max()),
                   float(cos.min())))
@@ -81,13 +87,18 @@ def per_layer_parity(B, torch, w, n_layers, dec_batches, prefill_rows=256, max_s
     stats = []
     try:
         for l in range(n_layers):
-            want64 = oracle.layer_apply(cfg, w.weight_seed, l, res[l], acc64=True)
+            cache = {}
+
+            def want64(l=l, cache=cache):
+                if "y" not in cache:
+                    cache["y"] = oracle.layer_apply(cfg, w.weight_seed, l, res[l], acc64=True)
+                return cache["y"]
             # prefill form: positions 0..T0-1 of prefill_rows rows
             rows = np.arange(prefill_rows) % R
             x = torch.from_numpy(np.ascontiguousarray(res[l][rows, :T0].astype(dt))).cuda()
             h.op_layer(l, x.data_ptr(), prefill_rows, T0, 0)
             got = x.cpu().numpy().astype(np.float32)
-            check_layer(l, got[:R], res[l + 1][:, :T0], want64[:, :T0], stats)
+            check_layer(l, got[:R], res[l + 1][:, :T0], lambda: want64()[:, :T0], stats)
             assert all(np.array_equal(got[b], got[b % R]) for b in range(prefill_rows))
             # decode forms: one position at a time, for each batch size
             for p in range(T0, N):
@@ -100,14 +111,15 @@ def per_layer_parity(B, torch, w, n_layers, dec_batches, prefill_rows=256, max_s
                         sel = [b for b in range(nb) if b % R == r]
                         assert all(np.array_equal(got[b], got[sel[0]]) for b in sel)
                     k = min(R, nb)
-                    check_layer(l, got[:k], res[l + 1][:k, p:p + 1], want64[:k, p:p + 1], stats)
+                    check_layer(l, got[:k], res[l + 1][:k, p:p + 1], lambda: want64()[:k, p:p + 1], stats)
             if l % 10 == 0 or l == n_layers - 1:
                 say(f"  layer {l}: max|d| {max(s[1] for s in stats[-1 - len(dec_batches) * STEPS:]):.3e}")
     finally:
         h.destroy()
     worst = max(stats, key=lambda s: s[2])
     say(f"  {w.name}: worst layer {worst[0]}: max|d| {worst[1]:.3e} = {worst[2]:.2f} ulp of the row max, "
-        f"oracle fp32/fp64 spread {worst[3]:.3e}, min cos {min(s[4] for s in stats):.8f}")
+        f"min cos {min(s[4] for s in stats):.8f}; oracle fp64 runs needed on "
+        f"{sum(s[3] > 0 for s in stats)} of {len(stats)} checks")
     return stats
 
 
