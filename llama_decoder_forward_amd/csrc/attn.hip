@@ -136,7 +136,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__re
     // Stage kt of the tile ring: direct global -> LDS copies, each lane
     // fetching the 16 bytes that belong at its slot of the operand order.
     // Wave w copies K blocks 4w..4w+3 (block (ks, t, s): lane rr + 16 gg
-    // holds key 32 ks + 8 (rr / 4) + 4 t + rr % 4, d 32 s + 8 gg .. +7) and V
+    // holds key 32 ks + 8 (rr / 4) + 4 t + rr % 4, d 32 s + 8 gg .. +7; the
+    // cache stores each such block as 1 KiB in this order, k16_offset) and V
     // blocks 4w..4w+3 (block (dt, ks): lane d % 16 + 16 gg holds the keys
     // 32 ks + 8 gg .. +7 of dimension d = 16 dt + d % 16).  Keys past Lk read
     // cache entries of the same (row, KV head) that the scores mask out.
@@ -149,9 +150,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__re
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int blk = 4 * wave + j;
-            const int ks = blk >> 3, t = (blk >> 2) & 1, s = blk & 3;
-            const int kap = 8 * (rr >> 2) + 4 * t + (rr & 3);
-            lds_copy16(kc + (ks ? hb1 : hb0) + kap * hd + (4 * s + gg) * 8, klds + (buf * 16 + blk) * 64);
+            const int ks = blk >> 3, ts = blk & 7;  // (t, s) block of the 32-key half ks
+            lds_copy16(kc + (ks ? hb1 : hb0) + (ts * 64 + lane) * 8, klds + (buf * 16 + blk) * 64);
         }
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -344,7 +344,7 @@ __global__ void kv_write_kernel(const Tv *k, const Tv *v, int T, int pos0, int H
     const int pos = pos0 + t;
     int off;
     const int64_t st = kv_stream(pg, b, kvh, pos, Hkv, off);
-    kc[k_offset(st, off, d, Sb, hd)] = k[(int64_t)b * per_row + i];
+    kc[sizeof(Tv) == 2 ? k16_offset(st, off, d, Sb, hd) : k_offset(st, off, d, Sb, hd)] = k[(int64_t)b * per_row + i];
     if (sizeof(Tv) == 2)
         vc[v16_offset(st, off, d, Sb, hd)] = v[(int64_t)b * per_row + i];
     else

@@ -99,12 +99,13 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
         const int k0 = 32 * st;
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-            const int kp = perm_key(t, r);
-            const bool ok = k0 + kp < L;
-            const half_t *krow = kc + base + (ok ? kp : 0) * hd + 8 * g;
+            // the cache holds operand (t, s) of the step as 1 KiB in lane
+            // order (k16_offset); keys past L read entries of the same
+            // stream and are zeroed
+            const bool ok = k0 + perm_key(t, r) < L;
 #pragma unroll
             for (int s = 0; s < 4; s++)
-                kf[t][s] = ok ? ld_kv<NT>(krow + 32 * s) : z;
+                kf[t][s] = ok ? ld_kv<NT>(kc + base + ((t * 4 + s) * 64 + lane) * 8) : z;
         }
         const int kk = k0 + 8 * g;
         const bool vok = kk + 8 <= L;

@@ -63,6 +63,16 @@ __host__ __device__ inline int64_t k_offset(int64_t st, int off, int d, int Sb, 
 {
     return (st * Sb + off) * hd + d;
 }
+// fp16 K (head_dim 128): each 32-position block of a stream is stored in the
+// operand order of the attention kernels, eight 1 KiB blocks (t, s), t = 0..1
+// the 16-key sub-tile, s = 0..3 the 32-wide d chunk: lane r + 16 g of block
+// (t, s) holds key 8 (r / 4) + 4 t + r % 4 of the 32 and d = 32 s + 8 g .. +7,
+// so every load of a K operand reads 1 KiB contiguously.
+__host__ __device__ inline int64_t k16_offset(int64_t st, int off, int d, int Sb, int hd)
+{
+    const int kk = off & 31, t = (kk >> 2) & 1, r = ((kk >> 3) << 2) | (kk & 3);
+    return (st * Sb + (off & ~31)) * hd + ((t * 4 + (d >> 5)) * 64 + r + 16 * ((d >> 3) & 3)) * 8 + (d & 7);
+}
 __host__ __device__ inline int64_t v16_offset(int64_t st, int off, int d, int Sb, int hd)
 {
     return (st * Sb + (off & ~31)) * hd + d * 32 + (off & 31);

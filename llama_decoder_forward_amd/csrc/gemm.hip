@@ -84,7 +84,7 @@ __device__ __forceinline__ void epilogue_frag(const Epilogue &ep, int n0, int m,
                 const int kvh = (n - qrows) / hd;
                 int off;
                 const int64_t st = kv_stream(ep.pg, b, kvh, pos, ep.Hkv, off);
-                *reinterpret_cast<half4 *>((half_t *)ep.kcache + k_offset(st, off, d0, ep.S, hd)) = o;
+                *reinterpret_cast<half4 *>((half_t *)ep.kcache + k16_offset(st, off, d0, ep.S, hd)) = o;
             }
         } else {
             const int r = n - qrows - krows, kvh = r / hd, d0 = r % hd;

@@ -87,7 +87,9 @@ static void check_kv(const void *kc, const void *vc, const KvPages &pg, int Sb, 
         // kv_stream is a device function; same arithmetic here
         if (pg.tab) { off = pos & ((1 << pg.shift) - 1); st = (int64_t)pg.tab[(int64_t)b * pg.ld + (pos >> pg.shift)] * Hkv + kvh; }
         else { off = pos; st = (int64_t)b * Hkv + kvh; }
-        CHECK((const char *)kc + k_offset(st, off, 0, Sb, hd) * g_es, (size_t)hd * g_es);
+        // fp16 K: the key's values are spread over its 32-position block (k16_offset)
+        if (g_es == 2) CHECK((const char *)kc + k_offset(st, off & ~31, 0, Sb, hd) * g_es, (size_t)32 * hd * g_es);
+        else CHECK((const char *)kc + k_offset(st, off, 0, Sb, hd) * g_es, (size_t)hd * g_es);
         const int64_t v0 = g_es == 2 ? v16_offset(st, off, 0, Sb, hd) : v32_offset(st, off, 0, Sb, hd);
         const int64_t v1 = g_es == 2 ? v16_offset(st, off, hd - 1, Sb, hd) : v32_offset(st, off, hd - 1, Sb, hd);
         CHECK((const char *)vc + v0 * g_es, g_es);
