@@ -101,6 +101,28 @@ def cpu_baseline(w, prompt, budget_s=15.0, max_steps=64):
             "seconds_per_token_row": t_dec / n, "prefill_s": t_prefill}
 
 
+def counter_traffic(w):
+    """HBM bytes (fetched + written) per decode product launch from the
+    committed counter summary of this workload, or None when there is none or
+    the product kernels' sources changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_products_traffic_{w.name}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        k, sep, v = line.partition(":")
+        if sep and v.split():
+            vals[k.strip()] = v.split()[0]
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "llama_decoder_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("source_sha256_16") != h.hexdigest()[:16] or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,7 +330,10 @@ def measure(w, n_steps, warmup, profile_reps, kv_block):
                               "the whole step (attention, sampling, launch gaps included) against the "
                               "step's roofline is detail.decode_frac_of_roofline",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(w),
+                     "traffic_source": f"profiles/decode_products_traffic_{w.name}.txt (FETCH_SIZE + WRITE_SIZE "
+                                       "per launch of the step's products, scaled by the 1 GiB copy calibration)"
+                                       if counter_traffic(w) else None,
                      "bytes_per_launch": round(step_prod_bytes / launches),
                      "avg_launch_us": round(step_prod_us / launches, 3),
                      "launches_per_step": launches,

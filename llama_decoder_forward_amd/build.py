@@ -46,6 +46,16 @@ def build(verbose: bool = True) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link failed")
     os.replace(tmp, OUT)
+    # the counter-run driver: a plain C++ program on the C ABI
+    drv = os.path.join(HERE, "profile_driver")
+    cmd = ["g++", "-O2", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"),
+           os.path.join(CSRC, "profile_driver.cpp"), "-o", drv + f".tmp{os.getpid()}",
+           "-L", HERE, "-lllm", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("profile_driver build failed")
+    os.replace(drv + f".tmp{os.getpid()}", drv)
     if verbose:
         print(f"built {OUT}")
     return OUT
