@@ -229,9 +229,10 @@ def test_attention_decode(B, small, L):
                                      (64, 700, 1024), (160, 1000, 1024), (160, 3, 1024)])
 def test_attention_decode_many_pairs(B, Bn, L, S):
     """Bn * n_kv_heads (row, KV head) pairs: 128 pairs take the eight-wave
-    work-groups with non-temporal K/V loads, 320 the four-wave ones, 512 the two-wave ones with the next
-    step prefetched (non-temporal too); caches of 320 and 1024 positions, ragged last steps,
-    long contexts and a single key included."""
+    work-groups with non-temporal K/V loads, 320 the four-wave ones, 512 the
+    two-wave ones with the next step prefetched (non-temporal too); caches
+    of 320 and 1024 positions, ragged last steps, long contexts and a single
+    key included.  A second launch gives the same bits."""
     kw = small_f16(max_batch_size=Bn, max_seq_len=S)
     h = B.llm_create(B.make_params(**kw), 78)
     H, Hkv, d = kw["n_heads"], kw["n_kv_heads"], 128
@@ -246,6 +247,8 @@ def test_attention_decode_many_pairs(B, Bn, L, S):
     qd, od = dev(q), empty((Bn, 1, H, d), np.float16)
     h.op_attention(0, qd.data_ptr(), Bn, 1, L - 1, od.data_ptr())
     got = host(od).astype(np.float32)
+    h.op_attention(0, qd.data_ptr(), Bn, 1, L - 1, od.data_ptr())
+    assert np.array_equal(host(od).astype(np.float32), got)
     rows = [0, Bn // 2 + 1, Bn - 1]
     want = attention_reference(q[rows], K[rows], V[rows], [L - 1], H // Hkv)
     assert np.max(np.abs(got[rows] - want)) < 4e-3
