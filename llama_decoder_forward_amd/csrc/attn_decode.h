@@ -107,18 +107,20 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
             for (int s = 0; s < 4; s++)
                 kf[t][s] = ok ? ld_kv<NT>(kc + base + ((t * 4 + s) * 64 + lane) * 8) : z;
         }
+        // V: one 16-byte load per operand; entries of keys past L (the
+        // step's block is always allocated in full) are zeroed, since a
+        // probability of 0 times a stale non-finite value would not vanish
         const int kk = k0 + 8 * g;
         const bool vok = kk + 8 <= L;
         const half_t *vblk = vc + base + 8 * g;
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) {
-            const half_t *vrow = vblk + (16 * dt + r) * 32;
-            if (vok) {
-                vf[dt] = ld_kv<NT>(vrow);
-            } else {
+            half8 v = ld_kv<NT>(vblk + (16 * dt + r) * 32);
+            if (!vok) {
 #pragma unroll
-                for (int e = 0; e < 8; e++) vf[dt][e] = (kk + e < L) ? vrow[e] : (half_t)0.f;
+                for (int e = 0; e < 8; e++) v[e] = kk + e < L ? v[e] : (half_t)0.f;
             }
+            vf[dt] = v;
         }
     };
     auto compute = [&](int st, const half8 (&kf)[2][4], const half8 (&vf)[8]) {
