@@ -605,6 +605,13 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(const half_t *__re
 // used), so a single counter wait covers both: after X(kt) the wave has
 // issued exactly the (W, X) groups of PD-1 later k-tiles.
 // ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int KIND, int NSW, int PD, int TOK = 256>
 __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t *__restrict__ W, const half_t *X,
                                                                       int M, int N, int K, int n_base, Epilogue ep)
@@ -642,10 +649,17 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t 
         for (int q = 0; q < 2; q++) lds_copy16(wsrc[q] + (int64_t)k * 64, lw + buf * 1024 + (wave * 2 + q) * 64);
     };
     half8 xb[PD][XF];
-    auto issue_x = [&](int kt, half8 (&d)[XF]) {
-        const int k = min(kt, KT - 1);
-#pragma unroll
-        for (int j = 0; j < XF; j++) d[j] = xsrc[j][(int64_t)k * 64];
+    auto copy_w1 = [&](int st, int q) {
+        lds_copy16(wsrc[q] + (int64_t)min(st, KT - 1) * 64, lw + (st % NSW) * 1024 + (wave * 2 + q) * 64);
+    };
+    // one X fragment of k-tile kt into d, from assembly like the copies, so
+    // that the compiler adds no waits of its own: the counter waits below
+    // cover both (indexes past the end are clamped, the results unused)
+    auto load_x1 = [&](int kt, int j, half8 &d) {
+        asm volatile("global_load_dwordx4 %0, %1, off"
+                     : "=v"(d)
+                     : "v"(xsrc[j] + (int64_t)min(kt, KT - 1) * 64)
+                     : "memory");
     };
     floatx4 acc[8][XF];
 #pragma unroll
@@ -658,58 +672,80 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t 
 #pragma unroll
     for (int p = 0; p < PD; p++) {
         issue_w(NSW - 1 - PD + p);
-        issue_x(p, xb[p]);
+#pragma unroll
+        for (int j = 0; j < XF; j++)
+            if (p == 0 || j < XF - 1) load_x1(p, j, xb[p][j]);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the epilogue's scalar argument loads
     // The A fragments of k-tile kt+1 are read from LDS while k-tile kt
     // multiplies (two register sets, alternating with the unrolled body).
     // Stage 0 first: after its copies this wave has issued W(1), W(2), X(0),
-    // W(3), X(1), i.e. 6 + 2 XF operations.  (X is not declared __restrict__: with
-    // it, the compiler treated the X loads as invariant and moved them past
-    // these counter waits, which then no longer counted what they assume.)
-    if (XF == 4) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    // W(3) and X(1) but its last fragment (which k-tile 0 loads), i.e.
+    // 6 + 2 XF - 1 operations.
+    wait_vmcnt<3 * 2 + 2 * XF - 1>();
     __builtin_amdgcn_s_barrier();
     half8 ab[PD][8];
 #pragma unroll
     for (int i = 0; i < 8; i++) ab[0][i] = lw[(wn * 8 + i) * 64 + lane];
     // KT % PD == 0 (checked by the launcher): no guard inside the unrolled
-    // body, so every path into the loop head has issued the X loads in the
-    // same order and the compiler's own waits for them stay tight (a guard
-    // made it assume the worst order and wait for every load, the W copies
-    // it does not see included, once per PD k-tiles)
+    // body.  Each k-tile's copies, fragment reads and X loads are spread over
+    // its MFMA groups (one per X fragment), so that neither wave of a SIMD
+    // issues them in one burst.  Per k-tile, in issue order: group 0 loads
+    // the last fragment of X(kt+1) after its MFMAs (into the register the
+    // previous k-tile's last group read); group j > 0 issues its W copies
+    // before its MFMAs and X(kt+2) fragment j-1 after them (into the register
+    // group j-1 read).  A fragment register is thus reloaded at least one
+    // MFMA group after its last reader, and an LDS fragment read never
+    // follows an MFMA that reads the register it fills: an LDS read placed
+    // directly after such an MFMA gave wrong sums (the MFMA had not yet read
+    // its operand).  Counts per k-tile: CW = 2 copies, XF loads.
+    constexpr int C0 = 2 / XF;                            // copies of group 0
+    constexpr int TOPW = 2 + XF;                          // k-tile kt-1's operations
+    constexpr int LASTW = 2 * (2 + XF - 1) - C0;          // after X(kt)'s last fragment
     for (int kt0 = 0; kt0 < KT; kt0 += PD) {
 #pragma unroll
         for (int p = 0; p < PD; p++) {
             const int kt = kt0 + p;
             {
-                // X(kt) and, issued before it, W stages up to kt+1 are in (the
-                // one later k-tile's group, 2 + XF operations, may be
-                // pending); the barrier makes every wave's W copies visible
-                // and tells this wave that all have finished reading buffer
-                // (kt - 1) % NSW (its fragments were read one k-tile ago)
-                if (XF == 4) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-                else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                // every operation k-tile kt-2 issued is in (k-tile kt-1's may
+                // be pending): X(kt) but its last fragment, and W stages up
+                // to kt+1; also the fragment reads of A(kt).  The barrier makes
+                // every wave's W copies visible and tells this wave that all
+                // have finished reading buffer (kt - 1) % NSW
+                wait_vmcnt<TOPW>();
+                __builtin_amdgcn_s_waitcnt(0xC07F);
                 __builtin_amdgcn_s_barrier();
-                issue_w(kt + NSW - 1);
                 const int nx = (kt + 1) % NSW;  // after the last k-tile: a stage never used
-#pragma unroll
-                for (int i = 0; i < 8; i++) ab[1 - p][i] = lw[nx * 1024 + (wn * 8 + i) * 64 + lane];
-                __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int j = 0; j < XF; j++) {
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
+                    for (int i = j * 8 / XF; i < (j + 1) * 8 / XF; i++)
+                        ab[1 - p][i] = lw[nx * 1024 + (wn * 8 + i) * 64 + lane];
+#pragma unroll
+                    for (int q = j * 2 / XF; q < (j + 1) * 2 / XF; q++) copy_w1(kt + NSW - 1, q);
+                    // the last group also needs X(kt)'s last fragment
+                    if (j == XF - 1) wait_vmcnt<LASTW>();
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
                     for (int i = 0; i < 8; i++) acc[i][j] = mfma16(ab[p][i], xb[p][j], acc[i][j]);
                     __builtin_amdgcn_sched_barrier(0);
+                    if (j == 0) load_x1(kt + 1, XF - 1, xb[1 - p][XF - 1]);
+                    else load_x1(kt + PD, j - 1, xb[p][j - 1]);
                 }
                 __builtin_amdgcn_s_setprio(0);
-                issue_x(kt + PD, xb[p]);
             }
         }
     }
+    // The last k-tiles' X loads are still landing in their registers, which
+    // hold no value the compiler still needs: each is tied to a statement
+    // after the wait, so that nothing else is put there before they land.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int p = 0; p < PD; p++)
+#pragma unroll
+        for (int j = 0; j < XF; j++) asm volatile("" ::"v"(xb[p][j]));
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         const int n0 = (nb * 16 + wn * 8 + i) * 16;
