@@ -600,10 +600,9 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(const half_t *__re
 // while the current one multiplies.  A third fewer LDS reads and half the
 // LDS copies; measured 4-7% faster than the form above on the 7B..70B
 // prefill shapes (interleaved runs, medians), with the same sums.  Every wave
-// issues, per k-tile, its two W copies and then its four X loads, all
-// unconditionally (indexes past the end are clamped and the results never
-// used), so a single counter wait covers both: after X(kt) the wave has
-// issued exactly the (W, X) groups of PD-1 later k-tiles.
+// issues per k-tile its two W copies and its X loads unconditionally
+// (indexes past the end are clamped and the results never used) and in a
+// fixed order, so that counter waits cover both operands.
 // ---------------------------------------------------------------------------
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
