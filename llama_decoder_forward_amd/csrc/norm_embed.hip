@@ -51,7 +51,16 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64
                                                           int M, int D, float eps, half_t *y, int y_lay)
 {
 #pragma clang fp contract(off)
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    int blk = blockIdx.x;
+    if (y_lay == ACT_TILED && (gridDim.x & 31) == 0) {
+        // the four work-groups that write one 16-row group of the tile
+        // layout (each 1 KiB block interleaves the 16 rows in 16-byte pieces)
+        // run on one XCD (work-groups go to the eight XCDs round-robin), so
+        // that the L2 they share merges the pieces into whole lines
+        const int xcd = blk & 7, local = blk >> 3;
+        blk = ((local >> 2) * 8 + xcd) * 4 + (local & 3);
+    }
+    const int row = blk * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (row >= M) return;
     const half8 *xr = reinterpret_cast<const half8 *>(x + (int64_t)row * ldx);
     half8 *yr = reinterpret_cast<half8 *>(y + (int64_t)row * D);
