@@ -5,8 +5,8 @@
 //
 //   profile_driver WORKLOAD [layers] [decode_steps]
 //
-// WORKLOAD: llama2-7b-bs1 (batch 1, 8-token prompt) or llama2-70b-gqa-bs32
-// (batch 32, 2048-token prompts).  `layers` overrides the depth (the per-layer
+// WORKLOAD: llama2-7b-bs1 (batch 1, 8-token prompt), llama2-13b-bs8 (batch 8,
+// 1024-token prompts) or llama2-70b-gqa-bs32 (batch 32, 2048-token prompts).  `layers` overrides the depth (the per-layer
 // kernels are the same at any depth).  Tokens are seeded and uniform over the
 // vocabulary; decode steps are greedy.  Prints one line per phase with its
 // wall time.
@@ -44,7 +44,8 @@ double now()
 int main(int argc, char **argv)
 {
     if (argc < 2) {
-        std::fprintf(stderr, "usage: %s llama2-7b-bs1|llama2-70b-gqa-bs32 [layers] [decode_steps]\n", argv[0]);
+        std::fprintf(stderr, "usage: %s llama2-7b-bs1|llama2-13b-bs8|llama2-70b-gqa-bs32 [layers] [decode_steps]\n",
+                     argv[0]);
         return 2;
     }
     llm_params p{};
@@ -53,6 +54,9 @@ int main(int argc, char **argv)
     if (!std::strcmp(argv[1], "llama2-7b-bs1")) {
         p = llm_params{32, 4096, 32, 32, 32000, 256, 0.f, 1e-5f, 10000.f, 1, 2048, LLM_F16};
         B = 1, T = 8, seed = 1002;
+    } else if (!std::strcmp(argv[1], "llama2-13b-bs8")) {
+        p = llm_params{40, 5120, 40, 40, 32000, 256, 0.f, 1e-5f, 10000.f, 8, 2048, LLM_F16};
+        B = 8, T = 1024, seed = 1004;
     } else if (!std::strcmp(argv[1], "llama2-70b-gqa-bs32")) {
         p = llm_params{80, 8192, 64, 8, 32000, 4096, 1.3f, 1e-5f, 10000.f, 32, 4096, LLM_F16};
         B = 32, T = 2048, seed = 1005;
