@@ -15,6 +15,8 @@
 // is key 8*(r/4) + 4*t + r%4.  The accumulator lane group g then holds keys
 // 8g..8g+7 of the step, which is exactly the B-operand k-group of P^T, and
 // the matching A operand V^T[d][8g..8g+7] is one contiguous 16-byte load.
+#include <type_traits>
+
 #include "common.h"
 #include "attn_decode.h"
 
@@ -27,6 +29,37 @@ __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c)
 
 
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp(m_old - m_new) is never NaN
+
+// Maximum and sum over the four 16-lane rows of a wave, every lane keeping its
+// column (the query), by gfx950's row swaps (no LDS round trip).  Every row
+// ends with the same bits; the sum is (x0 + x1) + (x2 + x3).
+__device__ __forceinline__ float vmax(float a, float b)
+{
+    float d;
+    asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+// a product the compiler may not fuse with a following add (scores are
+// scaled and rounded before the maximum is subtracted, in every tile alike)
+__device__ __forceinline__ float mul_rn(float a, float b)
+{
+#pragma clang fp contract(off)
+    return a * b;
+}
+__device__ __forceinline__ float rows_max(float v)
+{
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v)
+{
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // ---------------------------------------------------------------------------
 // Decode: one work-group of NW waves per (row b, KV head).  The attended
@@ -69,19 +102,38 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
 constexpr int PF_Q = 128, PF_K = 64;
 
 constexpr int PF_LDS = 2 * 2 * PF_K * 128 * 2;  // two stages of a K and a V tile (bytes)
+constexpr bool HEAVY_FIRST = true;
 
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__restrict__ q,
                                                            const half_t *__restrict__ kc,
                                                            const half_t *__restrict__ vc, int Tu, int p0u,
                                                            int H, int Hkv, int S, KvPages pg, const int *cu,
-                                                           half_t *__restrict__ out, int out_lay)
+                                                           half_t *__restrict__ out, int out_lay, int ny)
 {
     const int hd = 128;
     extern __shared__ half8 smem[];
     // per stage: K tile as 4 sub-tiles x 4 d-steps x 64 lanes, V^T tile as 8
     // d-tiles x 2 key-steps x 64 lanes (operand order)
     half8 *const klds = smem, *const vlds = smem + 2 * PF_K * hd / 8;
-    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    // Work order: query tile by query tile (HEAVY_FIRST: the last, longest
+    // tiles first), every (row, head) inside one.  Work-groups are dealt to
+    // the eight XCDs in turn (group i to XCD i % 8), each XCD with its own
+    // L2; when the (row, KV head) groups divide evenly among them, the n_rep
+    // query heads of a group and all its query tiles go to one XCD, so the
+    // K/V stream they share is fetched into one L2 only.
+    const int nbh = (int)gridDim.x / ny, n_rep = H / Hkv;
+    const int yk = (int)blockIdx.x / nbh, rem = (int)blockIdx.x % nbh;
+    int b, h;
+    if (n_rep > 1 && ((nbh / n_rep) & 7) == 0) {
+        const int xcd = rem & 7, j = rem >> 3;
+        const int gi = xcd + 8 * (j / n_rep);
+        b = gi / Hkv;
+        h = (gi % Hkv) * n_rep + j % n_rep;
+    } else {
+        b = rem / H;
+        h = rem % H;
+    }
+    const int qt = HEAVY_FIRST ? ny - 1 - yk : yk;
     // uniform rows: T = Tu tokens at p0u..; varlen: row b's T tokens are the
     // packed rows cu[b].. at positions 0..
     int T = Tu, p0 = p0u;
@@ -91,11 +143,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__re
         T = cu[b + 1] - cu[b];
         p0 = 0;
     }
-    if ((int)blockIdx.y * PF_Q >= T) return;  // a query tile past this row's end (whole work-group)
+    if (qt * PF_Q >= T) return;  // a query tile past this row's end (whole work-group)
     const int kvh = h / (H / Hkv);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int q0 = blockIdx.y * PF_Q;
+    const int q0 = qt * PF_Q;
     const int wq0 = q0 + 32 * wave;  // this wave's first query
     // scores are kept in log2 units (scaled by log2(e) / sqrt(d)), so each
     // softmax term is one native exp2: exp(s / sqrt(d) - m) = 2^(s log2(e) /
@@ -180,20 +232,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__re
         }
     };
 
-    issue_tile(0);
-    for (int kt = 0; kt < ntiles; kt++) {
-        // this wave's copies of stage kt have landed (none of stage kt+1 is
-        // issued yet); the barrier makes every wave's visible and ends the
-        // reads of stage kt-1, whose buffer the next copies reuse
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        clear_v_tail(kt);
-        __syncthreads();
-        if (kt + 1 < ntiles) issue_tile(kt + 1);
-        const half8 *kl = klds + (kt & 1) * 1024, *vl = vlds + (kt & 1) * 1024;
-        const int kbase = kt * PF_K;
-        if (kbase > p0 + wq0 + 31) continue;  // all keys after this wave's queries
-        // S^T for both query column groups: every K fragment is read from LDS
-        // once and used for both
+    // One 64-key tile: S^T for both query column groups (every K fragment is
+    // read from LDS once and used for both), the online softmax, and
+    // O^T += V^T P^T (every V fragment read once).  MASKED: the causal mask
+    // (only tiles that reach past this wave's first query need it).
+    auto step = [&](const half8 *kl, const half8 *vl, int kbase, auto masked_c) {
+        constexpr bool MASKED = decltype(masked_c)::value;
         floatx4 sc[2][2][2];  // [c][ks][t]
 #pragma unroll
         for (int ks = 0; ks < 2; ks++)
@@ -210,9 +254,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__re
                     sc[c][ks][t] = a;
                 }
             }
-        // online softmax per column group; tiles wholly before this wave's
-        // first query need no causal mask (a uniform test)
-        const bool unmasked = kbase + PF_K - 1 <= p0 + wq0;
         half8 pb[2][2];
         float fac[2];
 #pragma unroll
@@ -226,43 +267,61 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const half_t *__re
                 for (int t = 0; t < 2; t++)
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
-                        const int key = kbase + 32 * ks + 8 * g + 4 * t + i;
-                        float v = sc[c][ks][t][i] * sl2;
-                        if (!unmasked) v = key <= qi ? v : -INFINITY;
+                        float v = mul_rn(sc[c][ks][t][i], sl2);
+                        if (MASKED && kbase + 32 * ks + 8 * g + 4 * t + i > qi) v = -INFINITY;
                         p[ks][4 * t + i] = v;
                         mx = fmaxf(mx, v);
                     }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(mrun[c], mx);
+            const float mnew = fmaxf(mrun[c], rows_max(mx));
             fac[c] = __builtin_amdgcn_exp2f(mrun[c] - mnew);
             float ls = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 2; ks++)
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
-                    float ev = __builtin_amdgcn_exp2f(p[ks][e] - mnew);
+                    const float ev = __builtin_amdgcn_exp2f(p[ks][e] - mnew);
                     ls += ev;
                     pb[c][ks][e] = (half_t)ev;
                 }
-            ls += __shfl_xor(ls, 16);
-            ls += __shfl_xor(ls, 32);
-            lrun[c] = lrun[c] * fac[c] + ls;
+            lrun[c] = lrun[c] * fac[c] + rows_sum(ls);
             mrun[c] = mnew;
         }
-        // O^T += V^T P^T for both column groups: every V fragment read once
+        // the rescale by a factor of exactly 1 (no lane's maximum moved) is
+        // skipped: the same bits
+        if (__any(fac[0] != 1.f || fac[1] != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < 8; dt++) {
+                acc[0][dt] = acc[0][dt] * fac[0];
+                acc[1][dt] = acc[1][dt] * fac[1];
+            }
+        }
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) {
-            floatx4 o0 = acc[0][dt] * fac[0], o1 = acc[1][dt] * fac[1];
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
                 const half8 vf = vl[(dt * 2 + ks) * 64 + lane];
-                o0 = mfma16(vf, pb[0][ks], o0);
-                o1 = mfma16(vf, pb[1][ks], o1);
+                acc[0][dt] = mfma16(vf, pb[0][ks], acc[0][dt]);
+                acc[1][dt] = mfma16(vf, pb[1][ks], acc[1][dt]);
             }
-            acc[0][dt] = o0;
-            acc[1][dt] = o1;
         }
+    };
+
+    issue_tile(0);
+    for (int kt = 0; kt < ntiles; kt++) {
+        // this wave's copies of stage kt have landed (none of stage kt+1 is
+        // issued yet); the barrier makes every wave's visible and ends the
+        // reads of stage kt-1, whose buffer the next copies reuse
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        clear_v_tail(kt);
+        __syncthreads();
+        if (kt + 1 < ntiles) issue_tile(kt + 1);
+        const half8 *kl = klds + (kt & 1) * 1024, *vl = vlds + (kt & 1) * 1024;
+        const int kbase = kt * PF_K;
+        if (kbase > p0 + wq0 + 31) continue;  // all keys after this wave's queries
+        // tiles wholly before this wave's first query need no causal mask
+        // (a uniform test; the two forms are separate code)
+        if (kbase + PF_K - 1 <= p0 + wq0) step(kl, vl, kbase, std::false_type{});
+        else step(kl, vl, kbase, std::true_type{});
     }
 #pragma unroll
     for (int c = 0; c < 2; c++) {
@@ -383,9 +442,10 @@ hipError_t launch_attn_decode_f16(const AttnArgs &a, hipStream_t s)
 hipError_t launch_attn_prefill_f16(const AttnArgs &a, hipStream_t s)
 {
     if (a.out_lay != ACT_ROWS && a.out_lay != ACT_TILED) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.B * a.H, (a.T + PF_Q - 1) / PF_Q), dim3(256), PF_LDS,
-                       s, (const half_t *)a.q, (const half_t *)a.kcache, (const half_t *)a.vcache,
-                       a.T, a.pos_imm, a.H, a.Hkv, a.Sb, a.pg, a.cu, (half_t *)a.out, a.out_lay);
+    const int ny = (a.T + PF_Q - 1) / PF_Q;
+    hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.B * a.H * ny), dim3(256), PF_LDS, s, (const half_t *)a.q,
+                       (const half_t *)a.kcache, (const half_t *)a.vcache, a.T, a.pos_imm, a.H, a.Hkv, a.Sb,
+                       a.pg, a.cu, (half_t *)a.out, a.out_lay, ny);
     return hipGetLastError();
 }
 
