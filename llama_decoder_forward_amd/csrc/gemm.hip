@@ -604,6 +604,148 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_kernel(const half_t *__re
 // (indexes past the end are clamped and the results never used) and in a
 // fixed order, so that counter waits cover both operands.
 // ---------------------------------------------------------------------------
+// s_waitcnt vmcnt(0) with the other counters left alone (gfx9 encoding)
+constexpr int kVmcnt0 = 0x0F70;
+
+// The epilogue of one wave's share of a tile: 8 x XF accumulator fragments,
+// fragment (i, j) holding W rows nrow0 + 16 i .. +15 (of this launch, whose
+// first row is n_base) and tokens mtok0 + 16 j .. +15, with the arithmetic
+// of epilogue_frag element for element.  The memory a kind reads (the
+// residual rows, the rotation table, the row positions) is loaded for a
+// group of fragments before any of their results is stored, so a wave waits
+// on memory once per group instead of once per fragment.  SWIGLU swaps the
+// halves of each (a, b) fragment pair between lanes 32 apart (which hold a
+// and b of the same outputs), so every lane computes two outputs instead of
+// half the lanes computing four.
+template <int KIND, int XF>
+__device__ __forceinline__ void epilogue_tile(const Epilogue &ep, floatx4 (&acc)[8][XF], int nrow0, int mtok0,
+                                              int M, int N, int n_base, int lane)
+{
+#pragma clang fp contract(off)
+    const int g = lane >> 4;
+    if constexpr (KIND == EP_RESID) {
+        half4 rv[8][XF];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int j = 0; j < XF; j++) {
+                const int n0 = nrow0 + 16 * i, m = mtok0 + 16 * j + (lane & 15);
+                rv[i][j] = half4{};
+                if (m < M && n0 < N)
+                    rv[i][j] = *reinterpret_cast<const half4 *>((const half_t *)ep.out + (int64_t)m * ep.ldo + n_base +
+                                                                n0 + 4 * g);
+            }
+        // one wait for all of them, outside the per-fragment branches (which
+        // the compiler would otherwise give a wait each)
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int j = 0; j < XF; j++) {
+                const int n0 = nrow0 + 16 * i, m = mtok0 + 16 * j + (lane & 15);
+                if (!(m < M && n0 < N)) continue;
+                half4 o;
+                for (int e = 0; e < 4; e++) o[e] = (half_t)((float)rv[i][j][e] + r16(acc[i][j][e]));
+                *reinterpret_cast<half4 *>((half_t *)ep.out + (int64_t)m * ep.ldo + n_base + n0 + 4 * g) = o;
+            }
+    } else if constexpr (KIND == EP_SWIGLU) {
+        const int hi = g >> 1;  // lanes 32..63: outputs 2 and 3 of the group
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int j = 0; j < XF; j++) {
+                const int n0 = nrow0 + 16 * i, m = mtok0 + 16 * j + (lane & 15);
+                // lanes 0..31 hold a (w1 rows), lanes 32..63 the matching b
+                // (w3 rows); after the swaps s[k][0] is a and s[k][1] is b of
+                // this lane's output k (outputs 0, 1 below lane 32, 2, 3 above)
+                const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][0]),
+                                                                 __float_as_uint(acc[i][j][2]), false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][1]),
+                                                                 __float_as_uint(acc[i][j][3]), false, false);
+                if (!(m < M && n0 < N)) continue;
+                const float av[2] = {__uint_as_float(s0[0]), __uint_as_float(s1[0])};
+                const float bv[2] = {__uint_as_float(s0[1]), __uint_as_float(s1[1])};
+                half2v o;
+                for (int k = 0; k < 2; k++) {
+                    const float a = r16(av[k]);
+                    const float sl = r16(a / (1.0f + expf(-a)));
+                    o[k] = (half_t)(sl * r16(bv[k]));
+                }
+                const int f0 = ((n_base + n0) >> 4) * 8 + 4 * (g & 1);
+                *reinterpret_cast<half2v *>((half_t *)ep.out + act_offset(m, f0, ep.ldo, ep.ldo, ep.out_lay) + 2 * hi) = o;
+            }
+    } else if constexpr (KIND == EP_QKV) {
+        const int hd = ep.hd, qrows = ep.H * hd, krows = ep.Hkv * hd;
+        int bj[XF], pj[XF];
+#pragma unroll
+        for (int j = 0; j < XF; j++) {
+            const int m = mtok0 + 16 * j + (lane & 15);
+            bj[j] = pj[j] = 0;
+            if (m < M) locate_row(m, ep.T, ep.pos_dev, ep.pos_imm, ep.pos_rows, ep.rowmap, bj[j], pj[j]);
+        }
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+#pragma unroll
+        for (int i0 = 0; i0 < 8; i0 += 4) {
+            float4 cs[4][XF];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < XF; j++) {
+                    const int n0 = n_base + nrow0 + 16 * (i0 + i), n = n0 + 4 * g;
+                    const int m = mtok0 + 16 * j + (lane & 15);
+                    cs[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (m < M && n0 - n_base < N && n < qrows + krows)
+                        cs[i][j] = *reinterpret_cast<const float4 *>(ep.rope + ((int64_t)pj[j] * (hd / 2) + n % hd / 2) * 2);
+                }
+            __builtin_amdgcn_s_waitcnt(kVmcnt0);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < XF; j++) {
+                    const int n0 = n_base + nrow0 + 16 * (i0 + i), n = n0 + 4 * g;
+                    const int m = mtok0 + 16 * j + (lane & 15);
+                    if (!(m < M && n0 - n_base < N)) continue;
+                    const floatx4 &ac = acc[i0 + i][j];
+                    if (n < qrows + krows) {
+                        const int d0 = n % hd;  // multiple of 4: pairs (d0, d0+1), (d0+2, d0+3)
+                        const float c4[4] = {cs[i][j].x, cs[i][j].y, cs[i][j].z, cs[i][j].w};
+                        half4 o;
+                        for (int q = 0; q < 2; q++) {
+                            const float a = r16(ac[2 * q]), bb = r16(ac[2 * q + 1]);
+                            const float c = c4[2 * q], sn = c4[2 * q + 1];
+                            const float re = a * c - bb * sn;
+                            const float im = a * sn + bb * c;
+                            o[2 * q] = (half_t)re;
+                            o[2 * q + 1] = (half_t)im;
+                        }
+                        if (n < qrows) {
+                            *reinterpret_cast<half4 *>((half_t *)ep.out + (int64_t)m * ep.ldo + n) = o;
+                        } else {
+                            const int kvh = (n - qrows) / hd;
+                            int off;
+                            const int64_t st = kv_stream(ep.pg, bj[j], kvh, pj[j], ep.Hkv, off);
+                            *reinterpret_cast<half4 *>((half_t *)ep.kcache + k16_offset(st, off, d0, ep.S, hd)) = o;
+                        }
+                    } else {
+                        const int r = n - qrows - krows, kvh = r / hd, d0 = r % hd;
+                        int off;
+                        const int64_t st = kv_stream(ep.pg, bj[j], kvh, pj[j], ep.Hkv, off);
+                        half_t *vc = (half_t *)ep.vcache + v16_offset(st, off, d0, ep.S, hd);
+                        for (int e = 0; e < 4; e++) vc[e * 32] = (half_t)ac[e];
+                    }
+                }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int j = 0; j < XF; j++) {
+                const int n0 = nrow0 + 16 * i, m = mtok0 + 16 * j + (lane & 15);
+                epilogue_frag<KIND>(ep, n_base + n0, m, m < M && n0 < N, acc[i][j], lane);
+            }
+    }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -746,15 +888,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile256_xreg_kernel(const half_t 
     for (int p = 0; p < PD; p++)
 #pragma unroll
         for (int j = 0; j < XF; j++) asm volatile("" ::"v"(xb[p][j]));
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int n0 = (nb * 16 + wn * 8 + i) * 16;
-#pragma unroll
-        for (int j = 0; j < XF; j++) {
-            const int m = (mb * (TOK / 16) + wm * XF + j) * 16 + (lane & 15);
-            epilogue_frag<KIND>(ep, n_base + n0, m, m < M && n0 < N, acc[i][j], lane);
-        }
-    }
+    epilogue_tile<KIND, XF>(ep, acc, (nb * 16 + wn * 8) * 16, (mb * (TOK / 16) + wm * XF) * 16, M, N, n_base, lane);
 }
 
 // One launch over W rows [n_base, n_base + N) (a whole number of 256-row
