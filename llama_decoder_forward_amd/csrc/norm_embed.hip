@@ -104,6 +104,80 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const half_t *x, int64
     }
 }
 
+// The same RMSNorm into the weight tile layout (ACT_TILED): one work-group of
+// eight waves per half of a 16-row group, a wave per row with the arithmetic
+// above.  A 1 KiB tile holds, for each of its four 8-column chunks, the 16
+// rows' 16-byte pieces in row order, so rows 0..7 and rows 8..15 fill one
+// 128-byte line each: the work-group stages half its rows' range at a time
+// in LDS and writes whole lines.  The weight row is read once per
+// work-group into LDS.  Rows past M (the last group) are written as zeros.
+// D is a multiple of 512, so every lane holds J = D / 512 pieces and every
+// bound below is uniform.
+__global__ __launch_bounds__(512, 4) void rmsnorm_tiled_kernel(const half_t *x, int64_t ldx, const half_t *w, int M,
+                                                               int D, float eps, half_t *y)
+{
+#pragma clang fp contract(off)
+    extern __shared__ half8 sm[];  // weight row [D / 8], then [D / 64 tiles][4 chunks][8 rows]
+    const int nv = D / 8, J = D / 512, KT = D / 32, half_kt = KT / 2;
+    half8 *wl = sm, *st = sm + nv;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int grp = blockIdx.x >> 1, sub = blockIdx.x & 1, row = grp * 16 + sub * 8 + wave;
+    const half8 *wr = reinterpret_cast<const half8 *>(w);
+    for (int i = tid; i < nv; i += 512) wl[i] = wr[i];
+    const half8 *xr = reinterpret_cast<const half8 *>(x + (int64_t)row * ldx) + lane;
+    half8 v[RMS_VEC];
+    const bool live = row < M;  // uniform over the wave
+#pragma unroll
+    for (int j = 0; j < RMS_VEC; j++) v[j] = live && j < J ? xr[64 * j] : half8{};
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < RMS_VEC; j++) {
+        if (j < J) {
+#pragma unroll
+            for (int e = 0; e < 8; e++) { float f = (float)v[j][e]; ss += f * f; }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const float r = __frcp_rn(__fsqrt_rn(ss / (float)D + eps));
+    __syncthreads();  // the weight row is in LDS
+    half8 *yg = reinterpret_cast<half8 *>(y) + (int64_t)grp * KT * 64 + sub * 8;
+    // piece i = lane + 64 j (elements 8i..8i+7) sits in k-tile 16 j + lane / 4,
+    // chunk lane % 4.  Pass h stages the pieces of the odd or even j, i.e. the
+    // k-tiles 16 j .. 16 j + 15 of those j (J is even), at staging tile
+    // 16 (j / 2) + lane / 4.
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int jj = 0; jj < RMS_VEC / 2; jj++) {
+            const int j = 2 * jj + h;
+            if (j < J) {
+                const half8 wv = wl[lane + 64 * j];
+                // the fp32 values of the row are converted again here rather
+                // than kept from the sum of squares (that would hold twice
+                // the registers)
+                half8 vj = v[j];
+                asm volatile("" : "+v"(vj));
+                half8 o;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    half_t n = (half_t)((float)vj[e] * r);
+                    o[e] = (half_t)((float)n * (float)wv[e]);
+                }
+                st[((jj * 16 + (lane >> 2)) * 4 + (lane & 3)) * 8 + wave] = o;
+            }
+        }
+        __syncthreads();
+        // q = (staging tile t, chunk, row): 8 rows of a chunk are one
+        // 128-byte line at tile offset 256 chunk + 128 sub
+        for (int q = tid; q < half_kt * 32; q += 512) {
+            const int t = q >> 5, kt = ((t >> 4) * 2 + h) * 16 + (t & 15);
+            yg[(int64_t)kt * 64 + ((q >> 3) & 3) * 16 + (q & 7)] = st[q];
+        }
+        __syncthreads();  // before the next pass reuses the staging area
+    }
+}
+
 // The same RMSNorm for the few rows of a decode step: one row per work-group
 // of eight waves, so the row's loads are spread over eight times as many
 // CUs.  Thread t sums the squares of its elements 8t.., 8(t + 512).., ...,
@@ -238,6 +312,10 @@ hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int 
     if (dtype == 1 && M <= 64)
         hipLaunchKernelGGL(rmsnorm_row_kernel<0>, dim3(M), dim3(512), 0, s, (const half_t *)x, ldx,
                            (const half_t *)w, D, eps, (half_t *)y, y_lay, (const float *)nullptr, (half_t *)nullptr);
+    else if (dtype == 1 && y_lay == ACT_TILED && D % 1024 == 0)
+        // the output buffer spans whole 16-row groups
+        hipLaunchKernelGGL(rmsnorm_tiled_kernel, dim3((M + 15) / 16 * 2), dim3(512), (size_t)10 * D, s,
+                           (const half_t *)x, ldx, (const half_t *)w, M, D, eps, (half_t *)y);
     else if (dtype == 1)
         hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((M + 3) / 4), dim3(256), 0, s, (const half_t *)x, ldx,
                            (const half_t *)w, M, D, eps, (half_t *)y, y_lay);
