@@ -675,7 +675,10 @@ __device__ __forceinline__ void epilogue_tile(const Epilogue &ep, floatx4 (&acc)
                 *reinterpret_cast<half2v *>((half_t *)ep.out + act_offset(m, f0, ep.ldo, ep.ldo, ep.out_lay) + 2 * hi) = o;
             }
     } else if constexpr (KIND == EP_QKV) {
-        const int hd = ep.hd, qrows = ep.H * hd, krows = ep.Hkv * hd;
+        // head dimension 128 (checked by the launcher): the divisions below
+        // are shifts
+        constexpr int hd = 128;
+        const int qrows = ep.H * hd, krows = ep.Hkv * hd;
         int bj[XF], pj[XF];
 #pragma unroll
         for (int j = 0; j < XF; j++) {
@@ -950,8 +953,9 @@ template <bool XT>
 hipError_t launch_tile256(const GemmArgs &a, hipStream_t s)
 {
     if constexpr (XT) {
-        // fp16 models have dim and ffn width multiples of 64: K/32 is even
-        if ((a.K >> 5) % 2) return hipErrorInvalidValue;
+        // fp16 models have dim and ffn width multiples of 64: K/32 is even;
+        // the QKV epilogue of this form takes heads of 128
+        if ((a.K >> 5) % 2 || (a.ep.kind == EP_QKV && a.ep.hd != 128)) return hipErrorInvalidValue;
         return launch_tile256_xreg<5>(a, s);
     } else {
         // the eight-wave form with a five-stage ring (measured 4-16% faster than
