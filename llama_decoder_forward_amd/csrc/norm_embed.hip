@@ -309,6 +309,7 @@ hipError_t launch_rmsnorm(const void *x, int64_t ldx, const void *w, int M, int 
     if (M <= 0) return hipSuccess;
     if (y_lay && (dtype != 1 || D % 32)) return hipErrorInvalidValue;
     if ((y_lay == 1 || y_lay == 2) && M > 16 * y_lay) return hipErrorInvalidValue;
+    if (dtype == 1 && D > 64 * 8 * RMS_VEC) return hipErrorInvalidValue;  // the fp16 kernels hold a row in registers
     if (dtype == 1 && M <= 64)
         hipLaunchKernelGGL(rmsnorm_row_kernel<0>, dim3(M), dim3(512), 0, s, (const half_t *)x, ldx,
                            (const half_t *)w, D, eps, (half_t *)y, y_lay, (const float *)nullptr, (half_t *)nullptr);
