@@ -92,12 +92,14 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
 // Causal prefill of T tokens at positions p0..p0+T-1 of every row over the
 // cache prefix 0..p0-1 and themselves (walkthrough section 3.8: a zero
 // block before the causal triangle when p0 > 0): flash-style online
-// softmax.  Grid (B*H, ceil(T/128)); 4 waves x 32 queries (two MFMA column
-// groups).  64-key tiles of K (in permuted operand order) and V^T are staged
-// in LDS with register prefetch of the next tile.  Tiles entirely above a
-// wave's last query are skipped; the diagonal tile is masked.  Each 32-key
-// half of a tile lies in one cache stream (blocks of a paged cache hold a
-// multiple of 32 positions), located once per tile.
+// softmax.  One work-group per (row, head, 128 queries): 4 waves x 32
+// queries (two MFMA column groups), two work-groups per CU.  64-key tiles of
+// K (in permuted operand order) and V^T reach LDS by direct global -> LDS
+// copies into a two-stage ring, the next tile in flight while the current
+// one computes.  Tiles entirely above a wave's last query are skipped; tiles
+// that reach past its first query are masked.  Each 32-key half of a tile
+// lies in one cache stream (blocks of a paged cache hold a multiple of 32
+// positions), located once per tile.
 // ---------------------------------------------------------------------------
 constexpr int PF_Q = 128, PF_K = 64;
 
