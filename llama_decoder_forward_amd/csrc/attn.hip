@@ -428,14 +428,15 @@ hipError_t launch_decode(const AttnArgs &a, hipStream_t s)
     if (pairs >= 512)  // non-temporal K/V loads: 7B bs32 30.9 -> 29.6 us (L = 204), 51.9 -> 48.5 us (L = 512)
         hipLaunchKernelGGL((attn_decode_kernel<2, true, PAGED, true>), dim3(pairs), dim3(128), 0, s, q, kc, vc, a.H,
                            a.Hkv, a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
-    else if (pairs >= 300)  // 320 pairs (13B bs8); 256 (70B bs32) do better with eight
-        hipLaunchKernelGGL((attn_decode_kernel<4, false, PAGED>), dim3(pairs), dim3(256), 0, s, q, kc, vc, a.H, a.Hkv,
-                           a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
+    else if (pairs >= 300)  // 320 pairs (13B bs8; 256 (70B bs32) do better with eight): non-temporal K/V
+                            // loads, 13B bs8 decode attention 2.22 -> 2.05 ms per step
+        hipLaunchKernelGGL((attn_decode_kernel<4, false, PAGED, true>), dim3(pairs), dim3(256), 0, s, q, kc, vc, a.H,
+                           a.Hkv, a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
     else if (pairs >= 128)  // non-temporal K/V loads: 7% faster on 256 pairs (70B bs32), slower elsewhere
         hipLaunchKernelGGL((attn_decode_kernel<8, false, PAGED, true>), dim3(pairs), dim3(512), 0, s, q, kc, vc, a.H,
                            a.Hkv, a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
-    else
-        hipLaunchKernelGGL((attn_decode_kernel<8, false, PAGED>), dim3(pairs), dim3(512), 0, s, q, kc, vc, a.H, a.Hkv,
+    else  // next step prefetched: 7B bs1 decode attention 0.348 -> 0.322 ms per step
+        hipLaunchKernelGGL((attn_decode_kernel<8, true, PAGED>), dim3(pairs), dim3(512), 0, s, q, kc, vc, a.H, a.Hkv,
                            a.Sb, a.pg, a.pos_dev, a.pos_imm, a.pos_rows, o, a.out_lay);
     return hipGetLastError();
 }
