@@ -1134,6 +1134,16 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
     if (a.x_lay == 1) {
         // fragment-major activations, 3..16 rows
         if (nw || a.M > 16) return hipErrorInvalidValue;
+        if (a.pending && a.ep.part && a.ep.kind == EP_RESID && tiles == 320 && (a.K >> 5) % 4 == 0 &&
+            (int64_t)4 * a.M * a.N <= kSplitMaxFloats) {
+            // 320 row blocks (13B wo, w2), only when the next normalisation
+            // adds the partials: 64 groups of five row blocks over a quarter
+            // of K each, one work-group per CU, a quarter of the activation
+            // block through each (8 rows: w2 26.8 -> 23.0 us, wo 11.4 ->
+            // 10.0 us; two row blocks per work-group unsplit leave 96 CUs idle)
+            *a.pending = 4;
+            return skinny_split<4, 5, false, 4, false>(a, W, X, s, false);
+        }
         if (tiles < 1024 && tiles % 2 == 0)
             skinny<8, 2, false, false, false, true, false>(a, W, X, 0, 0, s);
         else if (tiles % 4 == 0)
