@@ -1194,7 +1194,8 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s)
         else if (tiles < 1024 && tiles % 4 == 0)
             skinny<2, 4, true, false, false, true, true>(a, W, X, 0, 0, s);
         else if (tiles < 1536 && tiles % 2 == 0)
-            skinny<2, 2, true, false, false, true, false>(a, W, X, 0, 0, s);
+            // two rounds in flight (7B w1|w3: 34.5 -> 34.2 us, same sums)
+            skinny<2, 2, true, false, false, true, true>(a, W, X, 0, 0, s);
         else if (tiles >= 2048 && tiles % 8 == 0)
             // eight row blocks per work-group read each activation fragment
             // once for all of them (the CUs' streaming rate, not HBM, bounds
