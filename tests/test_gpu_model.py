@@ -124,6 +124,40 @@ def test_small_fp16_forced(B, rows, T0):
     h.destroy()
 
 
+@pytest.mark.parametrize("rows", [1, 3])
+def test_fp16_decode_to_last_slot(B, rows):
+    """fp16 GQA model at max_seq_len 64: a 52-token prompt, then forced decode
+    steps up to position 63, the last slot of every cache stream (its K/V
+    entry closes the stream's last 32-position block), against the oracle."""
+    kw = small_kw(max_seq_len=64)
+    T0, steps = 52, 12
+    toks = synth.tokens(43, rows, T0 + steps, kw["vocab_size"])
+    say("fp16 decode to the last slot", rows)
+    h = B.llm_create(B.make_params(**kw), 93)
+    got, _ = gpu_forced_logits(h, toks, T0, steps)
+    h.destroy()
+    want = oracle.forward_stream(ocfg(kw), 93, toks, T0 - 1)
+    assert got.shape == want.shape
+    check_logits(got, want)
+
+
+@pytest.mark.parametrize("rows", [1, 2])
+def test_fp16_prefill_fills_the_cache(B, rows):
+    """A prompt of max_seq_len tokens (every cache slot written by one
+    prefill), compared with the oracle at its last position; decoding after
+    it is refused (no slot left)."""
+    kw = small_kw(max_seq_len=64)
+    toks = synth.tokens(47, rows, 64, kw["vocab_size"])
+    h = B.llm_create(B.make_params(**kw), 97)
+    h.prefill(toks)
+    got = h.get_logits()
+    with pytest.raises(RuntimeError):
+        h.decode(64)
+    h.destroy()
+    want = oracle.forward_stream(ocfg(kw), 97, toks, 63)[:, 0]
+    check_logits(got, want)
+
+
 @pytest.mark.parametrize("rows", [5, 16, 17, 32])
 def test_wide_batch_decode(B, rows):
     """Decode batches of 3..32 rows hand fragment-major activations between
