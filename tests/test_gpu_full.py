@@ -269,6 +269,38 @@ def test_13b_shape_8_rows_decode(B):
 
 
 @pytest.mark.timeout(600)
+def test_13b_shape_8_ragged_rows_decode(B):
+    """Two 13B-shaped layers at 8 rows with ragged prompts (one varlen
+    prefill), then 3 per-row decode steps with forced tokens: the rows sit
+    at different positions, and the 8-row products take the same forms as
+    in a uniform step (wo and w2 split over K, their partials added by the
+    next normalisation launch).  Rows 0 and 7 against the oracle's one-row
+    forward over their own tokens."""
+    w = configs.L13B_BS8
+    kw = w.model_kwargs(max_batch_size=8, max_seq_len=64)
+    kw["n_layers"] = 2
+    lens = [int(x) for x in synth.prompt_lengths(w.token_seed + 7, 8, 4, 14)]
+    steps = 3
+    toks = synth.tokens(w.token_seed + 8, 8, max(lens) + steps, w.vocab_size)
+    say("13B-shaped layers, 8 ragged rows: gpu", lens)
+    h = B.llm_create(B.make_params(**kw), w.weight_seed)
+    h.prefill_varlen([toks[b, :lens[b]] for b in range(8)])
+    got = [h.get_logits()]
+    for k in range(steps):
+        h.set_tokens_rows([toks[b, lens[b] + k] for b in range(8)])
+        h.decode_rows()
+        got.append(h.get_logits())
+    h.destroy()
+    got = np.stack(got, 1)
+    cfg = oracle.Cfg(**dict(kw, max_batch_size=1))
+    for b in (0, 7):
+        say("13B-shaped layers, ragged: oracle row", b)
+        n = lens[b] + steps
+        want = oracle.forward_stream(cfg, w.weight_seed, toks[b:b + 1, :n], lens[b] - 1)
+        check_logits(got[b:b + 1], want)
+
+
+@pytest.mark.timeout(600)
 def test_13b_shape_one_layer_long_prefill(B):
     """One 13B-shaped layer with the real embedding and head, the bench's
     prefill of 8 rows x 1024 tokens: 640 tiles of 256 x 256 for wo and w2
