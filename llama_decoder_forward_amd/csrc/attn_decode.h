@@ -163,9 +163,44 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
 #pragma unroll
         for (int dt = 0; dt < 8; dt++) acc[dt] = mfma16(vf[dt], pb, acc[dt] * fac);
     };
+    // static cache: a wave's first 32-key step does not depend on the
+    // attended length (read from memory by the kernel), so it is loaded
+    // before the length is known, and its keys past the length are zeroed
+    // afterwards as load() zeroes them (same operands)
+    auto load_raw = [&](int64_t base, half8 (&kf)[2][4], half8 (&vf)[8]) {
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int s = 0; s < 4; s++) kf[t][s] = ld_kv<NT>(kc + base + ((t * 4 + s) * 64 + lane) * 8);
+        const half_t *vblk = vc + base + 8 * g;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) vf[dt] = ld_kv<NT>(vblk + (16 * dt + r) * 32);
+    };
+    auto mask = [&](int st, half8 (&kf)[2][4], half8 (&vf)[8]) {
+        const int k0 = 32 * st;
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+            if (!(k0 + perm_key(t, r) < L)) {
+#pragma unroll
+                for (int s = 0; s < 4; s++) kf[t][s] = z;
+            }
+        const int kk = k0 + 8 * g;
+        if (!(kk + 8 <= L)) {
+#pragma unroll
+            for (int dt = 0; dt < 8; dt++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) vf[dt][e] = kk + e < L ? vf[dt][e] : (half_t)0.f;
+        }
+    };
     half8 kf[2][4], vf[8];
     int st = wave;
-    if (st < nsteps) load(st, step_base(st), kf, vf);
+    const bool spec = !PAGED && (wave + 1) * 32 <= S;
+    if (spec) {
+        load_raw(step_base(st), kf, vf);
+        if (st < nsteps) mask(st, kf, vf);
+    } else if (st < nsteps) {
+        load(st, step_base(st), kf, vf);
+    }
     for (; st < nsteps; st += NW) {
         const int nx = st + NW;
         const int64_t nbase = nx < nsteps ? step_base(nx) : 0;
