@@ -254,11 +254,32 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
 #pragma unroll
                 for (int u = 0; u < U; u++) d[t][u] = ldw1<NT>(Wt + ((int64_t)t * KS + min(b + u, KT - 1)) * 64);
         };
-        auto round = [&](half8 (&wc)[TPB][U], half8 (&wn)[TPB][U], int b, bool pre) {
+        // XPF (fragment-major activations from global memory): the next
+        // round's activation fragments are loaded with its weight tiles, one
+        // round ahead, instead of at the start of the round that uses them
+        constexpr bool XPF = XT && !STAGE;
+        constexpr int U1 = TWO ? U : 1;
+        half8 xa0[XPF ? U : 1], xa1[XPF ? U1 : 1], xb0[XPF ? U : 1], xb1[XPF ? U1 : 1];
+        auto ldx = [&](half8 (&d0)[XPF ? U : 1], half8 (&d1)[XPF ? U1 : 1], int b) {
+#pragma unroll
+            for (int u = 0; u < (XPF ? U : 0); u++) {
+                const int kt = min(b + u, KT - 1);
+                d0[u] = xt[(int64_t)kt * MH * 64];
+                if (TWO) d1[TWO ? u : 0] = xt[((int64_t)kt * MH + 1) * 64];
+            }
+        };
+        auto round = [&](half8 (&wc)[TPB][U], half8 (&wn)[TPB][U], half8 (&xc0)[XPF ? U : 1],
+                         half8 (&xc1)[XPF ? U1 : 1], half8 (&xn0)[XPF ? U : 1], half8 (&xn1)[XPF ? U1 : 1],
+                         int b, bool pre) {
             half8 b0[U], b1[TWO ? U : 1];
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int kt = min(b + u, KT - 1);
+                if (XPF) {
+                    b0[u] = xc0[XPF ? u : 0];
+                    if (TWO) b1[TWO ? u : 0] = xc1[XPF && TWO ? u : 0];
+                    continue;
+                }
                 if (STAGE) b0[u] = xl[kt * 4];
                 else if (XT) b0[u] = xt[(int64_t)kt * MH * 64];
                 else b0[u] = *reinterpret_cast<const half8 *>(x0 + kt * 32);
@@ -267,7 +288,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
                     else b1[TWO ? u : 0] = *reinterpret_cast<const half8 *>(x1 + kt * 32);
                 }
             }
-            if (pre) ldw(wn, b + STEP);
+            if (pre) {
+                ldw(wn, b + STEP);
+                if (XPF) ldx(xn0, xn1, b + STEP);
+            }
             // keep the scheduler from sinking the prefetch below the MFMAs
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -285,19 +309,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const half_t *__re
                 }
             }
         };
+        if (XPF) ldx(xa0, xa1, base);
         int i = 0;
         for (; i + 2 < nr; i += 2) {
-            round(w, w2, base, true);
+            round(w, w2, xa0, xa1, xb0, xb1, base, true);
             base += STEP;
-            round(w2, w, base, true);
+            round(w2, w, xb0, xb1, xa0, xa1, base, true);
             base += STEP;
         }
         if (nr - i == 2) {
-            round(w, w2, base, true);
+            round(w, w2, xa0, xa1, xb0, xb1, base, true);
             base += STEP;
-            round(w2, w, base, false);
+            round(w2, w, xb0, xb1, xa0, xa1, base, false);
         } else if (nr - i == 1) {
-            round(w, w2, base, false);
+            round(w, w2, xa0, xa1, xb0, xb1, base, false);
         }
     }
     for (; !PF && base < KT; base += NW * U) {
