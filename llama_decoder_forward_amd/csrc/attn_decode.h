@@ -10,8 +10,9 @@
 // lane owns its query's softmax state.  Inside a 32-key step, row r of S^T
 // sub-tile t is key 8*(r/4) + 4*t + r%4, so the accumulator lane group g
 // holds keys 8g..8g+7 of the step -- exactly the B-operand k-group of P^T --
-// and the matching V^T operand is one contiguous 16-byte load.  PF: a wave's
-// next step is loaded while the current one computes.  PAGED: each 32-key step
+// and the matching V^T operand is one contiguous 16-byte load.  A wave's first
+// step of the static cache is loaded before the attended length arrives.  PF: a
+// wave's next step is loaded while the current one computes.  PAGED: each 32-key step
 // lies in one block of the row's table; the table entries the row uses are
 // held in lanes and read with readlane.  NT: K and V are read non-temporally.  The NW
 // waves' states are merged in one round through LDS (fixed wave order).
