@@ -11,7 +11,8 @@
 // sub-tile t is key 8*(r/4) + 4*t + r%4, so the accumulator lane group g
 // holds keys 8g..8g+7 of the step -- exactly the B-operand k-group of P^T --
 // and the matching V^T operand is one contiguous 16-byte load.  A wave's first
-// step of the static cache is loaded before the attended length arrives.  PF: a
+// step (of the static cache, or inside the row's first block of a paged one) is
+// loaded before the attended length arrives.  PF: a
 // wave's next step is loaded while the current one computes.  PAGED: each 32-key step
 // lies in one block of the row's table; the table entries the row uses are
 // held in lanes and read with readlane.  NT: K and V are read non-temporally.  The NW
@@ -69,13 +70,14 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
     // PAGED: lane j holds entries j and 64 + j of the row's block table (the
     // entries its L positions use), so a step finds its block with a lane
     // read instead of a memory load; entries from 128 on are loaded
+    // (loaded after the early first step below, which does not need them)
     int tv0 = 0, tv1 = 0;
-    if (PAGED) {
+    auto load_table = [&]() {
         const int *trow = pg.tab + (int64_t)b * pg.ld;
         const int nent = ((L - 1) >> pg.shift) + 1;
         tv0 = lane < nent ? trow[lane] : 0;
         tv1 = 64 + lane < nent ? trow[64 + lane] : 0;
-    }
+    };
     // element offset of the first key of 32-key step st in both K and V
     auto step_base = [&](int st) -> int64_t {
         const int k0 = 32 * st;
@@ -195,9 +197,21 @@ __device__ __forceinline__ void attn_decode_wg(const half_t *__restrict__ q, con
     };
     half8 kf[2][4], vf[8];
     int st = wave;
-    const bool spec = !PAGED && (wave + 1) * 32 <= S;
+    // paged: a first step inside the row's first block (table entry 0, which
+    // every row holds, position 0 being written first) is read early the same way
+    const bool spec = PAGED ? 32 * (wave + 1) <= (1 << pg.shift) : (wave + 1) * 32 <= S;
     if (spec) {
-        load_raw(step_base(st), kf, vf);
+        int64_t sb;
+        if (PAGED) {
+            const int64_t blk = pg.tab[(int64_t)b * pg.ld];
+            sb = (((blk * Hkv + kvh) << pg.shift) + 32 * st) * hd;
+        } else {
+            sb = step_base(st);
+        }
+        load_raw(sb, kf, vf);
+    }
+    if (PAGED) load_table();
+    if (spec) {
         if (st < nsteps) mask(st, kf, vf);
     } else if (st < nsteps) {
         load(st, step_base(st), kf, vf);
